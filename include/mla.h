@@ -1,0 +1,203 @@
+/*
+ * mla.h -- C ABI of libmla: Multi-head Latent Attention (MLA) decoding over a
+ * paged, compressed latent KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * What is computed (sources are the web pages this method is described on):
+ *  - "Transformer升级之路：21、MLA好在哪里？（下）", section 双重投影 (the two-column
+ *    table): at decode time MLA is an MQA whose key and value are the cached
+ *    latent c itself; W_UK moves to the query side (q_lat = W_UK^T q_nope) and
+ *    W_UV to the output side (o = W_UV o_lat), per head.  Section 总而言之: a
+ *    shared low-dimensional RoPE key is concatenated to the key.
+ *  - "DeepSeek-V3 解读：Multi-head Latent Attention", section 为什么需要解耦 RoPE:
+ *    the per-head query part q_R and one shared key k_R carry the rotary
+ *    position; only the latent c_KV and the rotated k_R are cached.  Section
+ *    RoPE（旋转式位置编码）: consecutive pairs of dimensions are rotated by a
+ *    position-dependent angle.
+ *  - Tencent Cloud MLA article listing, FlashMLA snippet: decoding runs over a
+ *    paged cache addressed by a block table with per-sequence cache lengths and
+ *    returns (o, lse); splits of the key range are merged by log-sum-exp.
+ *
+ * Conventions for every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller (allocate them
+ *    however you like); the library never frees them, never keeps them after
+ *    the call returns, and never allocates device memory itself.
+ *  - Tensors are dense, row-major, with the shapes given below.  Element types
+ *    follow mla_dims.act_dtype ("act") and mla_dims.cache_dtype.
+ *  - Each call validates its arguments on the host first.  On any invalid
+ *    argument it returns an error status and launches nothing (outputs are left
+ *    untouched).  Otherwise it enqueues its kernels asynchronously on `stream`
+ *    (a hipStream_t; NULL = the default stream) and returns MLA_OK, or
+ *    MLA_ERR_LAUNCH if the runtime rejected a launch.  Faults inside a kernel
+ *    surface at the caller's next synchronisation.  No call synchronises.
+ *  - Integer index arrays (positions, sequence ids, block tables, lengths) are
+ *    int32 device arrays; their CONTENTS are trusted: the host cannot read
+ *    them without synchronising.  Kernels skip (never dereference) block-table
+ *    entries < 0 and tokens whose position falls outside the sequence's table.
+ *  - No call keeps mutable global state; concurrent calls on different streams
+ *    are safe as long as their output/workspace buffers do not overlap.
+ */
+#ifndef MLA_H_
+#define MLA_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MLA_OK = 0,
+  MLA_ERR_INVALID_ARG = 1,   /* NULL pointer, non-positive size, bad dims      */
+  MLA_ERR_UNSUPPORTED = 2,   /* valid but unsupported dtype / dims combination */
+  MLA_ERR_WORKSPACE = 3,     /* workspace missing or smaller than required     */
+  MLA_ERR_LAUNCH = 4         /* the HIP runtime rejected a kernel launch       */
+} mla_status;
+
+typedef enum {
+  MLA_F32 = 0,               /* IEEE binary32                                  */
+  MLA_BF16 = 1,              /* bfloat16                                       */
+  MLA_FP8_E4M3 = 2           /* OCP E4M3FN (cache only)                        */
+} mla_dtype;
+
+typedef void* mla_stream_t;  /* a hipStream_t */
+
+/*
+ * Problem dimensions, shared by every call.
+ *   n_heads       query heads H
+ *   d_c           latent width (also the value width of the absorbed form)
+ *   d_rope        decoupled RoPE width d_R (even)
+ *   d_nope        per-head NoPE query/key width (contracted with W_UK)
+ *   d_v           per-head output width (rows of W_UV)
+ *   block_size    tokens per cache block (the paging unit)
+ *   softmax_scale scale applied to q.k before the softmax (1/sqrt(d_nope + d_rope))
+ *   rope_base     RoPE base: pair i of a vector at position p turns by
+ *                 p * rope_base^(-2i/d_rope) radians.  The angle is formed in
+ *                 float64, its cos/sin are rounded to float32, and the rotated
+ *                 pair (x cos - y sin, x sin + y cos) is formed in float64 and
+ *                 rounded to the storage type.
+ *   act_dtype     dtype of q_nope, q_rope, c_kv, k_rope, W_UK, W_UV, q_abs,
+ *                 o_latent and out: MLA_F32 or MLA_BF16
+ *   cache_dtype   MLA_F32 (needs act F32), MLA_BF16 (needs act BF16) or
+ *                 MLA_FP8_E4M3 (needs act BF16)
+ *
+ * Cache pool layout: n_pool_blocks blocks of block_bytes each (see
+ * mla_cache_block_bytes), block b starting at byte b * block_bytes.
+ *   F32 / BF16 cache: a block is [block_size][d_c + d_rope] elements; row t of
+ *     block holds [c_KV | RoPE(k_R)] of one token.
+ *   FP8 cache: a block is [block_size][d_c] E4M3FN codes, then [block_size]
+ *     float32 scales, then [block_size][d_rope] bf16 rotated k_R.  A token's
+ *     latent is code * scale, scale = amax(|c_KV|)/448 (1 when amax is 0).
+ */
+typedef struct {
+  int32_t n_heads, d_c, d_rope, d_nope, d_v, block_size;
+  float softmax_scale;
+  float rope_base;
+  int32_t act_dtype;
+  int32_t cache_dtype;
+} mla_dims;
+
+/* Bytes of one cache block for these dims (0 if the dims are invalid). */
+size_t mla_cache_block_bytes(const mla_dims* dims);
+
+/* Human-readable text for a status code (static storage, never NULL). */
+const char* mla_status_string(mla_status status);
+
+/*
+ * mla_absorb_q -- absorb W_UK into the query and rotate the RoPE part
+ * ("Transformer升级之路：21、MLA好在哪里？（下）", 双重投影, decoding column:
+ * q = x W_q W_k^T; "DeepSeek-V3 解读", 为什么需要解耦 RoPE: RoPE on q_R).
+ *   q_abs[t, s, 0:d_c]          = sum_n q_nope[t, s, n] * w_uk[s, n, :]
+ *   q_abs[t, s, d_c:d_c+d_rope] = RoPE(q_rope[t, s, :], pos[t])
+ * Shapes: q_nope [n_tok, H, d_nope], q_rope [n_tok, H, d_rope] (unrotated),
+ * pos [n_tok] int32 (>= 0), w_uk [H, d_nope, d_c], q_abs [n_tok, H, d_c + d_rope]
+ * (output, act dtype; accumulation in float32).  n_tok may be 0 (no launch).
+ */
+mla_status mla_absorb_q(const mla_dims* dims, int32_t n_tok, const void* q_nope,
+                        const void* q_rope, const int32_t* pos, const void* w_uk,
+                        void* q_abs, mla_stream_t stream);
+
+/*
+ * mla_append_cache -- write new tokens into the paged latent cache
+ * ("DeepSeek-V3 解读", 为什么需要解耦 RoPE: the cached variables are the latent
+ * and the rotated shared key; FlashMLA snippet: block_table addressing).
+ * Token n (sequence seq_id[n], position pos[n]) is stored in physical block
+ * block_table[seq_id[n] * max_blocks + pos[n] / block_size], row
+ * pos[n] % block_size, as [c_kv[n] | RoPE(k_rope[n], pos[n])] at the cache
+ * dtype (FP8: per-token scale, RNE-saturated E4M3FN codes, bf16 rotated k_R).
+ * Shapes: c_kv [n_tok, d_c], k_rope [n_tok, d_rope] (act dtype, unrotated),
+ * seq_id/pos [n_tok] int32, block_table [n_seq, max_blocks] int32,
+ * cache_pool: n_pool_blocks blocks.  A token whose sequence id is outside
+ * [0, n_seq), whose position is negative or beyond the table, or whose block
+ * entry is < 0 or >= n_pool_blocks is skipped.  Nothing else in the pool is
+ * written.  Two tokens with the same (sequence, position) in one call race.
+ */
+mla_status mla_append_cache(const mla_dims* dims, int32_t n_tok, const void* c_kv,
+                            const void* k_rope, const int32_t* seq_id, const int32_t* pos,
+                            const int32_t* block_table, int32_t n_seq, int32_t max_blocks,
+                            void* cache_pool, int64_t n_pool_blocks, mla_stream_t stream);
+
+/*
+ * Workspace bytes mla_decode/mla_combine need for this problem (host only, no
+ * launch).  `max_blocks` is the block-table row length and bounds every
+ * sequence length; `num_splits` as for mla_decode (0 = automatic).
+ */
+size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
+                                  int32_t max_blocks, int32_t num_splits);
+
+/*
+ * mla_decode -- latent attention, the absorbed form ("Transformer升级之路：21、
+ * MLA好在哪里？（下）", 双重投影, decoding column: every head attends with key
+ * [c | k_R] and value c, shared by all heads).
+ * For sequence b with L = cache_seqlens[b] cached tokens (the q_per_seq new
+ * tokens included, already appended), query row j sits at position
+ * p = L - q_per_seq + j and sees tokens 0..p:
+ *   z_t  = softmax_scale * <q_abs[b, j, s, :], [c_t | kR_t]>
+ *   lse  = ln sum_t exp(z_t)
+ *   o_lat[b, j, s, :] = sum_t exp(z_t - lse) * c_t
+ * Shapes: q_abs [n_seq, q_per_seq, H, d_c + d_rope] (act), cache_seqlens
+ * [n_seq] int32 with q_per_seq <= L <= max_blocks * block_size,
+ * block_table [n_seq, max_blocks].  Outputs o_latent [n_seq, q_per_seq, H, d_c]
+ * (act) and lse [n_seq, q_per_seq, H] (float32).
+ * The key range may be split over work-groups ("num_splits": 0 = automatic,
+ * > 0 = that many work units); the partial results then go to `workspace`
+ * (at least mla_decode_workspace_bytes) and mla_combine must follow with the
+ * same arguments.  Whether mla_combine has work is reported by
+ * mla_decode_needs_combine; calling it when it has none is a cheap no-op.
+ */
+mla_status mla_decode(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
+                      const void* q_abs, const void* cache_pool, const int32_t* block_table,
+                      int32_t max_blocks, const int32_t* cache_seqlens, int32_t num_splits,
+                      void* workspace, size_t workspace_bytes, void* o_latent, float* lse,
+                      mla_stream_t stream);
+
+/* 1 if mla_decode with these arguments leaves partials for mla_combine, else 0. */
+int32_t mla_decode_needs_combine(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
+                                 int32_t max_blocks, int32_t num_splits);
+
+/*
+ * mla_combine -- merge split partials by log-sum-exp (FlashMLA snippet: the
+ * (o, lse) pair per split): lse = ln sum_k exp(lse_k),
+ * o_lat = sum_k exp(lse_k - lse) o_k; a split that saw no token has
+ * lse_k = -inf and weight 0.  Arguments as passed to mla_decode.
+ */
+mla_status mla_combine(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
+                       const int32_t* cache_seqlens, int32_t max_blocks, int32_t num_splits,
+                       const void* workspace, size_t workspace_bytes, void* o_latent, float* lse,
+                       mla_stream_t stream);
+
+/*
+ * mla_up_proj -- move W_UV back onto the output ("Transformer升级之路：21、
+ * MLA好在哪里？（下）", 双重投影, decoding column: o = [o^(1) W_v^(1), ...]).
+ *   out[t, s, v] = sum_c w_uv[s, v, c] * o_latent[t, s, c]
+ * Shapes: o_latent [n_tok, H, d_c], w_uv [H, d_v, d_c], out [n_tok, H, d_v]
+ * (act dtype; accumulation in float32).  n_tok may be 0 (no launch).
+ */
+mla_status mla_up_proj(const mla_dims* dims, int32_t n_tok, const void* o_latent,
+                       const void* w_uv, void* out, mla_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MLA_H_ */

@@ -1,0 +1,10 @@
+"""MLA decoding over a paged latent KV cache on MI355X (gfx950).
+
+The compute lives in libmla.so (HIP kernels behind the C ABI of
+include/mla.h); this package is its Python binding.
+"""
+from .binding import (  # noqa: F401
+    BF16, F32, FP8_E4M3, Dims, MLAError, absorb_q, append_cache, cache_block_bytes, combine, decode,
+    decode_needs_combine, decode_workspace_bytes, load_library, make_dims, up_proj,
+)
+from .pipeline import DecodeStep  # noqa: F401

@@ -1,0 +1,220 @@
+// C ABI of libmla: host-side validation, decode planning and dispatch.  Every
+// entry point checks its arguments before launching anything and returns a
+// status; no C++ exception crosses the boundary.
+#include <cmath>
+#include <cstring>
+
+#include "mla_internal.h"
+#include "decode_latent576.h"
+
+namespace mla {
+
+RopeFreqs make_rope_freqs(const mla_dims& d) {
+  RopeFreqs f;
+  std::memset(&f, 0, sizeof(f));
+  for (int i = 0; i < d.d_rope / 2; ++i)
+    f.inv_freq[i] = std::pow(static_cast<double>(d.rope_base), -(2.0 * i) / static_cast<double>(d.d_rope));
+  return f;
+}
+
+mla_status launch_status() { return hipGetLastError() == hipSuccess ? MLA_OK : MLA_ERR_LAUNCH; }
+
+int device_cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 256;
+  return n;
+}
+
+namespace {
+
+bool dims_valid(const mla_dims* d) {
+  if (!d) return false;
+  if (d->n_heads <= 0 || d->d_c <= 0 || d->d_rope < 0 || (d->d_rope & 1) || d->d_nope <= 0 || d->d_v <= 0 ||
+      d->block_size <= 0)
+    return false;
+  if (!(std::isfinite(d->softmax_scale) && d->softmax_scale > 0.f)) return false;
+  if (d->d_rope > 0 && !(std::isfinite(d->rope_base) && d->rope_base > 0.f)) return false;
+  if (d->act_dtype != MLA_F32 && d->act_dtype != MLA_BF16) return false;
+  if (d->cache_dtype != MLA_F32 && d->cache_dtype != MLA_BF16 && d->cache_dtype != MLA_FP8_E4M3) return false;
+  return true;
+}
+
+// dtype pairing and the size limits of the kernels
+mla_status dims_supported(const mla_dims* d) {
+  if (!dims_valid(d)) return MLA_ERR_INVALID_ARG;
+  if (d->cache_dtype == MLA_F32 && d->act_dtype != MLA_F32) return MLA_ERR_UNSUPPORTED;
+  if (d->cache_dtype != MLA_F32 && d->act_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (d->d_rope / 2 > kMaxRopePairs) return MLA_ERR_UNSUPPORTED;
+  if (d->d_c > 4096 || d->d_c + d->d_rope > 8192 || d->d_nope > 8192 || d->d_v > 65535) return MLA_ERR_UNSUPPORTED;
+  if (d->n_heads > 65535) return MLA_ERR_UNSUPPORTED;
+  if (d->cache_dtype == MLA_FP8_E4M3 && (d->d_c % 4) != 0) return MLA_ERR_UNSUPPORTED;  // fp32 scales stay aligned
+  return MLA_OK;
+}
+
+// Whether the tuned gfx950 kernel handles these dims and this query count.
+bool tuned_decode_applies(const mla_dims& d, int32_t q_per_seq) {
+  return decode576_supported(d, q_per_seq);
+}
+
+DecodePlan make_plan(const mla_dims& d, int32_t n_seq, int32_t q_per_seq, int32_t max_blocks, int32_t num_splits) {
+  DecodePlan p;
+  std::memset(&p, 0, sizeof(p));
+  const int64_t max_len = static_cast<int64_t>(max_blocks) * d.block_size;
+  if (tuned_decode_applies(d, q_per_seq)) {
+    p.kind = 1;
+    const int64_t tiles_bound = static_cast<int64_t>(n_seq) * ((max_len + kDecodeTile - 1) / kDecodeTile);
+    int64_t units = num_splits > 0 ? num_splits : decode576_default_units(n_seq, q_per_seq, device_cu_count());
+    if (units > tiles_bound) units = tiles_bound;
+    if (units < 1) units = 1;
+    p.n_splits = static_cast<int32_t>(units);
+    p.layout.mode = 1;
+    p.layout.n_splits = p.n_splits;
+    p.layout.tile = kDecodeTile;
+    p.n_slots = p.n_splits + n_seq;
+    p.needs_combine = p.n_splits > 1 ? 1 : 0;
+  } else {
+    p.kind = 0;
+    int64_t s = num_splits;
+    if (s <= 0) {
+      const int64_t rows = static_cast<int64_t>(n_seq) * q_per_seq * d.n_heads;
+      const int64_t want = (2LL * device_cu_count() + rows - 1) / rows;
+      const int64_t cap = (max_len + 255) / 256;
+      s = want < cap ? want : cap;
+    }
+    if (s > kMaxCombineSlots) s = kMaxCombineSlots;
+    if (s < 1) s = 1;
+    p.n_splits = static_cast<int32_t>(s);
+    p.layout.mode = 0;
+    p.layout.n_splits = p.n_splits;
+    p.layout.tile = 0;
+    p.n_slots = p.n_splits > 1 ? n_seq * p.n_splits : 0;
+    p.needs_combine = p.n_splits > 1 ? 1 : 0;
+  }
+  const int64_t rows_per_slot = static_cast<int64_t>(q_per_seq) * d.n_heads;
+  p.ws_lse_offset_floats = static_cast<int64_t>(p.n_slots) * rows_per_slot * d.d_c;
+  p.ws_bytes = p.n_slots ? static_cast<size_t>(p.ws_lse_offset_floats + p.n_slots * rows_per_slot) * sizeof(float) : 0;
+  return p;
+}
+
+mla_status check_decode_args(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, int32_t max_blocks,
+                             int32_t num_splits) {
+  const mla_status s = dims_supported(d);
+  if (s != MLA_OK) return s;
+  if (n_seq <= 0 || q_per_seq <= 0 || max_blocks <= 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
+  if (static_cast<int64_t>(max_blocks) * d->block_size > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(n_seq) * q_per_seq * d->n_heads > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
+  return MLA_OK;
+}
+
+}  // namespace
+}  // namespace mla
+
+using namespace mla;
+
+extern "C" {
+
+size_t mla_cache_block_bytes(const mla_dims* d) {
+  if (!dims_valid(d)) return 0;
+  const size_t bs = static_cast<size_t>(d->block_size);
+  switch (d->cache_dtype) {
+    case MLA_F32: return bs * (d->d_c + d->d_rope) * 4;
+    case MLA_BF16: return bs * (d->d_c + d->d_rope) * 2;
+    case MLA_FP8_E4M3: return bs * d->d_c + bs * 4 + bs * d->d_rope * 2;
+    default: return 0;
+  }
+}
+
+const char* mla_status_string(mla_status s) {
+  switch (s) {
+    case MLA_OK: return "ok";
+    case MLA_ERR_INVALID_ARG: return "invalid argument";
+    case MLA_ERR_UNSUPPORTED: return "unsupported dims or dtype combination";
+    case MLA_ERR_WORKSPACE: return "workspace missing or too small";
+    case MLA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+mla_status mla_absorb_q(const mla_dims* d, int32_t n_tok, const void* q_nope, const void* q_rope,
+                        const int32_t* pos, const void* w_uk, void* q_abs, mla_stream_t stream) {
+  const mla_status s = dims_supported(d);
+  if (s != MLA_OK) return s;
+  if (n_tok < 0) return MLA_ERR_INVALID_ARG;
+  if (n_tok == 0) return MLA_OK;
+  if (!q_nope || !w_uk || !q_abs || (d->d_rope > 0 && (!q_rope || !pos))) return MLA_ERR_INVALID_ARG;
+  if (n_tok > 2147483647 / d->n_heads) return MLA_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (absorb_tuned_applies(*d)) return launch_absorb_tuned(*d, n_tok, q_nope, q_rope, pos, w_uk, q_abs, st);
+  return launch_absorb_generic(*d, n_tok, q_nope, q_rope, pos, w_uk, q_abs, st);
+}
+
+mla_status mla_append_cache(const mla_dims* d, int32_t n_tok, const void* c_kv, const void* k_rope,
+                            const int32_t* seq_id, const int32_t* pos, const int32_t* block_table, int32_t n_seq,
+                            int32_t max_blocks, void* cache_pool, int64_t n_pool_blocks, mla_stream_t stream) {
+  const mla_status s = dims_supported(d);
+  if (s != MLA_OK) return s;
+  if (n_tok < 0 || n_seq <= 0 || max_blocks <= 0 || n_pool_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (n_tok == 0) return MLA_OK;
+  if (!c_kv || !seq_id || !pos || !block_table || !cache_pool || (d->d_rope > 0 && !k_rope))
+    return MLA_ERR_INVALID_ARG;
+  return launch_append_generic(*d, n_tok, c_kv, k_rope, seq_id, pos, block_table, n_seq, max_blocks, cache_pool,
+                               n_pool_blocks, static_cast<hipStream_t>(stream));
+}
+
+size_t mla_decode_workspace_bytes(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, int32_t max_blocks,
+                                  int32_t num_splits) {
+  if (check_decode_args(d, n_seq, q_per_seq, max_blocks, num_splits) != MLA_OK) return 0;
+  return make_plan(*d, n_seq, q_per_seq, max_blocks, num_splits).ws_bytes;
+}
+
+int32_t mla_decode_needs_combine(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, int32_t max_blocks,
+                                 int32_t num_splits) {
+  if (check_decode_args(d, n_seq, q_per_seq, max_blocks, num_splits) != MLA_OK) return 0;
+  return make_plan(*d, n_seq, q_per_seq, max_blocks, num_splits).needs_combine;
+}
+
+mla_status mla_decode(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const void* q_abs,
+                      const void* cache_pool, const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* cache_seqlens, int32_t num_splits, void* workspace, size_t workspace_bytes,
+                      void* o_latent, float* lse, mla_stream_t stream) {
+  const mla_status s = check_decode_args(d, n_seq, q_per_seq, max_blocks, num_splits);
+  if (s != MLA_OK) return s;
+  if (!q_abs || !cache_pool || !block_table || !cache_seqlens || !o_latent || !lse) return MLA_ERR_INVALID_ARG;
+  const DecodePlan plan = make_plan(*d, n_seq, q_per_seq, max_blocks, num_splits);
+  if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.kind == 1)
+    return launch_decode576(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, block_table, max_blocks, cache_seqlens,
+                            workspace, o_latent, lse, st);
+  return launch_decode_generic(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, block_table, max_blocks,
+                               cache_seqlens, plan.ws_bytes ? workspace : nullptr, o_latent, lse, st);
+}
+
+mla_status mla_combine(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const int32_t* cache_seqlens,
+                       int32_t max_blocks, int32_t num_splits, const void* workspace, size_t workspace_bytes,
+                       void* o_latent, float* lse, mla_stream_t stream) {
+  const mla_status s = check_decode_args(d, n_seq, q_per_seq, max_blocks, num_splits);
+  if (s != MLA_OK) return s;
+  if (!cache_seqlens || !o_latent || !lse) return MLA_ERR_INVALID_ARG;
+  const DecodePlan plan = make_plan(*d, n_seq, q_per_seq, max_blocks, num_splits);
+  if (!plan.needs_combine) return MLA_OK;
+  if (!workspace || workspace_bytes < plan.ws_bytes) return MLA_ERR_WORKSPACE;
+  return launch_combine(*d, plan, n_seq, q_per_seq, cache_seqlens, workspace, o_latent, lse,
+                        static_cast<hipStream_t>(stream));
+}
+
+mla_status mla_up_proj(const mla_dims* d, int32_t n_tok, const void* o_latent, const void* w_uv, void* out,
+                       mla_stream_t stream) {
+  const mla_status s = dims_supported(d);
+  if (s != MLA_OK) return s;
+  if (n_tok < 0) return MLA_ERR_INVALID_ARG;
+  if (n_tok == 0) return MLA_OK;
+  if (!o_latent || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  if (n_tok > 2147483647 / d->n_heads) return MLA_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (up_proj_tuned_applies(*d)) return launch_up_proj_tuned(*d, n_tok, o_latent, w_uv, out, st);
+  return launch_up_proj_generic(*d, n_tok, o_latent, w_uv, out, st);
+}
+
+}  // extern "C"

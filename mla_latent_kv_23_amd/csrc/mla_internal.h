@@ -1,0 +1,106 @@
+// Internal declarations of libmla: decode plans, the partial-slot layout the
+// decode and combine kernels agree on, and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "mla.h"
+#include "mla_device.h"
+
+namespace mla {
+
+constexpr int kMaxCombineSlots = 1024;   // partial results merged per (sequence, row, head)
+
+// Where the partial results of sequence b live in the workspace.
+//   kPerSequence: n_splits slots per sequence, slots b*n_splits .. +n_splits-1,
+//                 split k covers keys [k*ceil(L/n), (k+1)*ceil(L/n)).
+//   kStreamTiles: the key tiles of all sequences are laid end to end (sequence
+//                 major, ceil(L_b / tile) tiles each) and cut into n_units equal
+//                 runs; unit w handles tiles [floor(w*N/G), floor((w+1)*N/G)).
+//                 The piece of sequence b done by unit w has slot w + b (unique
+//                 because both indices only grow along the tile order).  A
+//                 sequence that lies inside one unit gets its final output
+//                 written directly and has no slots.
+struct SplitLayout {
+  int32_t mode;      // 0 = kPerSequence, 1 = kStreamTiles
+  int32_t n_splits;  // kPerSequence: splits per sequence; kStreamTiles: units G
+  int32_t tile;      // kStreamTiles: tokens per tile
+};
+
+struct DecodePlan {
+  int32_t kind;                  // 0 = generic kernel, 1 = tuned gfx950 latent-576 kernel
+  int32_t n_splits;              // generic: splits per sequence; tuned: work units
+  int32_t n_slots;               // partial slots in the workspace (0 = none)
+  int32_t needs_combine;         // partials are written (combine has work)
+  int64_t ws_lse_offset_floats;  // lse partials start here (floats from workspace start)
+  size_t ws_bytes;               // workspace bytes needed
+  SplitLayout layout;
+};
+
+// Unit w of G over N tiles: first tile floor(w*N/G).
+__host__ __device__ __forceinline__ int64_t unit_first_tile(int64_t w, int64_t N, int64_t G) { return w * N / G; }
+// The unit that holds tile T.
+__host__ __device__ __forceinline__ int64_t unit_of_tile(int64_t T, int64_t N, int64_t G) {
+  return ((T + 1) * G - 1) / N;
+}
+
+// Slot range of sequence b; for kStreamTiles `count` spans units first..last.
+struct SlotRange {
+  int first, count;        // slots first .. first+count-1 (count 0: no partials)
+  int64_t unit0, n_tiles;  // kStreamTiles: unit of slot `first`, total tiles
+};
+
+// Whether slot first+k of a range holds a partial (kStreamTiles units with no
+// tile at all write nothing).
+__device__ __forceinline__ bool slot_used(const SplitLayout& lay, const SlotRange& r, int k) {
+  if (lay.mode == 0) return true;
+  const int64_t w = r.unit0 + k;
+  return unit_first_tile(w, r.n_tiles, lay.n_splits) < unit_first_tile(w + 1, r.n_tiles, lay.n_splits);
+}
+
+__device__ __forceinline__ SlotRange slot_range(const SplitLayout& lay, const int32_t* seqlens, int n_seq, int b) {
+  SlotRange r;
+  if (lay.mode == 0) {
+    r.first = b * lay.n_splits;
+    r.count = lay.n_splits;
+    r.unit0 = 0;
+    r.n_tiles = 0;
+    return r;
+  }
+  int64_t start = 0, total = 0;
+  for (int i = 0; i < n_seq; ++i) {
+    const int64_t nt = (static_cast<int64_t>(seqlens[i]) + lay.tile - 1) / lay.tile;
+    if (i < b) start += nt;
+    total += nt;
+  }
+  const int64_t nb = (static_cast<int64_t>(seqlens[b]) + lay.tile - 1) / lay.tile;
+  const int64_t wf = unit_of_tile(start, total, lay.n_splits);
+  const int64_t wl = unit_of_tile(start + nb - 1, total, lay.n_splits);
+  r.first = static_cast<int>(wf + b);
+  r.count = (wf == wl) ? 0 : static_cast<int>(wl - wf + 1);
+  r.unit0 = wf;
+  r.n_tiles = total;
+  return r;
+}
+
+RopeFreqs make_rope_freqs(const mla_dims& d);
+mla_status launch_status();
+int device_cu_count();
+
+mla_status launch_absorb_generic(const mla_dims& d, int32_t n_tok, const void* q_nope, const void* q_rope,
+                                 const int32_t* pos, const void* w_uk, void* q_abs, hipStream_t st);
+mla_status launch_append_generic(const mla_dims& d, int32_t n_tok, const void* c_kv, const void* k_rope,
+                                 const int32_t* seq_id, const int32_t* pos, const int32_t* block_table,
+                                 int32_t n_seq, int32_t max_blocks, void* pool, int64_t n_pool_blocks,
+                                 hipStream_t st);
+mla_status launch_decode_generic(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
+                                 const void* q_abs, const void* pool, const int32_t* block_table,
+                                 int32_t max_blocks, const int32_t* seqlens, void* ws, void* o_lat, float* lse,
+                                 hipStream_t st);
+mla_status launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
+                          const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st);
+mla_status launch_up_proj_generic(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv,
+                                  void* out, hipStream_t st);
+
+}  // namespace mla

@@ -1,0 +1,45 @@
+"""One MLA decode step for one layer, as the five library calls in order:
+absorb the query, append the new tokens to the paged cache, attend over the
+latent cache, merge the key splits, project back to per-head outputs.
+
+Buffers are allocated once per shape; `run()` only enqueues library calls on
+the current stream.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class DecodeStep:
+    def __init__(self, dims: B.Dims, n_seq: int, q_per_seq: int, max_blocks: int, num_splits: int = 0,
+                 device="cuda"):
+        self.d, self.n_seq, self.q_per_seq = dims, n_seq, q_per_seq
+        self.max_blocks, self.num_splits = max_blocks, num_splits
+        at = B.act_torch_dtype(dims)
+        n_tok = n_seq * q_per_seq
+        H = dims.n_heads
+        self.q_abs = torch.empty((n_seq, q_per_seq, H, dims.d_c + dims.d_rope), dtype=at, device=device)
+        self.o_latent = torch.empty((n_seq, q_per_seq, H, dims.d_c), dtype=at, device=device)
+        self.lse = torch.empty((n_seq, q_per_seq, H), dtype=torch.float32, device=device)
+        self.out = torch.empty((n_tok, H, dims.d_v), dtype=at, device=device)
+        ws = B.decode_workspace_bytes(dims, n_seq, q_per_seq, max_blocks, num_splits)
+        self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
+        self.needs_combine = B.decode_needs_combine(dims, n_seq, q_per_seq, max_blocks, num_splits)
+
+    def run(self, *, q_nope, q_rope, q_pos, new_c_kv, new_k_rope, new_seq_id, new_pos, block_table, seqlens,
+            pool, w_uk, w_uv, stream=None):
+        """q_nope/q_rope [n_seq*q_per_seq, H, *]; q_pos [n_seq*q_per_seq]; new_* the tokens to append."""
+        d = self.d
+        n_tok = self.n_seq * self.q_per_seq
+        B.absorb_q(d, q_nope, q_rope, q_pos, w_uk, q_abs=self.q_abs.view(n_tok, d.n_heads, -1), stream=stream)
+        if new_c_kv is not None and new_c_kv.shape[0] > 0:
+            B.append_cache(d, new_c_kv, new_k_rope, new_seq_id, new_pos, block_table, pool, stream=stream)
+        B.decode(d, self.q_abs, pool, block_table, seqlens, self.num_splits, self.workspace, self.o_latent,
+                 self.lse, stream=stream)
+        if self.needs_combine:
+            B.combine(d, seqlens, self.max_blocks, self.workspace, self.o_latent, self.lse, self.num_splits,
+                      stream=stream)
+        B.up_proj(d, self.o_latent.view(n_tok, d.n_heads, d.d_c), w_uv, out=self.out, stream=stream)
+        return self.out, self.o_latent, self.lse
