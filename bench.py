@@ -1,0 +1,197 @@
+"""Benchmark: one MLA decode step (absorb -> append -> decode -> combine ->
+up-projection) per layer on one MI355X, on the DeepSeek-V3-shape workload
+(64 sequences x 8192 cached tokens, 128 heads, 512-wide latent + 64-wide RoPE
+key, bf16, 64-token paged blocks with a shuffled block table).
+
+Prints one JSON line.  `value` is whole-step throughput (query tokens per
+second) with every input resident in HBM.  `roofline` reports the decode
+kernel (the dominant one) against the HBM bound: algorithmic bytes = the
+cache read once (1152 B per cached token), divided by the decode launch time
+measured with HIP events around each decode launch inside the timed region.
+`cpu_baseline` times the CPU oracle (non-absorbed form, float64) on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="v3_bs64_ctx8k")
+    ap.add_argument("--num-splits", type=int, default=0)
+    ap.add_argument("--cpu-sample-seqs", type=int, default=2,
+                    help="sequences of the workload the CPU oracle is timed on (0 = skip)")
+    ap.add_argument("--decode-only", action="store_true",
+                    help="time only the decode+combine calls (for profiling)")
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(every box here has a single MI355X)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import mla_latent_kv_23_amd as M
+    import mla_synth as S
+
+    w = S.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = S.make_inputs(w, S.SEEDS[w.name])
+    d = M.make_dims(n_heads=w.n_heads, d_c=w.d_c, d_rope=w.d_rope, d_nope=w.d_nope, d_v=w.d_v,
+                    block_size=w.block_size, softmax_scale=w.softmax_scale, rope_base=w.rope_base,
+                    act_dtype=w.act_dtype, cache_dtype=w.cache_dtype)
+    B, sq, H = w.batch, w.q_per_seq, w.n_heads
+    n_tok = B * sq
+    bb = M.cache_block_bytes(d)
+    pool = torch.full((inp["n_blocks"] * bb,), 0xFF, dtype=torch.uint8, device=dev)
+    table = inp["block_table"].to(dev)
+    seqlens = inp["seqlens"].to(dev)
+    new_rows = S.new_token_rows(inp, sq)
+    hist = torch.ones(inp["c_kv"].shape[0], dtype=torch.bool)
+    hist[new_rows] = False
+    hist_rows = torch.nonzero(hist)[:, 0]
+    # the history is appended once, outside the timed region
+    M.append_cache(d, inp["c_kv"][hist_rows].to(dev), inp["k_rope"][hist_rows].to(dev),
+                   inp["tok_seq"][hist_rows].to(dev), inp["tok_pos"][hist_rows].to(dev), table, pool)
+    step_inputs = dict(
+        q_nope=inp["q_nope"].reshape(n_tok, H, -1).to(dev), q_rope=inp["q_rope"].reshape(n_tok, H, -1).to(dev),
+        q_pos=S.query_positions(inp["seqlens"], sq).reshape(-1).to(dev),
+        new_c_kv=inp["c_kv"][new_rows].to(dev), new_k_rope=inp["k_rope"][new_rows].to(dev),
+        new_seq_id=inp["tok_seq"][new_rows].to(dev), new_pos=inp["tok_pos"][new_rows].to(dev),
+        block_table=table, seqlens=seqlens, pool=pool, w_uk=inp["w_uk"].to(dev), w_uv=inp["w_uv"].to(dev))
+    step = M.DecodeStep(d, B, sq, table.shape[1], num_splits=args.num_splits, device=dev)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    stream = torch.cuda.current_stream()
+
+    def run_step(ev_pair=None):
+        if args.decode_only:
+            if ev_pair:
+                ev_pair[0].record(stream)
+            M.decode(d, step.q_abs, pool, table, seqlens, args.num_splits, step.workspace, step.o_latent,
+                     step.lse, stream=stream)
+            if ev_pair:
+                ev_pair[1].record(stream)
+            if step.needs_combine:
+                M.combine(d, seqlens, table.shape[1], step.workspace, step.o_latent, step.lse,
+                          args.num_splits, stream=stream)
+            return
+        dd = step.d
+        M.absorb_q(dd, step_inputs["q_nope"], step_inputs["q_rope"], step_inputs["q_pos"], step_inputs["w_uk"],
+                   q_abs=step.q_abs.view(n_tok, H, -1), stream=stream)
+        M.append_cache(dd, step_inputs["new_c_kv"], step_inputs["new_k_rope"], step_inputs["new_seq_id"],
+                       step_inputs["new_pos"], table, pool, stream=stream)
+        if ev_pair:
+            ev_pair[0].record(stream)
+        M.decode(dd, step.q_abs, pool, table, seqlens, args.num_splits, step.workspace, step.o_latent,
+                 step.lse, stream=stream)
+        if ev_pair:
+            ev_pair[1].record(stream)
+        if step.needs_combine:
+            M.combine(dd, seqlens, table.shape[1], step.workspace, step.o_latent, step.lse, args.num_splits,
+                      stream=stream)
+        M.up_proj(dd, step.o_latent.view(n_tok, H, -1), step_inputs["w_uv"], out=step.out, stream=stream)
+
+    if args.decode_only:   # the queries must exist once
+        M.absorb_q(d, step_inputs["q_nope"], step_inputs["q_rope"], step_inputs["q_pos"], step_inputs["w_uk"],
+                   q_abs=step.q_abs.view(n_tok, H, -1), stream=stream)
+    for _ in range(args.warmup):
+        run_step()
+    torch.cuda.synchronize()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(args.steps):
+        run_step(evs[i])
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / args.steps
+    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+
+    total_tokens = int(inp["seqlens"].to(torch.int64).sum())
+    cache_bytes = total_tokens * (bb // w.block_size)              # the cache read once
+    visible = sum(int(L) - sq + j + 1 for L in inp["seqlens"].tolist() for j in range(sq))
+    flops = visible * H * (2 * (w.d_c + w.d_rope) + 2 * w.d_c)
+    dec_gbps = cache_bytes / (dec_ms * 1e-3) / 1e9
+    dec_tflops = flops / (dec_ms * 1e-3) / 1e12
+    tokens_per_s = n_tok / (ms_step * 1e-3)
+
+    cpu = None
+    if args.cpu_sample_seqs > 0:
+        cpu = cpu_baseline(w, inp, args.cpu_sample_seqs)
+
+    rec = {
+        "metric": "MLA decode tokens/sec and achieved HBM GB/s (% peak), V3-shape bs64 ctx8k",
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.act_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(d_c)) weights)",
+        "config": {"workload": w.name, "batch": B, "q_per_seq": sq, "n_heads": H, "d_c": w.d_c,
+                   "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v, "seqlen": w.seqlen,
+                   "block_size": w.block_size, "cache_dtype": w.cache_dtype, "parallelism": "single GPU"},
+        "decode_ms": round(dec_ms, 4),
+        "decode_hbm_gbps": round(dec_gbps, 1),
+        "decode_tflops": round(dec_tflops, 1),
+        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "kernel": "decode576_kernel", "bytes_per_launch": cache_bytes,
+                     "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(w, inp, n_seqs):
+    """The oracle (non-absorbed, float64) on the first n_seqs sequences, all heads."""
+    import numpy as np
+    import torch
+
+    from oracle import mla_oracle as O
+    seqs = list(range(min(n_seqs, w.batch)))
+    t0 = time.time()
+    O.decode_batch(inp, q_per_seq=w.q_per_seq, scale=w.softmax_scale, base=w.rope_base,
+                   cache_dtype=w.cache_dtype, seqs=seqs)
+    dt = time.time() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max(int(p.get("num_threads", 1)) for p in threadpool_info()) if threadpool_info() else 1
+    except Exception:
+        cores = torch.get_num_threads()
+    return {"value": round(len(seqs) * w.q_per_seq / dt, 4), "unit": "tokens/s", "cores": cores,
+            "kind": "oracle",
+            "sample": f"{len(seqs)} of {w.batch} sequences x {w.q_per_seq} query rows, all {w.n_heads} heads, "
+                      f"{int(inp['seqlens'][0])} cached tokens each, float64 numpy ({dt:.1f} s)"}
+
+
+if __name__ == "__main__":
+    main()

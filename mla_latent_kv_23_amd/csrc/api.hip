@@ -71,7 +71,8 @@ DecodePlan make_plan(const mla_dims& d, int32_t n_seq, int32_t q_per_seq, int32_
     p.layout.mode = 1;
     p.layout.n_splits = p.n_splits;
     p.layout.tile = kDecodeTile;
-    p.n_slots = p.n_splits + n_seq;
+    p.layout.max_len = static_cast<int32_t>(max_len);
+    p.n_slots = p.n_splits + n_seq;       // also the staging area of whole sequences
     p.needs_combine = p.n_splits > 1 ? 1 : 0;
   } else {
     p.kind = 0;
@@ -88,12 +89,14 @@ DecodePlan make_plan(const mla_dims& d, int32_t n_seq, int32_t q_per_seq, int32_
     p.layout.mode = 0;
     p.layout.n_splits = p.n_splits;
     p.layout.tile = 0;
+    p.layout.max_len = static_cast<int32_t>(max_len);
     p.n_slots = p.n_splits > 1 ? n_seq * p.n_splits : 0;
     p.needs_combine = p.n_splits > 1 ? 1 : 0;
   }
   const int64_t rows_per_slot = static_cast<int64_t>(q_per_seq) * d.n_heads;
-  p.ws_lse_offset_floats = static_cast<int64_t>(p.n_slots) * rows_per_slot * d.d_c;
-  p.ws_bytes = p.n_slots ? static_cast<size_t>(p.ws_lse_offset_floats + p.n_slots * rows_per_slot) * sizeof(float) : 0;
+  p.ws_stats_offset_floats = static_cast<int64_t>(p.n_slots) * rows_per_slot * d.d_c;
+  p.ws_bytes =
+      p.n_slots ? static_cast<size_t>(p.ws_stats_offset_floats + 2LL * p.n_slots * rows_per_slot) * sizeof(float) : 0;
   return p;
 }
 
@@ -183,6 +186,7 @@ mla_status mla_decode(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const
   if (!q_abs || !cache_pool || !block_table || !cache_seqlens || !o_latent || !lse) return MLA_ERR_INVALID_ARG;
   const DecodePlan plan = make_plan(*d, n_seq, q_per_seq, max_blocks, num_splits);
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return MLA_ERR_WORKSPACE;
+  if (plan.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15)) return MLA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.kind == 1)
     return launch_decode576(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, block_table, max_blocks, cache_seqlens,

@@ -1,0 +1,488 @@
+// Tuned gfx950 latent-attention decode for a 512-wide latent plus a 64-wide
+// shared RoPE key in bf16 (the absorbed form of MLA: every head attends with
+// key [c | k_R] (576 wide) and value c (512 wide), shared by all heads).
+//
+// Work decomposition (one work-group = 4 waves = one per SIMD of a CU):
+//  * The key tiles (32 tokens) of all sequences are laid end to end and cut
+//    into `units` equal runs (stream-K); a run may cover several sequences or
+//    a piece of one.  A sequence lying inside one run gets its final output
+//    written here; otherwise each piece writes (o, lse) partials for the
+//    log-sum-exp combine.
+//  * A work-group serves 128 (query row, head) "pairs": all 128 heads of one
+//    query row, or 64 heads x 2 rows (grid.y picks the head group).
+//  * HBM -> LDS: each tile (32 rows x 1152 B, contiguous inside a paged block)
+//    is copied with 16-byte direct-to-LDS loads into a 4-stage ring, so up to
+//    three tiles are in flight while one is consumed.  In LDS a tile is a grid
+//    of 1 KB blocks, each holding 8 rows x 8 sixteen-byte chunks; inside a
+//    block the chunk position is XOR-swizzled by the row, which keeps both
+//    operand read patterns below free of LDS bank conflicts and lets one wave
+//    load a whole 1 KB block per instruction with a single per-lane offset.
+//  * S^T = K Q^T on bf16 MFMA 32x32x16: wave w owns pairs 32w..32w+31 and
+//    keeps their queries in registers as the B operand; the K tile is the A
+//    operand (one 16-byte LDS read per lane per k-step).
+//  * Online softmax in the exp2 domain against a per-pair reference max fixed
+//    by the first tile that shows the pair a key; P = 2^(z - ref) is rounded
+//    to bf16 and exchanged through LDS.  Should a later tile exceed the
+//    reference by more than 2^16, the reference is raised and the sequence
+//    piece is computed once more (never in practice; it keeps the result
+//    exact without ever rescaling the accumulators, which are only ever
+//    MFMA-updated, zeroed or stored raw).
+//  * O^T += V^T P^T on bf16 MFMA 32x32x16: wave w owns latent dims
+//    128w..128w+127 for all 128 pairs (fp32 accumulators, 256 per lane); V^T
+//    comes straight from the row-major tile with the LDS transpose read.
+#include <math.h>
+
+#include "decode_latent576.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+
+constexpr int kDc = 512, kDk = 576, kRowBytes = kDk * 2;   // bf16 cache row
+constexpr int kTile = kDecodeTile;                          // 32 tokens
+constexpr int kTileBytes = kTile * kRowBytes;               // 36864
+constexpr int kChunksPerRow = kRowBytes / 16;               // 72
+constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;        // 9 wave-wide 16-byte loads per wave per tile
+constexpr int kStages = 4;
+constexpr int kPairs = 128;
+constexpr int kPRow = 80;                                   // bytes per P row: 32 bf16 + 16 pad
+constexpr int kQSteps = kDk / 16;                           // 36 k-steps of the QK contraction
+
+constexpr int kOffP = kStages * kTileBytes;                 // 147456
+constexpr int kOffL = kOffP + kPairs * kPRow;               // 157696
+constexpr int kOffM = kOffL + kPairs * 4;                   // 158208
+constexpr int kOffFlag = kOffM + kPairs * 4;                // 158720
+constexpr int kOffScan = kOffFlag + 16;                     // 158736
+constexpr int kOffMisc = kOffScan + 4 * 4;                  // 158752
+constexpr int kLdsBytes = kOffMisc + 64;                    // 158816 <= 163840
+
+constexpr float kRestartThreshold = 16.0f;                  // log2 units: weights stay <= 2^16
+
+static_assert(kTile == 32, "the MFMA tiling below assumes 32-token tiles");
+static_assert(kLdsBytes <= 163840, "LDS budget of a gfx950 CU");
+
+struct Args {
+  const uint16_t* q_abs;        // [n_seq][q_per_seq][H][576] bf16
+  const uint8_t* pool;          // paged cache, block_bytes per block
+  uint16_t* o_final;            // [n_seq][q_per_seq][H][512] bf16
+  float* lse_final;             // [n_seq][q_per_seq][H]
+  float* ws_o;                  // partials [slots][q_per_seq*H][512], raw (relative to 2^m)
+  float* ws_stats;              // partials [slots][q_per_seq*H][2] = (m in log2 units, l)
+  int64_t block_bytes;
+  int32_t max_blocks, block_size, n_seq, q_per_seq, n_heads, units, heads_per_wg;
+  float scale_log2;             // softmax_scale * log2(e)
+};
+
+// LDS tile layout: row r, 16-byte chunk c lives in 1 KB block
+// (r / 8) * 9 + c / 8 at byte (r % 8) * 128 + 16 * ((c % 8) ^ swz(r % 8)).
+// swz is a permutation of 0..7 (16-byte reads of 8 rows at one chunk hit 8
+// different bank groups) and, within each aligned group of 4 rows, swz >> 1 is
+// a permutation of 0..3 (transpose reads of 4 rows x 32 bytes do not collide).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ uint32_t tile_off(int r, int c) {
+  return ((r >> 3) * 9 + (c >> 3)) * 1024 + (r & 7) * 128 + 16 * ((c & 7) ^ swz(r & 7));
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ int tiles_of(int32_t L) { return (L + kTile - 1) / kTile; }
+
+// wait until at most n tiles' worth of this wave's loads are still in flight
+__device__ __forceinline__ void wait_tiles(int64_t n) {
+  if (n >= 3) wait_vmcnt<3 * kLoadsPerWave>();
+  else if (n == 2) wait_vmcnt<2 * kLoadsPerWave>();
+  else if (n == 1) wait_vmcnt<kLoadsPerWave>();
+  else wait_vmcnt<0>();
+}
+
+// Copy one tile (32 rows starting at `src`) into LDS stage `dst`.  Wave w
+// loads rows 8w..8w+7: nine 1 KB blocks, one per instruction; lane l brings
+// row 8w + l/8, logical chunk 8i + ((l % 8) ^ swz(l / 8)).  Rows at or beyond
+// `valid` re-read row 0 (finite data; their probabilities are 0).
+__device__ __forceinline__ void issue_tile(const uint8_t* src, int valid, lds_u8* dst, int wave, int lane) {
+  const int rho = lane >> 3;
+  const int row = 8 * wave + rho;
+  const uint32_t lane_off = (row < valid ? row * kRowBytes : 0) + 16 * ((lane & 7) ^ swz(rho));
+#pragma unroll
+  for (int i = 0; i < kLoadsPerWave; ++i)
+    __builtin_amdgcn_global_load_lds(src + lane_off + 128 * i,
+                                     (__attribute__((address_space(3))) void*)(dst + (wave * kLoadsPerWave + i) * 1024),
+                                     16, 0, 0);
+}
+
+__global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t* __restrict__ block_table,
+                                                          const int32_t* __restrict__ seqlens) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
+  lds_u8* lds = (lds_u8*)lds_raw;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int unit = blockIdx.x, hg = blockIdx.y;
+  const int G = a.units;
+  const int32_t max_len = a.max_blocks * a.block_size;
+  // sequence length as used here: clamped to what the block table can address
+  auto seq_len = [&](int b) -> int32_t { return min(max(seqlens[b], 0), max_len); };
+
+  // ---- tiles per sequence: exclusive scan over sequences (chunked per thread)
+  const int chunk = (a.n_seq + 255) / 256;
+  const int s_lo = min(tid * chunk, a.n_seq), s_hi = min(s_lo + chunk, a.n_seq);
+  int local = 0;
+  for (int b = s_lo; b < s_hi; ++b) local += tiles_of(seq_len(b));
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += v;
+  }
+  lds_i32* scan = (lds_i32*)(lds + kOffScan);
+  if (lane == 63) scan[wave] = incl;
+  lds_barrier();
+  int wave_off = 0;
+  for (int w = 0; w < wave; ++w) wave_off += scan[w];
+  const int64_t N = (int64_t)scan[0] + scan[1] + scan[2] + scan[3];
+  const int excl = wave_off + incl - local;
+  const int64_t T0 = unit_first_tile(unit, N, G), T1 = unit_first_tile(unit + 1, N, G);
+  lds_i32* misc = (lds_i32*)(lds + kOffMisc);
+  if (local > 0 && T0 >= excl && T0 < excl + local) {
+    int start = excl, b = s_lo;
+    while (start + tiles_of(seq_len(b)) <= T0) { start += tiles_of(seq_len(b)); ++b; }
+    misc[0] = b;
+    misc[1] = start;
+  }
+  lds_barrier();
+  if (T0 >= T1) return;                    // an empty unit (more units than tiles)
+  int b_first = __builtin_amdgcn_readfirstlane(misc[0]);
+  int b_first_start = __builtin_amdgcn_readfirstlane(misc[1]);
+
+  // ---- per-wave identity of its 32 QK pairs; each lane owns pair 32*wave + lane%32
+  const int hpw = a.heads_per_wg;
+  const int my_pair = 32 * wave + (lane & 31);
+  const int my_j = my_pair / hpw;
+  const int my_s = hg * hpw + my_pair % hpw;
+  const int half = lane >> 5;
+  const int rows_per_seq = a.q_per_seq * a.n_heads;
+
+  // per-lane LDS byte offsets (within a tile / the P buffer) of the operand reads
+  uint32_t kq_base[4];                     // K rows: row lane%32, chunk 8*(k/4) + 2*(k%4) + half
+  {
+    const int r = lane & 31;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) kq_base[m] = tile_off(r, 2 * m + half);
+  }
+  uint32_t v_base[4];                      // V^T transpose reads, by (db & 1, hh), for ks = 0, db < 2
+  {
+    const int gi = lane >> 4, sp = lane & 15;
+    const int dim = 128 * wave + 16 * (gi & 1) + 4 * (sp & 3);   // + 32 db
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int row = 8 * (gi >> 1) + 4 * hh + (sp >> 2);     // + 16 ks
+        v_base[x * 2 + hh] = tile_off(row, (dim + 32 * x) >> 3) + ((dim & 7) << 1);
+      }
+  }
+  const uint32_t p_base = (uint32_t)(uintptr_t)(lds + kOffP) + (lane & 31) * kPRow + 16 * half;
+
+  const float sl2 = a.scale_log2;
+  lds_f32* s_l = (lds_f32*)(lds + kOffL);
+  lds_f32* s_m = (lds_f32*)(lds + kOffM);
+  lds_i32* s_flag = (lds_i32*)(lds + kOffFlag);
+
+  // O^T tiles [db][pb] for dims 128*wave + 32*db, pairs 32*pb.  Tiles 0..14 are
+  // MFMA accumulators (AGPRs); tile 15 is kept in plain VGPRs (o15) and gets
+  // each tile's contribution added with vector ALU ops, so that the MFMA
+  // accumulators (15 O tiles + the S tile) fit the 256 AGPRs.  The
+  // accumulators are only ever MFMA-updated, zeroed, or stored raw.
+  f32x16 o[15];
+  float o15[16];
+  bf16x8 q[kQSteps];
+
+  // ---- the pieces: one per sequence overlapping [T0, T1)
+  int b = b_first;
+  int64_t seq_start = b_first_start;
+  for (;;) {
+    const int32_t L = seq_len(b);
+    const int64_t seq_end = seq_start + tiles_of(L);
+    const int64_t p0 = seq_start > T0 ? seq_start : T0;
+    const int64_t p1 = seq_end < T1 ? seq_end : T1;
+    const bool whole = seq_start >= T0 && seq_end <= T1;
+    const int32_t* bt_row = block_table + (int64_t)b * a.max_blocks;
+
+    // queries of this sequence: B operand fragments, pair my_pair, dims 16k + 8*half .. +7
+    {
+      const int64_t row = ((int64_t)b * a.q_per_seq + my_j) * a.n_heads + my_s;
+      const bf16x8* src = (const bf16x8*)(a.q_abs + row * kDk) + half;
+#pragma unroll
+      for (int k = 0; k < kQSteps; ++k) q[k] = src[2 * k];
+    }
+    __builtin_amdgcn_s_waitcnt(0);           // queries resident before any tile load is queued
+    float m_ref = -INFINITY, l_part = 0.f;
+    // source of tile T of this sequence (rows beyond L or a padded block entry read block 0, masked)
+    auto tile_src = [&](int64_t T, int* valid) -> const uint8_t* {
+      const int tok0 = (int)(T - seq_start) * kTile;
+      *valid = min(kTile, L - tok0);
+      const int32_t blk = bt_row[tok0 / a.block_size];
+      if (blk < 0) {
+        *valid = 0;
+        return a.pool;
+      }
+      return a.pool + (int64_t)blk * a.block_bytes + (int64_t)(tok0 % a.block_size) * kRowBytes;
+    };
+
+    for (;;) {                               // attempts: a second one only after a reference jump
+#pragma unroll
+      for (int i = 0; i < 15; ++i) o[i] = f32x16{};
+#pragma unroll
+      for (int i = 0; i < 16; ++i) o15[i] = 0.f;
+      l_part = 0.f;
+      int64_t T_issue = p0;                  // loads in flight cover [T, T_issue)
+      for (int st = 0; st < kStages - 1 && T_issue < p1; ++st, ++T_issue) {
+        int valid;
+        const uint8_t* src = tile_src(T_issue, &valid);
+        issue_tile(src, valid, lds + (int)(T_issue % kStages) * kTileBytes, wave, lane);
+      }
+      bool redo = false;                     // a reference jumped during this attempt (wave-uniform)
+      for (int64_t T = p0; T < p1; ++T) {
+        wait_tiles(T_issue - 1 - T);         // tile T (and the queries) have landed
+        lds_barrier();                       // tile T visible to all; the stage of T-1 is free
+        if (T_issue < p1) {
+          int valid;
+          const uint8_t* src = tile_src(T_issue, &valid);
+          issue_tile(src, valid, lds + (int)(T_issue % kStages) * kTileBytes, wave, lane);
+          ++T_issue;
+        }
+        const uint32_t tb = (uint32_t)(uintptr_t)(lds + (int)(T % kStages) * kTileBytes);
+        const int tok0 = (int)(T - seq_start) * kTile;
+
+        // ---- S^T = K Q^T for this wave's 32 pairs: lane holds pair my_pair, tokens 8(i/4)+4*half+i%4.
+        // K-step k reads logical chunk 2k + half of row lane%32: chunk group k/4
+        // adds 1 KB, so four per-lane bases (by k%4) plus immediates suffice.
+        f32x16 sacc = {};
+        {
+          // four K fragments in flight ahead of the MFMA chain
+          bf16x8 kf[4];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) kf[k] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k]);
+#pragma unroll
+          for (int k = 0; k < kQSteps; ++k) {
+            const bf16x8 cur = kf[k % 4];
+            if (k + 4 < kQSteps)
+              kf[k % 4] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * ((k + 4) / 4));
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, q[k], sacc, 0, 0, 0);
+          }
+          // issue order: 4 reads, then (MFMA, read) pairs, then the last 4 MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+#pragma unroll
+          for (int k = 0; k < kQSteps - 4; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+        }
+
+        // ---- softmax against the reference max (exp2 domain)
+        const int vis = L - a.q_per_seq + my_j - tok0 + 1;    // tokens [0, vis) of this tile are visible
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = 8 * (i / 4) + 4 * half + (i % 4);
+          sacc[i] = t < vis ? sacc[i] * sl2 : -INFINITY;
+          tmax = fmaxf(tmax, sacc[i]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        // the reference is set by the first tile that shows this pair a key; a
+        // later jump by more than 2^16 raises it (weights stay <= 2^16) and
+        // marks the piece for a second pass
+        const bool had_ref = m_ref != -INFINITY;
+        const bool grow = tmax > m_ref + kRestartThreshold;
+        if (grow) m_ref = tmax;
+        redo |= __builtin_amdgcn_ballot_w64(grow && had_ref) != 0;
+        float psum = 0.f;
+        uint32_t pk[8];
+#pragma unroll
+        for (int i = 0; i < 16; i += 2) {
+          const float p0v = sacc[i] == -INFINITY ? 0.f : exp2f(sacc[i] - m_ref);
+          const float p1v = sacc[i + 1] == -INFINITY ? 0.f : exp2f(sacc[i + 1] - m_ref);
+          const uint16_t b0 = f32_to_bf16_bits(p0v), b1 = f32_to_bf16_bits(p1v);
+          psum += bf16_bits_to_f32(b0) + bf16_bits_to_f32(b1);   // normaliser uses the rounded weights
+          pk[i / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+        }
+        l_part += psum;
+        {
+          lds_u8* prow = lds + kOffP + my_pair * kPRow;
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            u32x2 v2 = {pk[2 * qq], pk[2 * qq + 1]};
+            *(lds_u32x2*)(prow + (8 * qq + 4 * half) * 2) = v2;
+          }
+        }
+        lds_barrier();
+
+        // ---- O^T += V^T P^T: this wave's 128 dims x all 128 pairs
+        f32x16 t15 = {};
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+          bf16x8 pf[4];
+#pragma unroll
+          for (int pb = 0; pb < 4; ++pb)
+            pf[pb] = *(const lds_bf16x8*)(uintptr_t)(p_base + 32 * pb * kPRow + 32 * ks);
+          // V^T fragments for the 4 dim blocks: two transpose reads each (4 tokens
+          // apiece).  They are issued together and waited for inside one asm block,
+          // so no load result is ever outstanding outside it.
+          bf16x4 h[8];
+          const uint32_t b0 = tb + v_base[0], b1 = tb + v_base[1], b2 = tb + v_base[2], b3 = tb + v_base[3];
+          asm volatile(
+              "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+              "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
+              "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
+              "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
+              "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
+              "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
+              "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
+              "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+              "s_waitcnt lgkmcnt(0)"
+              : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]), "=&v"(h[5]), "=&v"(h[6]),
+                "=&v"(h[7])
+              : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "i"(2 * 9 * 1024 * ks), "i"(2 * 9 * 1024 * ks + 1024)
+              : "memory");
+          // h[x*2 + hh] (+ 4 for dim blocks 2, 3): block db uses h[(db >> 1) * 4 + (db & 1) * 2 + hh]
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const bf16x4 lo = h[(db >> 1) * 4 + (db & 1) * 2], hi = h[(db >> 1) * 4 + (db & 1) * 2 + 1];
+            const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+#pragma unroll
+            for (int pb = 0; pb < 4; ++pb) {
+              if (db * 4 + pb == 15) t15 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], t15, 0, 0, 0);
+              else o[db * 4 + pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], o[db * 4 + pb], 0, 0, 0);
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) o15[i] += t15[i];
+      }
+      wait_vmcnt<0>();
+      if (lane == 0) s_flag[wave] = redo ? 1 : 0;
+      lds_barrier();
+      const bool any_redo = (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) != 0;
+      lds_barrier();                         // flags read; every wave is done with the last tile and P
+      if (!any_redo) break;
+      // Some pair's reference rose by more than 2^16 after it had accumulated
+      // weights: run the piece again.  Every reference now lies within 2^16 of
+      // its pair's maximum over the piece, so the second pass cannot jump.
+    }
+
+    // ---- finish the piece: raw accumulators to slot unit + b, (m, l) per row
+    const int64_t slot_row0 = (int64_t)(unit + b) * rows_per_seq;
+#pragma unroll
+    for (int pb = 0; pb < 4; ++pb) {
+      const int pair = 32 * pb + (lane & 31);
+      const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
+      float* dst_row = a.ws_o + (slot_row0 + row_in_seq) * kDc + 128 * wave + 4 * half;
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          float* dst = dst_row + 32 * db + 8 * qq;
+          if (db * 4 + pb == 15) *(f32x4*)dst = f32x4{o15[4 * qq], o15[4 * qq + 1], o15[4 * qq + 2], o15[4 * qq + 3]};
+          else *(f32x4*)dst = f32x4{o[db * 4 + pb][4 * qq], o[db * 4 + pb][4 * qq + 1], o[db * 4 + pb][4 * qq + 2],
+                                    o[db * 4 + pb][4 * qq + 3]};
+        }
+      }
+    }
+    const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
+    if (lane < 32) {
+      const int my_row = my_j * a.n_heads + my_s;
+      a.ws_stats[(slot_row0 + my_row) * 2] = m_ref;
+      a.ws_stats[(slot_row0 + my_row) * 2 + 1] = l_tot;
+      s_l[my_pair] = l_tot;
+      s_m[my_pair] = m_ref;
+    }
+    if (whole) {
+      // the whole sequence is in this unit: normalise from the slot, write bf16 o_lat and lse
+      __syncthreads();
+      const int pair = tid >> 1;               // thread t: pair t/2, dims 256*(t%2) .. +255
+      const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
+      const float l = s_l[pair], m = s_m[pair];
+      const float inv = l > 0.f ? 1.0f / l : 0.f;
+      const float* src = a.ws_o + (slot_row0 + row_in_seq) * kDc + 256 * (tid & 1);
+      uint16_t* dst = a.o_final + ((int64_t)b * rows_per_seq + row_in_seq) * kDc + 256 * (tid & 1);
+      for (int d = 0; d < 256; d += 4) {
+        const f32x4 v = *(const f32x4*)(src + d);
+        u32x2 pk2;
+        pk2[0] = (uint32_t)f32_to_bf16_bits(v[0] * inv) | ((uint32_t)f32_to_bf16_bits(v[1] * inv) << 16);
+        pk2[1] = (uint32_t)f32_to_bf16_bits(v[2] * inv) | ((uint32_t)f32_to_bf16_bits(v[3] * inv) << 16);
+        *(u32x2*)(dst + d) = pk2;
+      }
+      if ((tid & 1) == 0)
+        a.lse_final[(int64_t)b * rows_per_seq + row_in_seq] =
+            l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+    }
+    __syncthreads();                           // s_l / s_m and the LDS stages are free again
+    if (seq_end >= T1) break;
+    // next sequence holding tiles
+    seq_start = seq_end;
+    do {
+      ++b;
+    } while (tiles_of(seq_len(b)) == 0);
+  }
+}
+
+}  // namespace
+
+bool decode576_supported(const mla_dims& d, int32_t q_per_seq) {
+  if (d.d_c != 512 || d.d_rope != 64 || d.act_dtype != MLA_BF16 || d.cache_dtype != MLA_BF16) return false;
+  if (d.block_size % kTile != 0) return false;
+  if (q_per_seq <= 0 || kPairs % q_per_seq != 0) return false;
+  const int hpw = kPairs / q_per_seq;
+  return d.n_heads % hpw == 0;
+}
+
+int64_t decode576_default_units(int32_t n_seq, int32_t q_per_seq, int cu_count) {
+  (void)n_seq;
+  (void)q_per_seq;
+  return cu_count;   // one resident work-group per CU
+}
+
+mla_status launch_decode576(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
+                            const void* q_abs, const void* pool, const int32_t* block_table, int32_t max_blocks,
+                            const int32_t* seqlens, void* ws, void* o_lat, float* lse, hipStream_t st) {
+  Args a;
+  a.q_abs = static_cast<const uint16_t*>(q_abs);
+  a.pool = static_cast<const uint8_t*>(pool);
+  a.o_final = static_cast<uint16_t*>(o_lat);
+  a.lse_final = lse;
+  a.ws_o = static_cast<float*>(ws);
+  a.ws_stats = static_cast<float*>(ws) + plan.ws_stats_offset_floats;
+  a.block_bytes = static_cast<int64_t>(mla_cache_block_bytes(&d));
+  a.max_blocks = max_blocks;
+  a.block_size = d.block_size;
+  a.n_seq = n_seq;
+  a.q_per_seq = q_per_seq;
+  a.n_heads = d.n_heads;
+  a.units = plan.n_splits;
+  a.heads_per_wg = kPairs / q_per_seq;
+  a.scale_log2 = d.softmax_scale * 1.4426950408889634f;
+  dim3 grid(plan.n_splits, d.n_heads / a.heads_per_wg);
+  hipLaunchKernelGGL(decode576_kernel, grid, dim3(256), 0, st, a, block_table, seqlens);
+  return launch_status();
+}
+
+}  // namespace mla

@@ -102,7 +102,7 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
     const T* __restrict__ q_abs, const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
     int max_blocks, const int32_t* __restrict__ seqlens, int q_per_seq, int H, int d_c, int d_rope,
     int block_size, int64_t block_bytes, float scale, int n_splits, T* __restrict__ o_final,
-    float* __restrict__ lse_final, float* __restrict__ ws_o, float* __restrict__ ws_lse) {
+    float* __restrict__ lse_final, float* __restrict__ ws_o, float* __restrict__ ws_stats) {
   extern __shared__ float sh[];             // q [d_c + d_rope] | p [256] | acc [d_c]
   const int d_k = d_c + d_rope;
   float* sh_q = sh;
@@ -112,7 +112,7 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
   const int row = blockIdx.x;                // ((b * q_per_seq) + j) * H + s
   const int s = row % H, j = (row / H) % q_per_seq, b = row / (H * q_per_seq);
   const int split = blockIdx.y;
-  const int L = seqlens[b];
+  const int L = min(max(seqlens[b], 0), max_blocks * block_size);   // what the table can address
   const int p_q = L - q_per_seq + j;         // query position; sees tokens 0..p_q
   const int chunk = (L + n_splits - 1) / n_splits;
   const int t0 = split * chunk;
@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
   for (int tc = t0; tc < t1; tc += 256) {
     const int t = tc + threadIdx.x;
     float z = -INFINITY;
-    if (t < t1) {
+    if (t < t1 && bt[t / block_size] >= 0) {
       const uint8_t* blk = pool + static_cast<int64_t>(bt[t / block_size]) * block_bytes;
       const int slot = t % block_size;
       float dot = 0.f;
@@ -161,7 +161,7 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
     }
     __syncthreads();
     const float m = sh_m, alpha = sh_alpha;
-    const float pt = (t < t1) ? expf(z - m) : 0.f;
+    const float pt = (z == -INFINITY) ? 0.f : expf(z - m);
     sh_p[threadIdx.x] = pt;
     red[threadIdx.x] = pt;
     __syncthreads();
@@ -178,6 +178,7 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
         float a = acc[r] * alpha;
         for (int u = 0; u < nt; ++u) {
           const int tt = tc + u;
+          if (bt[tt / block_size] < 0) continue;    // padding entry: weight 0, never read
           const uint8_t* blk = pool + static_cast<int64_t>(bt[tt / block_size]) * block_bytes;
           const int slot = tt % block_size;
           float v;
@@ -209,47 +210,64 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
   }
   if (threadIdx.x == 0) {
     if (final_out) lse_final[row] = lse_v;
-    else ws_lse[(static_cast<int64_t>(b) * n_splits + split) * q_per_seq * H + j * H + s] = lse_v;
+    else ws_stats[((static_cast<int64_t>(b) * n_splits + split) * q_per_seq * H + j * H + s) * 2] = lse_v;
   }
 }
 
 // ----------------------------------------------------------------------------
 // combine: one block per (sequence, query row, head); partial slots of
-// sequence b are first..first+count-1 (see slot_range).
+// sequence b are first..first+count-1 (see slot_range).  Normalised partials
+// (kPerSequence) merge as lse = log sum e^(lse_k), o = sum e^(lse_k - lse) o_k;
+// raw partials (kStreamTiles, log2 units) as M = max m_k, L = sum 2^(m_k-M) l_k,
+// o = sum 2^(m_k - M) o_k / L, lse = (M + log2 L) ln 2.
 // ----------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) combine_kernel(
-    const float* __restrict__ ws_o, const float* __restrict__ ws_lse, const int32_t* __restrict__ seqlens,
+    const float* __restrict__ ws_o, const float* __restrict__ ws_stats, const int32_t* __restrict__ seqlens,
     int n_seq, int q_per_seq, int H, int d_c, SplitLayout lay, T* __restrict__ o_lat, float* __restrict__ lse) {
   __shared__ float w_sh[kMaxCombineSlots];
-  __shared__ float tot_sh, lse_sh;
+  __shared__ float scale_sh, lse_sh;
   const int row = blockIdx.x;
   const int s = row % H, j = (row / H) % q_per_seq, b = row / (H * q_per_seq);
   const SlotRange r = slot_range(lay, seqlens, n_seq, b);
   if (r.count == 0) return;                  // the decode kernel wrote this row itself
   const int first = r.first, count = min(r.count, kMaxCombineSlots);
   const int64_t per_slot = static_cast<int64_t>(q_per_seq) * H;
+  const int64_t rr = j * H + s;
   if (threadIdx.x == 0) {
     float m = -INFINITY;
-    for (int k = 0; k < count; ++k)
-      if (slot_used(lay, r, k)) m = fmaxf(m, ws_lse[(first + k) * per_slot + j * H + s]);
+    for (int k = 0; k < count; ++k) {
+      if (!slot_used(lay, r, k)) continue;
+      const float* st = ws_stats + ((first + k) * per_slot + rr) * 2;
+      if (lay.mode == 0 || st[1] > 0.f) m = fmaxf(m, st[0]);
+    }
     const float msafe = (m == -INFINITY) ? 0.f : m;
     float tot = 0.f;
     for (int k = 0; k < count; ++k) {
-      const float w = slot_used(lay, r, k) ? expf(ws_lse[(first + k) * per_slot + j * H + s] - msafe) : 0.f;
+      float w = 0.f;
+      if (slot_used(lay, r, k)) {
+        const float* st = ws_stats + ((first + k) * per_slot + rr) * 2;
+        if (lay.mode == 0) {
+          w = expf(st[0] - msafe);
+          tot += w;
+        } else if (st[1] > 0.f) {
+          w = exp2f(st[0] - msafe);
+          tot += w * st[1];
+        }
+      }
       w_sh[k] = w;
-      tot += w;
     }
-    tot_sh = tot;
-    lse_sh = (tot > 0.f) ? msafe + logf(tot) : -INFINITY;
+    scale_sh = tot > 0.f ? 1.0f / tot : 0.f;
+    if (lay.mode == 0) lse_sh = (tot > 0.f) ? msafe + logf(tot) : -INFINITY;
+    else lse_sh = (tot > 0.f) ? (msafe + log2f(tot)) * 0.69314718055994530942f : -INFINITY;
   }
   __syncthreads();
-  const float inv = tot_sh > 0.f ? 1.0f / tot_sh : 0.f;
+  const float inv = scale_sh;
   for (int c = threadIdx.x; c < d_c; c += blockDim.x) {
     float a = 0.f;
     for (int k = 0; k < count; ++k) {
       const float w = w_sh[k];
-      if (w != 0.f) a = fmaf(w, ws_o[((first + k) * per_slot + j * H + s) * d_c + c], a);
+      if (w != 0.f) a = fmaf(w, ws_o[((first + k) * per_slot + rr) * d_c + c], a);
     }
     Act<T>::st(o_lat, static_cast<int64_t>(row) * d_c + c, a * inv);
   }
@@ -327,35 +345,35 @@ mla_status launch_decode_generic(const mla_dims& d, const DecodePlan& plan, int3
   dim3 grid(n_seq * q_per_seq * d.n_heads, plan.n_splits);
   const size_t shm = sizeof(float) * (d.d_c + d.d_rope + 256);
   float* ws_o = static_cast<float*>(ws);
-  float* ws_lse = ws_o ? ws_o + plan.ws_lse_offset_floats : nullptr;
+  float* ws_stats = ws_o ? ws_o + plan.ws_stats_offset_floats : nullptr;
   if (d.cache_dtype == MLA_F32)
     hipLaunchKernelGGL((decode_generic_kernel<float, false>), grid, dim3(256), shm, st, (const float*)q_abs,
                        (const uint8_t*)pool, block_table, max_blocks, seqlens, q_per_seq, d.n_heads, d.d_c,
                        d.d_rope, d.block_size, bb, d.softmax_scale, plan.n_splits, (float*)o_lat, lse, ws_o,
-                       ws_lse);
+                       ws_stats);
   else if (d.cache_dtype == MLA_BF16)
     hipLaunchKernelGGL((decode_generic_kernel<uint16_t, false>), grid, dim3(256), shm, st,
                        (const uint16_t*)q_abs, (const uint8_t*)pool, block_table, max_blocks, seqlens, q_per_seq,
                        d.n_heads, d.d_c, d.d_rope, d.block_size, bb, d.softmax_scale, plan.n_splits,
-                       (uint16_t*)o_lat, lse, ws_o, ws_lse);
+                       (uint16_t*)o_lat, lse, ws_o, ws_stats);
   else
     hipLaunchKernelGGL((decode_generic_kernel<uint16_t, true>), grid, dim3(256), shm, st,
                        (const uint16_t*)q_abs, (const uint8_t*)pool, block_table, max_blocks, seqlens, q_per_seq,
                        d.n_heads, d.d_c, d.d_rope, d.block_size, bb, d.softmax_scale, plan.n_splits,
-                       (uint16_t*)o_lat, lse, ws_o, ws_lse);
+                       (uint16_t*)o_lat, lse, ws_o, ws_stats);
   return launch_status();
 }
 
 mla_status launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
                           const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st) {
   const float* ws_o = static_cast<const float*>(ws);
-  const float* ws_lse = ws_o + plan.ws_lse_offset_floats;
+  const float* ws_stats = ws_o + plan.ws_stats_offset_floats;
   dim3 grid(n_seq * q_per_seq * d.n_heads);
   if (d.act_dtype == MLA_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, ws_o, ws_lse, seqlens, n_seq, q_per_seq,
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, ws_o, ws_stats, seqlens, n_seq, q_per_seq,
                        d.n_heads, d.d_c, plan.layout, (float*)o_lat, lse);
   else
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, st, ws_o, ws_lse, seqlens, n_seq,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, st, ws_o, ws_stats, seqlens, n_seq,
                        q_per_seq, d.n_heads, d.d_c, plan.layout, (uint16_t*)o_lat, lse);
   return launch_status();
 }

@@ -12,6 +12,11 @@ namespace mla {
 
 constexpr int kMaxCombineSlots = 1024;   // partial results merged per (sequence, row, head)
 
+// Workspace: partial outputs o[slot][q_per_seq * H][d_c] (fp32), then per-row
+// statistics stats[slot][q_per_seq * H][2] (fp32).
+//   kPerSequence partials are normalised: o = sum p v / sum p, stats[0] = lse.
+//   kStreamTiles partials are raw: o = sum 2^(z - m) v, stats = (m, sum 2^(z - m)),
+//   with z the scaled score in log2 units.
 // Where the partial results of sequence b live in the workspace.
 //   kPerSequence: n_splits slots per sequence, slots b*n_splits .. +n_splits-1,
 //                 split k covers keys [k*ceil(L/n), (k+1)*ceil(L/n)).
@@ -26,6 +31,7 @@ struct SplitLayout {
   int32_t mode;      // 0 = kPerSequence, 1 = kStreamTiles
   int32_t n_splits;  // kPerSequence: splits per sequence; kStreamTiles: units G
   int32_t tile;      // kStreamTiles: tokens per tile
+  int32_t max_len;   // lengths are clamped to [0, max_len] (what the block table addresses)
 };
 
 struct DecodePlan {
@@ -33,7 +39,7 @@ struct DecodePlan {
   int32_t n_splits;              // generic: splits per sequence; tuned: work units
   int32_t n_slots;               // partial slots in the workspace (0 = none)
   int32_t needs_combine;         // partials are written (combine has work)
-  int64_t ws_lse_offset_floats;  // lse partials start here (floats from workspace start)
+  int64_t ws_stats_offset_floats;  // per-row statistics start here (floats from workspace start)
   size_t ws_bytes;               // workspace bytes needed
   SplitLayout layout;
 };
@@ -68,13 +74,21 @@ __device__ __forceinline__ SlotRange slot_range(const SplitLayout& lay, const in
     r.n_tiles = 0;
     return r;
   }
-  int64_t start = 0, total = 0;
+  int64_t start = 0, total = 0, nb = 0;
   for (int i = 0; i < n_seq; ++i) {
-    const int64_t nt = (static_cast<int64_t>(seqlens[i]) + lay.tile - 1) / lay.tile;
+    const int32_t L = min(max(seqlens[i], 0), lay.max_len);
+    const int64_t nt = (static_cast<int64_t>(L) + lay.tile - 1) / lay.tile;
     if (i < b) start += nt;
+    if (i == b) nb = nt;
     total += nt;
   }
-  const int64_t nb = (static_cast<int64_t>(seqlens[b]) + lay.tile - 1) / lay.tile;
+  if (nb == 0) {                 // nothing to merge for an empty sequence
+    r.first = 0;
+    r.count = 0;
+    r.unit0 = 0;
+    r.n_tiles = total;
+    return r;
+  }
   const int64_t wf = unit_of_tile(start, total, lay.n_splits);
   const int64_t wl = unit_of_tile(start + nb - 1, total, lay.n_splits);
   r.first = static_cast<int>(wf + b);
