@@ -22,7 +22,11 @@
  *    however you like); the library never frees them, never keeps them after
  *    the call returns, and never allocates device memory itself.
  *  - Tensors are dense, row-major, with the shapes given below.  Element types
- *    follow mla_dims.act_dtype ("act") and mla_dims.cache_dtype.
+ *    follow mla_dims.act_dtype ("act") and mla_dims.cache_dtype.  Every tensor
+ *    and workspace pointer should be 16-byte aligned (any device allocator's
+ *    default); mla_decode rejects unaligned q_abs / cache_pool / o_latent /
+ *    workspace with MLA_ERR_INVALID_ARG where its tuned kernel applies, the
+ *    other calls fall back to their generic kernels.
  *  - Each call validates its arguments on the host first.  On any invalid
  *    argument it returns an error status and launches nothing (outputs are left
  *    untouched).  Otherwise it enqueues its kernels asynchronously on `stream`

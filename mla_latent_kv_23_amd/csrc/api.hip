@@ -28,6 +28,8 @@ int device_cu_count() {
 
 namespace {
 
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 0; }
+
 bool dims_valid(const mla_dims* d) {
   if (!d) return false;
   if (d->n_heads <= 0 || d->d_c <= 0 || d->d_rope < 0 || (d->d_rope & 1) || d->d_nope <= 0 || d->d_v <= 0 ||
@@ -148,7 +150,8 @@ mla_status mla_absorb_q(const mla_dims* d, int32_t n_tok, const void* q_nope, co
   if (!q_nope || !w_uk || !q_abs || (d->d_rope > 0 && (!q_rope || !pos))) return MLA_ERR_INVALID_ARG;
   if (n_tok > 2147483647 / d->n_heads) return MLA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (absorb_tuned_applies(*d)) return launch_absorb_tuned(*d, n_tok, q_nope, q_rope, pos, w_uk, q_abs, st);
+  if (absorb_tuned_applies(*d) && aligned16(q_nope) && aligned16(w_uk) && aligned16(q_abs))
+    return launch_absorb_tuned(*d, n_tok, q_nope, q_rope, pos, w_uk, q_abs, st);
   return launch_absorb_generic(*d, n_tok, q_nope, q_rope, pos, w_uk, q_abs, st);
 }
 
@@ -188,9 +191,11 @@ mla_status mla_decode(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return MLA_ERR_WORKSPACE;
   if (plan.ws_bytes > 0 && (reinterpret_cast<uintptr_t>(workspace) & 15)) return MLA_ERR_INVALID_ARG;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (plan.kind == 1)
+  if (plan.kind == 1) {
+    if (!aligned16(q_abs) || !aligned16(cache_pool) || !aligned16(o_latent)) return MLA_ERR_INVALID_ARG;
     return launch_decode576(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, block_table, max_blocks, cache_seqlens,
                             workspace, o_latent, lse, st);
+  }
   return launch_decode_generic(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, block_table, max_blocks,
                                cache_seqlens, plan.ws_bytes ? workspace : nullptr, o_latent, lse, st);
 }
@@ -217,7 +222,8 @@ mla_status mla_up_proj(const mla_dims* d, int32_t n_tok, const void* o_latent, c
   if (!o_latent || !w_uv || !out) return MLA_ERR_INVALID_ARG;
   if (n_tok > 2147483647 / d->n_heads) return MLA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (up_proj_tuned_applies(*d)) return launch_up_proj_tuned(*d, n_tok, o_latent, w_uv, out, st);
+  if (up_proj_tuned_applies(*d) && aligned16(o_latent) && aligned16(w_uv) && aligned16(out))
+    return launch_up_proj_tuned(*d, n_tok, o_latent, w_uv, out, st);
   return launch_up_proj_generic(*d, n_tok, o_latent, w_uv, out, st);
 }
 

@@ -39,6 +39,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -315,15 +317,17 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         const bool grow = tmax > m_ref + kRestartThreshold;
         if (grow) m_ref = tmax;
         redo |= __builtin_amdgcn_ballot_w64(grow && had_ref) != 0;
+        // exp2 of masked scores is 0; an unset reference (no visible key yet) is taken as 0
+        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
         float psum = 0.f;
         uint32_t pk[8];
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const float p0v = sacc[i] == -INFINITY ? 0.f : exp2f(sacc[i] - m_ref);
-          const float p1v = sacc[i + 1] == -INFINITY ? 0.f : exp2f(sacc[i + 1] - m_ref);
-          const uint16_t b0 = f32_to_bf16_bits(p0v), b1 = f32_to_bf16_bits(p1v);
-          psum += bf16_bits_to_f32(b0) + bf16_bits_to_f32(b1);   // normaliser uses the rounded weights
-          pk[i / 2] = (uint32_t)b0 | ((uint32_t)b1 << 16);
+          const f32x2 pv = {__builtin_amdgcn_exp2f(sacc[i] - m_use), __builtin_amdgcn_exp2f(sacc[i + 1] - m_use)};
+          const bf16x2 pb2 = __builtin_convertvector(pv, bf16x2);              // round to nearest even
+          const uint32_t bits = *(const uint32_t*)&pb2;
+          psum += __uint_as_float(bits << 16) + __uint_as_float(bits & 0xffff0000u);  // the rounded weights
+          pk[i / 2] = bits;
         }
         l_part += psum;
         {

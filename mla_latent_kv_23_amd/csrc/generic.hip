@@ -366,6 +366,8 @@ mla_status launch_decode_generic(const mla_dims& d, const DecodePlan& plan, int3
 
 mla_status launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
                           const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st) {
+  if (plan.layout.mode == 1 && d.act_dtype == MLA_BF16 && d.d_c == 512)
+    return launch_combine_stream(d, plan, n_seq, q_per_seq, seqlens, ws, o_lat, lse, st);
   const float* ws_o = static_cast<const float*>(ws);
   const float* ws_stats = ws_o + plan.ws_stats_offset_floats;
   dim3 grid(n_seq * q_per_seq * d.n_heads);

@@ -114,6 +114,8 @@ mla_status launch_decode_generic(const mla_dims& d, const DecodePlan& plan, int3
                                  hipStream_t st);
 mla_status launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
                           const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st);
+mla_status launch_combine_stream(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
+                                 const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st);
 mla_status launch_up_proj_generic(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv,
                                   void* out, hipStream_t st);
 

@@ -1,0 +1,166 @@
+// Tuned gfx950 kernels for the two per-head projections around the latent
+// attention (bf16 in, fp32 accumulation on MFMA 32x32x16, bf16 out):
+//   absorb:  q_abs[t,s,:d_c] = W_UK[s]^T q_nope[t,s]  (+ RoPE of q_R into q_abs[t,s,d_c:])
+//   up-proj: out[t,s,:]      = W_UV[s] o_lat[t,s]
+// Both are computed transposed (output rows = feature, columns = tokens) so
+// that the 32 tokens of a block land in the 32 lanes and each lane writes 4
+// consecutive features.
+//  * up-proj: W_UV[s] is stored [d_v][d_c], i.e. contraction-contiguous, so
+//    both MFMA operands come straight from global memory (16 bytes per lane).
+//  * absorb: W_UK[s] is stored [d_nope][d_c] (feature-contiguous); a
+//    [d_nope x 128] slab is staged in LDS and read back with the LDS
+//    transpose read, which yields 4 consecutive contraction elements per lane.
+#include <math.h>
+
+#include "decode_latent576.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+
+constexpr int kAbsorbCols = 128;       // latent columns per absorb work-group
+constexpr int kMaxNope = 256;          // LDS slab: d_nope x 128 bf16 <= 64 KB
+
+__device__ __forceinline__ int swz8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+// 4 fp32 -> 4 bf16 (round to nearest even) packed in 8 bytes
+__device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
+  u32x2 r;
+  r[0] = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  r[1] = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
+  return r;
+}
+
+// grid (H, d_c / 128), block 256.  LDS slab row n (one contraction index) holds
+// latent columns cblk*128 .. +127 as 16 chunks of 16 bytes; chunk c of row n is
+// stored at chunk (c & ~7) | ((c ^ swz8(n)) & 7) so the transpose reads (4 rows
+// x 32 bytes per 16 lanes) are free of bank conflicts.
+__global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __restrict__ q_nope,
+                                                           const uint16_t* __restrict__ q_rope,
+                                                           const int32_t* __restrict__ pos,
+                                                           const uint16_t* __restrict__ w_uk,
+                                                           uint16_t* __restrict__ q_abs, int n_tok, int H, int d_c,
+                                                           int d_rope, int d_nope, RopeFreqs freqs) {
+  __shared__ __attribute__((aligned(16))) uint8_t slab_raw[kMaxNope * kAbsorbCols * 2];
+  lds_u8* slab = (lds_u8*)slab_raw;
+  const int s = blockIdx.x, cblk = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int d_k = d_c + d_rope;
+  // stage W_UK[s][:, cblk*128 .. +127]
+  const uint16_t* wsrc = w_uk + (int64_t)s * d_nope * d_c + cblk * kAbsorbCols;
+  for (int i = tid; i < d_nope * 16; i += 256) {
+    const int n = i >> 4, c = i & 15;
+    const u32x4 v = *(const u32x4*)(wsrc + (int64_t)n * d_c + c * 8);
+    const int pc = (c & ~7) | ((c ^ swz8(n)) & 7);
+    *(lds_u32x4*)(slab + n * 256 + pc * 16) = v;
+  }
+  __syncthreads();
+  // wave w: latent columns 32w .. 32w+31 of this block
+  const int gi = lane >> 4, sp = lane & 15, half = lane >> 5;
+  for (int t0 = 0; t0 < n_tok; t0 += 32) {
+    const int t = t0 + (lane & 31);
+    const int tc = t < n_tok ? t : n_tok - 1;
+    const bf16x8* qsrc = (const bf16x8*)(q_nope + ((int64_t)tc * H + s) * d_nope) + half;
+    f32x16 acc = {};
+    for (int ks = 0; ks < d_nope / 16; ++ks) {
+      bf16x4 h[2];
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int n = 16 * ks + 8 * (gi >> 1) + 4 * hh + (sp >> 2);
+        const int col = 32 * wave + 16 * (gi & 1) + 4 * (sp & 3);
+        const int c = col >> 3;
+        const int pc = (c & ~7) | ((c ^ swz8(n)) & 7);
+        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(slab + n * 256 + pc * 16 + (col & 7) * 2));
+      }
+      const bf16x8 a = bf16x8{h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
+      const bf16x8 bq = qsrc[2 * ks];
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc, 0, 0, 0);
+    }
+    if (t < n_tok) {
+      uint16_t* dst = q_abs + ((int64_t)t * H + s) * d_k + cblk * kAbsorbCols + 32 * wave + 4 * half;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(u32x2*)(dst + 8 * g) = pack4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+    }
+  }
+  // the rotated query part, once per head
+  if (cblk == 0) {
+    const int pairs = d_rope / 2;
+    for (int i = tid; i < n_tok * pairs; i += 256) {
+      const int t = i / pairs, p = i - t * pairs;
+      const int64_t row = (int64_t)t * H + s;
+      float cs, sn, ox, oy;
+      rope_cos_sin(pos[t], freqs.inv_freq[p], &cs, &sn);
+      rope_pair(bf16_bits_to_f32(q_rope[row * d_rope + 2 * p]), bf16_bits_to_f32(q_rope[row * d_rope + 2 * p + 1]),
+                cs, sn, &ox, &oy);
+      q_abs[row * d_k + d_c + 2 * p] = f32_to_bf16_bits(ox);
+      q_abs[row * d_k + d_c + 2 * p + 1] = f32_to_bf16_bits(oy);
+    }
+  }
+}
+
+// grid (H, ceil(n_tok / 32)), block 256: wave w computes output rows
+// 32*vb .. +31 (vb = w, w + 4, ...) for the block's 32 tokens.
+__global__ void __launch_bounds__(256) up_proj_tuned_kernel(const uint16_t* __restrict__ o_lat,
+                                                            const uint16_t* __restrict__ w_uv,
+                                                            uint16_t* __restrict__ out, int n_tok, int H, int d_c,
+                                                            int d_v) {
+  const int s = blockIdx.x;
+  const int t0 = blockIdx.y * 32;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
+  const int t = t0 + (lane & 31);
+  const int tc = t < n_tok ? t : n_tok - 1;
+  const bf16x8* bsrc = (const bf16x8*)(o_lat + ((int64_t)tc * H + s) * d_c) + half;
+  for (int vb = wave; vb < d_v / 32; vb += 4) {
+    const bf16x8* asrc = (const bf16x8*)(w_uv + ((int64_t)s * d_v + 32 * vb + (lane & 31)) * d_c) + half;
+    f32x16 acc = {};
+#pragma unroll 8
+    for (int ks = 0; ks < d_c / 16; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(asrc[2 * ks], bsrc[2 * ks], acc, 0, 0, 0);
+    if (t < n_tok) {
+      uint16_t* dst = out + ((int64_t)t * H + s) * d_v + 32 * vb + 4 * half;
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(u32x2*)(dst + 8 * g) = pack4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
+    }
+  }
+}
+
+}  // namespace
+
+bool absorb_tuned_applies(const mla_dims& d) {
+  return d.act_dtype == MLA_BF16 && d.d_c % kAbsorbCols == 0 && d.d_nope % 16 == 0 && d.d_nope <= kMaxNope &&
+         d.d_rope % 2 == 0;
+}
+
+mla_status launch_absorb_tuned(const mla_dims& d, int32_t n_tok, const void* q_nope, const void* q_rope,
+                               const int32_t* pos, const void* w_uk, void* q_abs, hipStream_t st) {
+  const RopeFreqs f = make_rope_freqs(d);
+  dim3 grid(d.n_heads, d.d_c / kAbsorbCols);
+  hipLaunchKernelGGL(absorb_tuned_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(q_nope),
+                     static_cast<const uint16_t*>(q_rope), pos, static_cast<const uint16_t*>(w_uk),
+                     static_cast<uint16_t*>(q_abs), n_tok, d.n_heads, d.d_c, d.d_rope, d.d_nope, f);
+  return launch_status();
+}
+
+bool up_proj_tuned_applies(const mla_dims& d) {
+  return d.act_dtype == MLA_BF16 && d.d_c % 16 == 0 && d.d_v % 32 == 0;
+}
+
+mla_status launch_up_proj_tuned(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv, void* out,
+                                hipStream_t st) {
+  dim3 grid(d.n_heads, (n_tok + 31) / 32);
+  hipLaunchKernelGGL(up_proj_tuned_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(o_lat),
+                     static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), n_tok, d.n_heads, d.d_c,
+                     d.d_v);
+  return launch_status();
+}
+
+}  // namespace mla
