@@ -134,3 +134,70 @@ def test_chain_vs_non_absorbed_oracle(name, cuda_device):
     U.assert_close(out.view(B, sq, w.n_heads, w.d_v), ref["o"], w.act_dtype, "o")
     U.assert_close(o_lat, ref["o_lat"], w.act_dtype, "o_lat")
     U.assert_close(lse, ref["lse"], w.act_dtype, "lse")
+
+
+@pytest.mark.parametrize("lens", [[31, 32, 33], [63, 64, 65], [1, 2, 127], [96, 4097]])
+def test_decode_tile_edges(lens, cuda_device):
+    """Lengths around the 32-token tile and 64-token block edges, single-token
+    sequences and padded block-table entries (the pool is NaN-poisoned)."""
+    import mla_latent_kv_23_amd as M
+    w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=len(lens))
+    inp = S.make_inputs(w, 4242, seqlens=torch.tensor(lens, dtype=torch.int32), spare_blocks=3)
+    U.say(f"[edges] {lens}")
+    d = U.dims_of(w)
+    pos = S.query_positions(inp["seqlens"], 1).numpy()
+    q_abs = O.absorb_q(inp["q_nope"].double().numpy(), inp["q_rope"].double().numpy(),
+                       pos[:, :, None] * np.ones((1, 1, w.n_heads), np.int64), inp["w_uk"].double().numpy(),
+                       w.rope_base)
+    q_dev = U.to_act(q_abs, "bf16", cuda_device)
+    q_r = q_dev.double().cpu().numpy()
+    pool = U.gpu_pool(w, inp, cuda_device, poison=0xFF)
+    bt, L = inp["block_table"].to(cuda_device), inp["seqlens"].to(cuda_device)
+    for ns in [0, 1, 5]:
+        o_lat, lse, ws = M.decode(d, q_dev, pool, bt, L, num_splits=ns)
+        M.combine(d, L, bt.shape[1], ws, o_lat, lse, num_splits=ns)
+        cu = inp["cu_seqlens"].numpy()
+        for b, Lb in enumerate(lens):
+            c, kr = O.cached_token_values(inp["c_kv"][cu[b]:cu[b] + Lb].double().numpy(),
+                                          inp["k_rope"][cu[b]:cu[b] + Lb].double().numpy(), np.arange(Lb), "bf16",
+                                          w.rope_base)
+            want_o, want_lse = O.decode_absorbed_form(q_r[b], c, kr, pos[b], w.softmax_scale)
+            U.assert_close(o_lat[b], want_o, "bf16", f"o_lat L={Lb} splits={ns}")
+            U.assert_close(lse[b], want_lse, "bf16", f"lse L={Lb} splits={ns}")
+
+
+def test_decode_large_logit_jump(cuda_device):
+    """Late keys with much larger scores than the first tile: the kernel's per-pair
+    reference max must move (second pass) and still match the oracle."""
+    import mla_latent_kv_23_amd as M
+    w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=2)
+    inp = S.make_inputs(w, 99, seqlens=torch.tensor([700, 300], dtype=torch.int32))
+    cu = inp["cu_seqlens"]
+    # tokens 600.. of sequence 0 get a 64x larger latent: scores jump by far more than 2^16 in exp2 units
+    c = inp["c_kv"].float()
+    c[cu[0] + 600:cu[0] + 700] *= 64.0
+    inp["c_kv"] = c.to(torch.bfloat16)
+    U.say("[jump]")
+    d = U.dims_of(w)
+    pos = S.query_positions(inp["seqlens"], 1).numpy()
+    q_abs = O.absorb_q(inp["q_nope"].double().numpy(), inp["q_rope"].double().numpy(),
+                       pos[:, :, None] * np.ones((1, 1, w.n_heads), np.int64), inp["w_uk"].double().numpy(),
+                       w.rope_base)
+    q_dev = U.to_act(q_abs, "bf16", cuda_device)
+    q_r = q_dev.double().cpu().numpy()
+    pool = U.gpu_pool(w, inp, cuda_device, poison=0xFF)
+    bt, L = inp["block_table"].to(cuda_device), inp["seqlens"].to(cuda_device)
+    for ns in [0, 1, 3]:
+        o_lat, lse, ws = M.decode(d, q_dev, pool, bt, L, num_splits=ns)
+        M.combine(d, L, bt.shape[1], ws, o_lat, lse, num_splits=ns)
+        for b in range(2):
+            Lb = int(inp["seqlens"][b])
+            cc, kr = O.cached_token_values(inp["c_kv"][cu[b]:cu[b] + Lb].double().numpy(),
+                                           inp["k_rope"][cu[b]:cu[b] + Lb].double().numpy(), np.arange(Lb),
+                                           "bf16", w.rope_base)
+            want_o, want_lse = O.decode_absorbed_form(q_r[b], cc, kr, pos[b], w.softmax_scale)
+            # relative bars: the outputs here are large (latents scaled by 64)
+            mx, rel = U.errors(o_lat[b], want_o, "bf16")
+            assert rel <= U.BF16_REL_L2, f"o_lat seq {b} splits={ns}: rel-L2 {rel:.3e}"
+            _, rel_l = U.errors(lse[b], want_lse, "f32")
+            assert rel_l <= 1e-4, f"lse seq {b} splits={ns}: rel-L2 {rel_l:.3e}"
