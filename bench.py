@@ -39,7 +39,22 @@ def parse():
                     help="sequences of the workload the CPU oracle is timed on (0 = skip)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode+combine calls (for profiling)")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="instead of the benchmark, run a plain device copy of this many MiB (5 launches): "
+                         "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+def calib_copy(mib):
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calib_copy_bytes_read": n, "calib_copy_bytes_written": n, "launches": 5}), flush=True)
 
 
 def main():
@@ -48,6 +63,9 @@ def main():
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
               "(every box here has a single MI355X)", file=sys.stderr)
         sys.exit(2)
+    if args.calib_copy_mib > 0:
+        calib_copy(args.calib_copy_mib)
+        return
     import torch
 
     import mla_latent_kv_23_amd as M

@@ -13,6 +13,7 @@ namespace {
 
 constexpr int kRowsPerBlock = 16;
 constexpr int kDc = 512;
+constexpr int kGroup = 4;   // pieces whose loads are in flight together
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -66,35 +67,43 @@ __global__ void __launch_bounds__(256) combine_stream_kernel(const float* __rest
   if (r >= rows_per_seq) return;
   const int d0 = (tid & 15) * 32;
 
-  // weights of the pieces for this row
-  float m = -INFINITY;
-  for (int64_t k = 0; k < count; ++k) {
-    const int64_t w = wf + k;
-    if (unit_first_tile(w, total, lay.n_splits) == unit_first_tile(w + 1, total, lay.n_splits)) continue;
-    const float* st = ws_stats + ((w + b) * rows_per_seq + r) * 2;
-    if (st[1] > 0.f) m = fmaxf(m, st[0]);
-  }
-  const float msafe = m == -INFINITY ? 0.f : m;
+  // Online merge over the pieces, four at a time: the stats and the 32 values
+  // of all four pieces are loaded before any is used (one memory latency per
+  // group), then folded in against a running maximum m:
+  //   acc <- acc 2^(m - m') + 2^(m_k - m') O_k,  tot likewise with l_k.
+  float m = -INFINITY, tot = 0.f;
   float acc[32];
 #pragma unroll
   for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-  float tot = 0.f;
-  for (int64_t k = 0; k < count; ++k) {
-    const int64_t w = wf + k;
-    if (unit_first_tile(w, total, lay.n_splits) == unit_first_tile(w + 1, total, lay.n_splits)) continue;
-    const float* st = ws_stats + ((w + b) * rows_per_seq + r) * 2;
-    const float l = st[1];
-    if (!(l > 0.f)) continue;
-    const float wgt = exp2f(st[0] - msafe);
-    tot += wgt * l;
-    const f32x4* src = (const f32x4*)(ws_o + ((w + b) * rows_per_seq + r) * kDc + d0);
+  for (int64_t k0 = 0; k0 < count; k0 += kGroup) {
+    float sm[kGroup], sl[kGroup];
+    f32x4 v[kGroup][8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const f32x4 v = src[i];
-      acc[4 * i] = fmaf(wgt, v[0], acc[4 * i]);
-      acc[4 * i + 1] = fmaf(wgt, v[1], acc[4 * i + 1]);
-      acc[4 * i + 2] = fmaf(wgt, v[2], acc[4 * i + 2]);
-      acc[4 * i + 3] = fmaf(wgt, v[3], acc[4 * i + 3]);
+    for (int j = 0; j < kGroup; ++j) {
+      const int64_t w = wf + min(k0 + j, count - 1);   // clamped: a repeated piece is masked below
+      const float* st = ws_stats + ((w + b) * rows_per_seq + r) * 2;
+      sm[j] = st[0];
+      sl[j] = st[1];
+      const f32x4* src = (const f32x4*)(ws_o + ((w + b) * rows_per_seq + r) * kDc + d0);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[j][i] = src[i];
+    }
+#pragma unroll
+    for (int j = 0; j < kGroup; ++j) {
+      const int64_t w = wf + k0 + j;
+      if (k0 + j >= count) break;
+      // a unit that owns no tile left nothing in its slot
+      if (unit_first_tile(w, total, lay.n_splits) == unit_first_tile(w + 1, total, lay.n_splits)) continue;
+      if (!(sl[j] > 0.f)) continue;
+      const float mn = fmaxf(m, sm[j]);
+      const float keep = exp2f(m - mn);          // 0 while nothing is accumulated (m = -inf)
+      const float wgt = exp2f(sm[j] - mn);
+      tot = fmaf(tot, keep, wgt * sl[j]);
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) acc[4 * i + e] = fmaf(acc[4 * i + e], keep, wgt * v[j][i][e]);
+      m = mn;
     }
   }
   const float inv = tot > 0.f ? 1.0f / tot : 0.f;
@@ -109,7 +118,7 @@ __global__ void __launch_bounds__(256) combine_stream_kernel(const float* __rest
     dst[i] = v;
   }
   if ((tid & 15) == 0)
-    lse[(int64_t)b * rows_per_seq + r] = tot > 0.f ? (msafe + log2f(tot)) * 0.69314718055994530942f : -INFINITY;
+    lse[(int64_t)b * rows_per_seq + r] = tot > 0.f ? (m + log2f(tot)) * 0.69314718055994530942f : -INFINITY;
 }
 
 }  // namespace

@@ -55,7 +55,6 @@ typedef __attribute__((address_space(3))) int32_t lds_i32;
 constexpr int kDc = 512, kDk = 576, kRowBytes = kDk * 2;   // bf16 cache row
 constexpr int kTile = kDecodeTile;                          // 32 tokens
 constexpr int kTileBytes = kTile * kRowBytes;               // 36864
-constexpr int kChunksPerRow = kRowBytes / 16;               // 72
 constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;        // 9 wave-wide 16-byte loads per wave per tile
 constexpr int kStages = 4;
 constexpr int kPairs = 128;
@@ -119,16 +118,54 @@ __device__ __forceinline__ void wait_tiles(int64_t n) {
 // loads rows 8w..8w+7: nine 1 KB blocks, one per instruction; lane l brings
 // row 8w + l/8, logical chunk 8i + ((l % 8) ^ swz(l / 8)).  Rows at or beyond
 // `valid` re-read row 0 (finite data; their probabilities are 0).
+// The direct-to-LDS loads are written in assembly: the compiler's wait-count
+// bookkeeping treats a pending LDS DMA as a possible writer of every LDS read,
+// which makes it wait for all LDS reads at once instead of only the oldest.
+// Their completion is tracked here by hand (wait_tiles + barrier); being
+// invisible to the compiler only makes its own memory-count waits stricter.
+// M0 (the LDS destination of each load) is declared clobbered and left as the
+// last load set it; no other code in this kernel uses M0.
+// (the compiler notes that M0 is reserved; it is deliberately written here)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void issue_tile(const uint8_t* src, int valid, lds_u8* dst, int wave, int lane) {
   const int rho = lane >> 3;
   const int row = 8 * wave + rho;
   const uint32_t lane_off = (row < valid ? row * kRowBytes : 0) + 16 * ((lane & 7) ^ swz(rho));
-#pragma unroll
-  for (int i = 0; i < kLoadsPerWave; ++i)
-    __builtin_amdgcn_global_load_lds(src + lane_off + 128 * i,
-                                     (__attribute__((address_space(3))) void*)(dst + (wave * kLoadsPerWave + i) * 1024),
-                                     16, 0, 0);
+  // LDS base and source are wave-uniform: pin them to scalar registers
+  // (readfirstlane yields a signed int: each half goes through uint32_t before widening)
+  const uint32_t m0 =
+      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst + (uint32_t)(wave * kLoadsPerWave * 1024));
+  const uint64_t sa = (uint64_t)(uintptr_t)src;
+  const uint32_t s_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sa >> 32));
+  const uint32_t s_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sa);
+  const uint64_t sv = ((uint64_t)s_hi << 32) | (uint64_t)s_lo;
+  uint32_t t;
+  static_assert(kLoadsPerWave == 9, "the load sequence below issues nine 1 KB blocks");
+  asm volatile(
+      "s_mov_b32 m0, %[m]\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[o], %[s]\n\t"
+      "v_add_u32 %[t], 0x80, %[o]\n\ts_add_u32 m0, %[m], 0x400\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x100, %[o]\n\ts_add_u32 m0, %[m], 0x800\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x180, %[o]\n\ts_add_u32 m0, %[m], 0xc00\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x200, %[o]\n\ts_add_u32 m0, %[m], 0x1000\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x280, %[o]\n\ts_add_u32 m0, %[m], 0x1400\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x300, %[o]\n\ts_add_u32 m0, %[m], 0x1800\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x380, %[o]\n\ts_add_u32 m0, %[m], 0x1c00\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x400, %[o]\n\ts_add_u32 m0, %[m], 0x2000\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]"
+      : [t] "=&v"(t)
+      : [o] "v"(lane_off), [s] "s"(sv), [m] "s"(m0)
+      : "memory", "m0", "scc");
 }
+#pragma clang diagnostic pop
 
 __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t* __restrict__ block_table,
                                                           const int32_t* __restrict__ seqlens) {
@@ -348,25 +385,14 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
 #pragma unroll
           for (int pb = 0; pb < 4; ++pb)
             pf[pb] = *(const lds_bf16x8*)(uintptr_t)(p_base + 32 * pb * kPRow + 32 * ks);
-          // V^T fragments for the 4 dim blocks: two transpose reads each (4 tokens
-          // apiece).  They are issued together and waited for inside one asm block,
-          // so no load result is ever outstanding outside it.
+          // V^T fragments for the 4 dim blocks: two transpose reads each (4 tokens apiece)
           bf16x4 h[8];
-          const uint32_t b0 = tb + v_base[0], b1 = tb + v_base[1], b2 = tb + v_base[2], b3 = tb + v_base[3];
-          asm volatile(
-              "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
-              "ds_read_b64_tr_b16 %1, %9 offset:%12\n\t"
-              "ds_read_b64_tr_b16 %2, %10 offset:%12\n\t"
-              "ds_read_b64_tr_b16 %3, %11 offset:%12\n\t"
-              "ds_read_b64_tr_b16 %4, %8 offset:%13\n\t"
-              "ds_read_b64_tr_b16 %5, %9 offset:%13\n\t"
-              "ds_read_b64_tr_b16 %6, %10 offset:%13\n\t"
-              "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
-              "s_waitcnt lgkmcnt(0)"
-              : "=&v"(h[0]), "=&v"(h[1]), "=&v"(h[2]), "=&v"(h[3]), "=&v"(h[4]), "=&v"(h[5]), "=&v"(h[6]),
-                "=&v"(h[7])
-              : "v"(b0), "v"(b1), "v"(b2), "v"(b3), "i"(2 * 9 * 1024 * ks), "i"(2 * 9 * 1024 * ks + 1024)
-              : "memory");
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int x = 0; x < 4; ++x)
+              h[hh * 4 + x] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                  (lds_bf16x4*)(uintptr_t)(tb + v_base[x] + 2 * 9 * 1024 * ks + 1024 * hh));
           // h[x*2 + hh] (+ 4 for dim blocks 2, 3): block db uses h[(db >> 1) * 4 + (db & 1) * 2 + hh]
 #pragma unroll
           for (int db = 0; db < 4; ++db) {

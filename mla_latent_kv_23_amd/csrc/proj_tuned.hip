@@ -4,12 +4,17 @@
 //   up-proj: out[t,s,:]      = W_UV[s] o_lat[t,s]
 // Both are computed transposed (output rows = feature, columns = tokens) so
 // that the 32 tokens of a block land in the 32 lanes and each lane writes 4
-// consecutive features.
-//  * up-proj: W_UV[s] is stored [d_v][d_c], i.e. contraction-contiguous, so
-//    both MFMA operands come straight from global memory (16 bytes per lane).
+// consecutive features.  Both are weight-streaming (a decode step has few
+// tokens), so the contraction sizes are compile-time constants: every loop
+// unrolls and each wave issues all of its global loads before the first MFMA
+// waits on one, instead of paying one memory latency per k-step.
 //  * absorb: W_UK[s] is stored [d_nope][d_c] (feature-contiguous); a
 //    [d_nope x 128] slab is staged in LDS and read back with the LDS
 //    transpose read, which yields 4 consecutive contraction elements per lane.
+//  * up-proj: W_UV[s] is stored [d_v][d_c], i.e. contraction-contiguous, so
+//    both MFMA operands come straight from global memory (16 bytes per lane).
+//    The contraction is split over the 4 waves (128 latent dims each) and the
+//    four fp32 partial tiles are summed through LDS.
 #include <math.h>
 
 #include "decode_latent576.h"
@@ -25,9 +30,12 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) float lds_f32;
 
 constexpr int kAbsorbCols = 128;       // latent columns per absorb work-group
-constexpr int kMaxNope = 256;          // LDS slab: d_nope x 128 bf16 <= 64 KB
+constexpr int kNope = 128;             // d_nope of the tuned absorb
+constexpr int kUpDc = 512;             // d_c of the tuned up-projection
+constexpr int kUpDv = 128;             // d_v of the tuned up-projection
 
 __device__ __forceinline__ int swz8(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
 
@@ -42,54 +50,83 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
 // grid (H, d_c / 128), block 256.  LDS slab row n (one contraction index) holds
 // latent columns cblk*128 .. +127 as 16 chunks of 16 bytes; chunk c of row n is
 // stored at chunk (c & ~7) | ((c ^ swz8(n)) & 7) so the transpose reads (4 rows
-// x 32 bytes per 16 lanes) are free of bank conflicts.
+// x 32 bytes per 16 lanes) are free of bank conflicts.  Wave w computes latent
+// columns 32w .. 32w+31 of the block for every 32-token block in turn; the
+// next block's query fragments are loaded while the current one is multiplied.
 __global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __restrict__ q_nope,
                                                            const uint16_t* __restrict__ q_rope,
                                                            const int32_t* __restrict__ pos,
                                                            const uint16_t* __restrict__ w_uk,
                                                            uint16_t* __restrict__ q_abs, int n_tok, int H, int d_c,
-                                                           int d_rope, int d_nope, RopeFreqs freqs) {
-  __shared__ __attribute__((aligned(16))) uint8_t slab_raw[kMaxNope * kAbsorbCols * 2];
+                                                           int d_rope, RopeFreqs freqs) {
+  constexpr int kSteps = kNope / 16;                 // 8 k-steps of 16
+  constexpr int kChunks = kNope * 16 / 256;          // slab chunks per thread
+  __shared__ __attribute__((aligned(16))) uint8_t slab_raw[kNope * kAbsorbCols * 2];
   lds_u8* slab = (lds_u8*)slab_raw;
   const int s = blockIdx.x, cblk = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d_k = d_c + d_rope;
-  // stage W_UK[s][:, cblk*128 .. +127]
-  const uint16_t* wsrc = w_uk + (int64_t)s * d_nope * d_c + cblk * kAbsorbCols;
-  for (int i = tid; i < d_nope * 16; i += 256) {
-    const int n = i >> 4, c = i & 15;
-    const u32x4 v = *(const u32x4*)(wsrc + (int64_t)n * d_c + c * 8);
+  const int gi = lane >> 4, sp = lane & 15, half = lane >> 5;
+
+  // slab loads (W_UK[s][:, cblk*128 .. +127]) and the first block's queries, all in flight together
+  const uint16_t* wsrc = w_uk + (int64_t)s * kNope * d_c + cblk * kAbsorbCols;
+  u32x4 wv[kChunks];
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int idx = tid + 256 * i, n = idx >> 4, c = idx & 15;
+    wv[i] = *(const u32x4*)(wsrc + (int64_t)n * d_c + c * 8);
+  }
+  auto load_q = [&](int t0, bf16x8 (&qf)[kSteps]) {
+    const int t = min(t0 + (lane & 31), n_tok - 1);
+    const bf16x8* qsrc = (const bf16x8*)(q_nope + ((int64_t)t * H + s) * kNope) + half;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) qf[ks] = qsrc[2 * ks];
+  };
+  bf16x8 qf[kSteps];
+  load_q(0, qf);
+  // the first block's queries are consumed here, together with the slab, so
+  // that both sets of loads share one memory latency
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks) asm volatile("" ::"v"(qf[ks]));
+#pragma unroll
+  for (int i = 0; i < kChunks; ++i) {
+    const int idx = tid + 256 * i, n = idx >> 4, c = idx & 15;
     const int pc = (c & ~7) | ((c ^ swz8(n)) & 7);
-    *(lds_u32x4*)(slab + n * 256 + pc * 16) = v;
+    *(lds_u32x4*)(slab + n * 256 + pc * 16) = wv[i];
   }
   __syncthreads();
-  // wave w: latent columns 32w .. 32w+31 of this block
-  const int gi = lane >> 4, sp = lane & 15, half = lane >> 5;
-  for (int t0 = 0; t0 < n_tok; t0 += 32) {
-    const int t = t0 + (lane & 31);
-    const int tc = t < n_tok ? t : n_tok - 1;
-    const bf16x8* qsrc = (const bf16x8*)(q_nope + ((int64_t)tc * H + s) * d_nope) + half;
-    f32x16 acc = {};
-    for (int ks = 0; ks < d_nope / 16; ++ks) {
-      bf16x4 h[2];
+
+  // per-lane transpose-read offsets for k-step 0 (k-step ks adds 16 rows = 4 KB)
+  uint32_t tr_off[2];
 #pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int n = 16 * ks + 8 * (gi >> 1) + 4 * hh + (sp >> 2);
-        const int col = 32 * wave + 16 * (gi & 1) + 4 * (sp & 3);
-        const int c = col >> 3;
-        const int pc = (c & ~7) | ((c ^ swz8(n)) & 7);
-        h[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(slab + n * 256 + pc * 16 + (col & 7) * 2));
-      }
-      const bf16x8 a = bf16x8{h[0][0], h[0][1], h[0][2], h[0][3], h[1][0], h[1][1], h[1][2], h[1][3]};
-      const bf16x8 bq = qsrc[2 * ks];
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bq, acc, 0, 0, 0);
+  for (int hh = 0; hh < 2; ++hh) {
+    const int n = 8 * (gi >> 1) + 4 * hh + (sp >> 2);
+    const int col = 32 * wave + 16 * (gi & 1) + 4 * (sp & 3);
+    const int c = col >> 3;
+    const int pc = (c & ~7) | ((c ^ swz8(n)) & 7);
+    tr_off[hh] = (uint32_t)(uintptr_t)slab + n * 256 + pc * 16 + (col & 7) * 2;
+  }
+  for (int t0 = 0; t0 < n_tok; t0 += 32) {
+    bf16x8 qn[kSteps];
+    if (t0 + 32 < n_tok) load_q(t0 + 32, qn);
+    __builtin_amdgcn_sched_barrier(0);
+    f32x16 acc = {};
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) {
+      const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(tr_off[0] + ks * 16 * 256));
+      const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(tr_off[1] + ks * 16 * 256));
+      const bf16x8 a = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], acc, 0, 0, 0);
     }
+    const int t = t0 + (lane & 31);
     if (t < n_tok) {
       uint16_t* dst = q_abs + ((int64_t)t * H + s) * d_k + cblk * kAbsorbCols + 32 * wave + 4 * half;
 #pragma unroll
       for (int g = 0; g < 4; ++g)
         *(u32x2*)(dst + 8 * g) = pack4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
     }
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) qf[ks] = qn[ks];
   }
   // the rotated query part, once per head
   if (cblk == 0) {
@@ -107,37 +144,69 @@ __global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __res
   }
 }
 
-// grid (H, ceil(n_tok / 32)), block 256: wave w computes output rows
-// 32*vb .. +31 (vb = w, w + 4, ...) for the block's 32 tokens.
+// grid (H, ceil(n_tok / 32)), block 256.  Wave w contracts latent dims
+// 128w .. 128w+127 for all d_v/32 output-row blocks of the block's 32 tokens
+// (all its operands are loaded up front), writes its fp32 partial tiles to
+// LDS, and after the barrier finishes output-row block w by summing the four
+// partials in a fixed order.
 __global__ void __launch_bounds__(256) up_proj_tuned_kernel(const uint16_t* __restrict__ o_lat,
                                                             const uint16_t* __restrict__ w_uv,
-                                                            uint16_t* __restrict__ out, int n_tok, int H, int d_c,
-                                                            int d_v) {
+                                                            uint16_t* __restrict__ out, int n_tok, int H) {
+  constexpr int kVb = kUpDv / 32;                    // 4 output-row blocks
+  constexpr int kSlice = kUpDc / 4;                  // latent dims per wave
+  constexpr int kSteps = kSlice / 16;                // 8 k-steps
+  static_assert(kVb == 4, "one output-row block per wave in the reduction");
+  __shared__ __attribute__((aligned(16))) float red_raw[4 * kVb * 16 * 64];   // [wave][vb][reg][lane]
+  lds_f32* red = (lds_f32*)red_raw;
   const int s = blockIdx.x;
   const int t0 = blockIdx.y * 32;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, half = lane >> 5;
   const int t = t0 + (lane & 31);
-  const int tc = t < n_tok ? t : n_tok - 1;
-  const bf16x8* bsrc = (const bf16x8*)(o_lat + ((int64_t)tc * H + s) * d_c) + half;
-  for (int vb = wave; vb < d_v / 32; vb += 4) {
-    const bf16x8* asrc = (const bf16x8*)(w_uv + ((int64_t)s * d_v + 32 * vb + (lane & 31)) * d_c) + half;
-    f32x16 acc = {};
-#pragma unroll 8
-    for (int ks = 0; ks < d_c / 16; ++ks) acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(asrc[2 * ks], bsrc[2 * ks], acc, 0, 0, 0);
-    if (t < n_tok) {
-      uint16_t* dst = out + ((int64_t)t * H + s) * d_v + 32 * vb + 4 * half;
+  const int tc = min(t, n_tok - 1);
+  const bf16x8* bsrc = (const bf16x8*)(o_lat + ((int64_t)tc * H + s) * kUpDc + kSlice * wave) + half;
+  bf16x8 bf[kSteps];
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(u32x2*)(dst + 8 * g) = pack4(acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]);
-    }
+  for (int ks = 0; ks < kSteps; ++ks) bf[ks] = bsrc[2 * ks];
+  bf16x8 af[kVb][kSteps];
+#pragma unroll
+  for (int vb = 0; vb < kVb; ++vb) {
+    const bf16x8* asrc = (const bf16x8*)(w_uv + ((int64_t)s * kUpDv + 32 * vb + (lane & 31)) * kUpDc + kSlice * wave) + half;
+#pragma unroll
+    for (int ks = 0; ks < kSteps; ++ks) af[vb][ks] = asrc[2 * ks];
+  }
+  __builtin_amdgcn_sched_barrier(0);   // every load is issued before the first MFMA waits
+  f32x16 acc[kVb];
+#pragma unroll
+  for (int vb = 0; vb < kVb; ++vb) acc[vb] = f32x16{};
+#pragma unroll
+  for (int ks = 0; ks < kSteps; ++ks)
+#pragma unroll
+    for (int vb = 0; vb < kVb; ++vb) acc[vb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[vb][ks], bf[ks], acc[vb], 0, 0, 0);
+#pragma unroll
+  for (int vb = 0; vb < kVb; ++vb)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) red[((wave * kVb + vb) * 16 + i) * 64 + lane] = acc[vb][i];
+  __syncthreads();
+  // output-row block vb = wave: rows 32*vb + 8(i/4) + 4*half + i%4, token t
+  float v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    float x = red[((0 * kVb + wave) * 16 + i) * 64 + lane];
+#pragma unroll
+    for (int w2 = 1; w2 < 4; ++w2) x += red[((w2 * kVb + wave) * 16 + i) * 64 + lane];
+    v[i] = x;
+  }
+  if (t < n_tok) {
+    uint16_t* dst = out + ((int64_t)t * H + s) * kUpDv + 32 * wave + 4 * half;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) *(u32x2*)(dst + 8 * g) = pack4(v[4 * g], v[4 * g + 1], v[4 * g + 2], v[4 * g + 3]);
   }
 }
 
 }  // namespace
 
 bool absorb_tuned_applies(const mla_dims& d) {
-  return d.act_dtype == MLA_BF16 && d.d_c % kAbsorbCols == 0 && d.d_nope % 16 == 0 && d.d_nope <= kMaxNope &&
-         d.d_rope % 2 == 0;
+  return d.act_dtype == MLA_BF16 && d.d_c % kAbsorbCols == 0 && d.d_nope == kNope && d.d_rope % 2 == 0;
 }
 
 mla_status launch_absorb_tuned(const mla_dims& d, int32_t n_tok, const void* q_nope, const void* q_rope,
@@ -146,20 +215,19 @@ mla_status launch_absorb_tuned(const mla_dims& d, int32_t n_tok, const void* q_n
   dim3 grid(d.n_heads, d.d_c / kAbsorbCols);
   hipLaunchKernelGGL(absorb_tuned_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(q_nope),
                      static_cast<const uint16_t*>(q_rope), pos, static_cast<const uint16_t*>(w_uk),
-                     static_cast<uint16_t*>(q_abs), n_tok, d.n_heads, d.d_c, d.d_rope, d.d_nope, f);
+                     static_cast<uint16_t*>(q_abs), n_tok, d.n_heads, d.d_c, d.d_rope, f);
   return launch_status();
 }
 
 bool up_proj_tuned_applies(const mla_dims& d) {
-  return d.act_dtype == MLA_BF16 && d.d_c % 16 == 0 && d.d_v % 32 == 0;
+  return d.act_dtype == MLA_BF16 && d.d_c == kUpDc && d.d_v == kUpDv;
 }
 
 mla_status launch_up_proj_tuned(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv, void* out,
                                 hipStream_t st) {
   dim3 grid(d.n_heads, (n_tok + 31) / 32);
   hipLaunchKernelGGL(up_proj_tuned_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(o_lat),
-                     static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), n_tok, d.n_heads, d.d_c,
-                     d.d_v);
+                     static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), n_tok, d.n_heads);
   return launch_status();
 }
 
