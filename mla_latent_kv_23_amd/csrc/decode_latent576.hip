@@ -50,6 +50,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 
 constexpr int kDc = 512, kDk = 576, kRowBytes = kDk * 2;   // bf16 cache row
@@ -60,6 +61,8 @@ constexpr int kStages = 4;
 constexpr int kPairs = 128;
 constexpr int kPRow = 80;                                   // bytes per P row: 32 bf16 + 16 pad
 constexpr int kQSteps = kDk / 16;                           // 36 k-steps of the QK contraction
+constexpr int kKAhead = 8;                                  // K fragment reads in flight per wave
+static_assert(kKAhead % 4 == 0, "K prefetch depth is a multiple of the 4 per-lane read bases");
 
 constexpr int kOffP = kStages * kTileBytes;                 // 147456
 constexpr int kOffL = kOffP + kPairs * kPRow;               // 157696
@@ -68,6 +71,11 @@ constexpr int kOffFlag = kOffM + kPairs * 4;                // 158720
 constexpr int kOffScan = kOffFlag + 16;                     // 158736
 constexpr int kOffMisc = kOffScan + 4 * 4;                  // 158752
 constexpr int kLdsBytes = kOffMisc + 64;                    // 158816 <= 163840
+
+// epilogue staging: 64 rows of 512 fp32, padded by 16 bytes so that 8 lanes
+// writing 8 consecutive rows at one column hit 8 different 16-byte slots
+constexpr int kXRow = kDc * 4 + 16;
+static_assert(64 * kXRow <= kOffP, "epilogue staging fits in the tile stages");
 
 constexpr float kRestartThreshold = 16.0f;                  // log2 units: weights stay <= 2^16
 
@@ -105,6 +113,15 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 __device__ __forceinline__ int tiles_of(int32_t L) { return (L + kTile - 1) / kTile; }
+
+constexpr int kXcds = 8;                                    // MI355X: 8 XCDs of 32 CUs
+// Bijection of [0, G): work-group i runs on XCD i % 8 as its (i / 8)-th
+// group there; XCD x takes the contiguous unit range starting at
+// x * (G / 8) + min(x, G % 8).
+__device__ __forceinline__ int xcd_unit(int i, int G) {
+  const int x = i % kXcds, j = i / kXcds, q = G / kXcds, r = G % kXcds;
+  return x * q + min(x, r) + j;
+}
 
 // wait until at most n tiles' worth of this wave's loads are still in flight
 __device__ __forceinline__ void wait_tiles(int64_t n) {
@@ -174,8 +191,11 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int unit = blockIdx.x, hg = blockIdx.y;
   const int G = a.units;
+  // Work-groups are handed to the 8 XCDs round-robin by their linear index;
+  // consecutive units (the pieces of one sequence, which read the same
+  // queries) are given to work-groups of one XCD so they share its L2.
+  const int unit = xcd_unit(blockIdx.x, G), hg = blockIdx.y;
   const int32_t max_len = a.max_blocks * a.block_size;
   // sequence length as used here: clamped to what the block table can address
   auto seq_len = [&](int b) -> int32_t { return min(max(seqlens[b], 0), max_len); };
@@ -316,37 +336,54 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         // adds 1 KB, so four per-lane bases (by k%4) plus immediates suffice.
         f32x16 sacc = {};
         {
-          // four K fragments in flight ahead of the MFMA chain
-          bf16x8 kf[4];
+          // kKAhead K fragments in flight ahead of the MFMA chain (the LDS is
+          // shared by the four waves, whose reads queue behind each other)
+          bf16x8 kf[kKAhead];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) kf[k] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k]);
+          for (int k = 0; k < kKAhead; ++k) kf[k] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (k / 4));
 #pragma unroll
           for (int k = 0; k < kQSteps; ++k) {
-            const bf16x8 cur = kf[k % 4];
-            if (k + 4 < kQSteps)
-              kf[k % 4] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * ((k + 4) / 4));
+            const bf16x8 cur = kf[k % kKAhead];
+            if (k + kKAhead < kQSteps)
+              kf[k % kKAhead] =
+                  *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * ((k + kKAhead) / 4));
             sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, q[k], sacc, 0, 0, 0);
           }
-          // issue order: 4 reads, then (MFMA, read) pairs, then the last 4 MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);
+          // issue order: kKAhead reads, then (MFMA, read) pairs, then the last kKAhead MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
 #pragma unroll
-          for (int k = 0; k < kQSteps - 4; ++k) {
+          for (int k = 0; k < kQSteps - kKAhead; ++k) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
+          __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
         }
 
-        // ---- softmax against the reference max (exp2 domain)
-        const int vis = L - a.q_per_seq + my_j - tok0 + 1;    // tokens [0, vis) of this tile are visible
-        float tmax = -INFINITY;
+        // ---- softmax against the reference max (exp2 domain).  The scale is
+        // positive (checked by the API), so the max of the raw scores gives the
+        // max of the scaled ones and the scale folds into one FMA per weight.
+        float sv[16];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int t = 8 * (i / 4) + 4 * half + (i % 4);
-          sacc[i] = t < vis ? sacc[i] * sl2 : -INFINITY;
-          tmax = fmaxf(tmax, sacc[i]);
+        for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+        // causal / length mask: only a tile reaching past the first query row's
+        // last visible token needs it (wave-uniform test)
+        if (tok0 + kTile > L - a.q_per_seq + 1) {
+          const int vis = L - a.q_per_seq + my_j - tok0 + 1;  // tokens [0, vis) of this tile are visible
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int t = 8 * (i / 4) + 4 * half + (i % 4);
+            sv[i] = t < vis ? sv[i] : -INFINITY;
+          }
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        float smax = sv[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sv[i]);
+        {
+          // the pair's other 16 tokens live in lane l ^ 32
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+          smax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+        }
+        const float tmax = smax * sl2;
         // the reference is set by the first tile that shows this pair a key; a
         // later jump by more than 2^16 raises it (weights stay <= 2^16) and
         // marks the piece for a second pass
@@ -355,16 +392,17 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         if (grow) m_ref = tmax;
         redo |= __builtin_amdgcn_ballot_w64(grow && had_ref) != 0;
         // exp2 of masked scores is 0; an unset reference (no visible key yet) is taken as 0
-        const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+        const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
         float psum = 0.f;
         uint32_t pk[8];
+        const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 #pragma unroll
         for (int i = 0; i < 16; i += 2) {
-          const f32x2 pv = {__builtin_amdgcn_exp2f(sacc[i] - m_use), __builtin_amdgcn_exp2f(sacc[i + 1] - m_use)};
+          const f32x2 pv = {__builtin_amdgcn_exp2f(fmaf(sv[i], sl2, neg_m)),
+                            __builtin_amdgcn_exp2f(fmaf(sv[i + 1], sl2, neg_m))};
           const bf16x2 pb2 = __builtin_convertvector(pv, bf16x2);              // round to nearest even
-          const uint32_t bits = *(const uint32_t*)&pb2;
-          psum += __uint_as_float(bits << 16) + __uint_as_float(bits & 0xffff0000u);  // the rounded weights
-          pk[i / 2] = bits;
+          psum = __builtin_amdgcn_fdot2_f32_bf16(pb2, ones, psum, false);     // sum of the rounded weights
+          pk[i / 2] = *(const uint32_t*)&pb2;
         }
         l_part += psum;
         {
@@ -419,51 +457,72 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       // its pair's maximum over the piece, so the second pass cannot jump.
     }
 
-    // ---- finish the piece: raw accumulators to slot unit + b, (m, l) per row
+    // ---- finish the piece.  The accumulators go out through LDS (free now:
+    // every load has landed and every wave is past the last tile), 64 pairs at
+    // a time, so that each store instruction writes 1 KB of one output row
+    // instead of 32-byte pieces of 32 rows.  A piece that is a whole sequence
+    // is normalised on the way (bf16 o_lat and lse); any other piece leaves its
+    // raw partial (relative to 2^m) and (m, l) in slot unit + b.
     const int64_t slot_row0 = (int64_t)(unit + b) * rows_per_seq;
-#pragma unroll
-    for (int pb = 0; pb < 4; ++pb) {
-      const int pair = 32 * pb + (lane & 31);
-      const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
-      float* dst_row = a.ws_o + (slot_row0 + row_in_seq) * kDc + 128 * wave + 4 * half;
-#pragma unroll
-      for (int db = 0; db < 4; ++db) {
-#pragma unroll
-        for (int qq = 0; qq < 4; ++qq) {
-          float* dst = dst_row + 32 * db + 8 * qq;
-          if (db * 4 + pb == 15) *(f32x4*)dst = f32x4{o15[4 * qq], o15[4 * qq + 1], o15[4 * qq + 2], o15[4 * qq + 3]};
-          else *(f32x4*)dst = f32x4{o[db * 4 + pb][4 * qq], o[db * 4 + pb][4 * qq + 1], o[db * 4 + pb][4 * qq + 2],
-                                    o[db * 4 + pb][4 * qq + 3]};
-        }
-      }
+    float l_tot;
+    {
+      // the pair's other 16 tokens were summed in lane l ^ 32
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+      l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
-    const float l_tot = l_part + __shfl_xor(l_part, 32, 64);
     if (lane < 32) {
-      const int my_row = my_j * a.n_heads + my_s;
-      a.ws_stats[(slot_row0 + my_row) * 2] = m_ref;
-      a.ws_stats[(slot_row0 + my_row) * 2 + 1] = l_tot;
+      if (!whole) {
+        const int my_row = my_j * a.n_heads + my_s;
+        a.ws_stats[(slot_row0 + my_row) * 2] = m_ref;
+        a.ws_stats[(slot_row0 + my_row) * 2 + 1] = l_tot;
+      }
       s_l[my_pair] = l_tot;
       s_m[my_pair] = m_ref;
     }
-    if (whole) {
-      // the whole sequence is in this unit: normalise from the slot, write bf16 o_lat and lse
-      __syncthreads();
-      const int pair = tid >> 1;               // thread t: pair t/2, dims 256*(t%2) .. +255
+#pragma unroll
+    for (int hp = 0; hp < 2; ++hp) {               // pairs 64*hp .. 64*hp+63
+#pragma unroll
+      for (int pbl = 0; pbl < 2; ++pbl) {
+        const int pb = 2 * hp + pbl;
+        lds_u8* xrow = lds + (32 * pbl + (lane & 31)) * kXRow + (128 * wave + 4 * half) * 4;
+#pragma unroll
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            f32x4 v;
+            if (db * 4 + pb == 15) v = f32x4{o15[4 * qq], o15[4 * qq + 1], o15[4 * qq + 2], o15[4 * qq + 3]};
+            else v = f32x4{o[db * 4 + pb][4 * qq], o[db * 4 + pb][4 * qq + 1], o[db * 4 + pb][4 * qq + 2],
+                           o[db * 4 + pb][4 * qq + 3]};
+            *(lds_f32x4*)(xrow + (32 * db + 8 * qq) * 4) = v;
+          }
+      }
+      lds_barrier();                              // the 64 rows (and s_l, s_m) are in LDS
+      // thread t: 16-byte chunk t % 128 of rows t / 128 + 2k
+      const int c = tid & 127;
+#pragma unroll 4
+      for (int k = 0; k < 32; ++k) {
+        const int r = (tid >> 7) + 2 * k;
+        const int pair = 64 * hp + r;
+        const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
+        const f32x4 v = *(const lds_f32x4*)(lds + r * kXRow + c * 16);
+        if (!whole) {
+          *(f32x4*)(a.ws_o + (slot_row0 + row_in_seq) * kDc + 4 * c) = v;
+        } else {
+          const float l = s_l[pair];
+          const float inv = l > 0.f ? 1.0f / l : 0.f;
+          u32x2 pk2;
+          pk2[0] = (uint32_t)f32_to_bf16_bits(v[0] * inv) | ((uint32_t)f32_to_bf16_bits(v[1] * inv) << 16);
+          pk2[1] = (uint32_t)f32_to_bf16_bits(v[2] * inv) | ((uint32_t)f32_to_bf16_bits(v[3] * inv) << 16);
+          *(u32x2*)(a.o_final + ((int64_t)b * rows_per_seq + row_in_seq) * kDc + 4 * c) = pk2;
+        }
+      }
+      lds_barrier();                              // the staging rows are free again
+    }
+    if (whole && tid < kPairs) {
+      const int pair = tid;
       const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
       const float l = s_l[pair], m = s_m[pair];
-      const float inv = l > 0.f ? 1.0f / l : 0.f;
-      const float* src = a.ws_o + (slot_row0 + row_in_seq) * kDc + 256 * (tid & 1);
-      uint16_t* dst = a.o_final + ((int64_t)b * rows_per_seq + row_in_seq) * kDc + 256 * (tid & 1);
-      for (int d = 0; d < 256; d += 4) {
-        const f32x4 v = *(const f32x4*)(src + d);
-        u32x2 pk2;
-        pk2[0] = (uint32_t)f32_to_bf16_bits(v[0] * inv) | ((uint32_t)f32_to_bf16_bits(v[1] * inv) << 16);
-        pk2[1] = (uint32_t)f32_to_bf16_bits(v[2] * inv) | ((uint32_t)f32_to_bf16_bits(v[3] * inv) << 16);
-        *(u32x2*)(dst + d) = pk2;
-      }
-      if ((tid & 1) == 0)
-        a.lse_final[(int64_t)b * rows_per_seq + row_in_seq] =
-            l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
+      a.lse_final[(int64_t)b * rows_per_seq + row_in_seq] = l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
     }
     __syncthreads();                           // s_l / s_m and the LDS stages are free again
     if (seq_end >= T1) break;
