@@ -27,6 +27,41 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0            # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
 
+# HBM traffic of the decode kernel measured with rocprofv3 counters (FETCH_SIZE,
+# WRITE_SIZE, each scaled by its reading for a plain copy of known size); the
+# summary records a hash of the kernel sources it was measured on, and the
+# figure is reported only while the sources still match.
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode576_v3_bs64_ctx8k_traffic.md")
+KERNEL_SOURCES = ["decode_latent576.hip", "decode_latent576.h", "mla_internal.h", "mla_device.h"]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "mla_latent_kv_23_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """Bytes per decode launch from the committed counter summary, or None when
+    the summary is missing or was taken on other kernel sources."""
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_PROFILE) as f:
+        for line in f:
+            if ":" in line and line.strip().startswith(("traffic_bytes_per_launch", "kernel_sources_sha256")):
+                k, v = line.strip().split(":", 1)
+                vals[k.strip()] = v.strip().strip("`")
+    if vals.get("kernel_sources_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(vals["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
 
 def parse():
     ap = argparse.ArgumentParser()
@@ -35,7 +70,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="v3_bs64_ctx8k")
     ap.add_argument("--num-splits", type=int, default=0)
-    ap.add_argument("--cpu-sample-seqs", type=int, default=2,
+    ap.add_argument("--cpu-sample-seqs", type=int, default=16,
                     help="sequences of the workload the CPU oracle is timed on (0 = skip)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode+combine calls (for profiling)")
@@ -180,7 +215,7 @@ def main():
         "decode_hbm_gbps": round(dec_gbps, 1),
         "decode_tflops": round(dec_tflops, 1),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
                      "kernel": "decode576_kernel", "bytes_per_launch": cache_bytes,
                      "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": cpu,

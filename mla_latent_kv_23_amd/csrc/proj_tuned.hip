@@ -128,11 +128,14 @@ __global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __res
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) qf[ks] = qn[ks];
   }
-  // the rotated query part, once per head
-  if (cblk == 0) {
+  // the rotated query part of head s: the d_c / 128 work-groups of the head
+  // share it, work-group cblk taking tokens t = cblk (mod gridDim.y)
+  {
     const int pairs = d_rope / 2;
-    for (int i = tid; i < n_tok * pairs; i += 256) {
-      const int t = i / pairs, p = i - t * pairs;
+    const int ny = gridDim.y;
+    const int n_mine = (n_tok - cblk + ny - 1) / ny;
+    for (int i = tid; i < n_mine * pairs; i += 256) {
+      const int t = cblk + ny * (i / pairs), p = i % pairs;
       const int64_t row = (int64_t)t * H + s;
       float cs, sn, ox, oy;
       rope_cos_sin(pos[t], freqs.inv_freq[p], &cs, &sn);
