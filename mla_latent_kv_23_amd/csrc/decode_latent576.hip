@@ -30,47 +30,30 @@
 //  * O^T += V^T P^T on bf16 MFMA 32x32x16: wave w owns latent dims
 //    128w..128w+127 for all 128 pairs (fp32 accumulators, 256 per lane); V^T
 //    comes straight from the row-major tile with the LDS transpose read.
-#include <math.h>
-
-#include "decode_latent576.h"
+#include "decode_tile.h"
 
 namespace mla {
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) uint8_t lds_u8;
-typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
-typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
-typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
-typedef __attribute__((address_space(3))) float lds_f32;
-typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
-typedef __attribute__((address_space(3))) int32_t lds_i32;
-
-constexpr int kDc = 512, kDk = 576, kRowBytes = kDk * 2;   // bf16 cache row
-constexpr int kTile = kDecodeTile;                          // 32 tokens
-constexpr int kTileBytes = kTile * kRowBytes;               // 36864
-constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;        // 9 wave-wide 16-byte loads per wave per tile
 constexpr int kStages = 4;
 constexpr int kPairs = 128;
-constexpr int kPRow = 80;                                   // bytes per P row: 32 bf16 + 16 pad
+constexpr int kPRow = 64;                                   // bytes per P row: 32 bf16, 16-byte chunks XOR-swizzled
+constexpr int kPBufBytes = kPairs * kPRow;                  // 8192
 constexpr int kQSteps = kDk / 16;                           // 36 k-steps of the QK contraction
 constexpr int kKAhead = 8;                                  // K fragment reads in flight per wave
 static_assert(kKAhead % 4 == 0, "K prefetch depth is a multiple of the 4 per-lane read bases");
 
-constexpr int kOffP = kStages * kTileBytes;                 // 147456
-constexpr int kOffL = kOffP + kPairs * kPRow;               // 157696
-constexpr int kOffM = kOffL + kPairs * 4;                   // 158208
-constexpr int kOffFlag = kOffM + kPairs * 4;                // 158720
-constexpr int kOffScan = kOffFlag + 16;                     // 158736
-constexpr int kOffMisc = kOffScan + 4 * 4;                  // 158752
-constexpr int kLdsBytes = kOffMisc + 64;                    // 158816 <= 163840
+constexpr int kOffP = kStages * kTileBytes;                 // 147456: two P buffers (tile T in buffer T % 2)
+constexpr int kLdsBytes = kOffP + 2 * kPBufBytes;           // 163840
+// Small scratch shares P buffer 0; it is used only while no weights are live
+// there: the sequence scan before the first tile, the redo flags after the
+// last PV of an attempt, the (l, m) rows in the piece epilogue.
+constexpr int kOffL = kOffP;                                // 128 floats
+constexpr int kOffM = kOffL + kPairs * 4;                   // 128 floats
+constexpr int kOffFlag = kOffM + kPairs * 4;                // 4 ints
+constexpr int kOffScan = kOffFlag + 16;                     // 4 ints
+constexpr int kOffMisc = kOffScan + 16;                     // 2 ints
+static_assert(kOffMisc + 8 <= kOffP + kPBufBytes, "scratch inside P buffer 0");
 
 // epilogue staging: 64 rows of 512 fp32, padded by 16 bytes so that 8 lanes
 // writing 8 consecutive rows at one column hit 8 different 16-byte slots
@@ -94,35 +77,6 @@ struct Args {
   float scale_log2;             // softmax_scale * log2(e)
 };
 
-// LDS tile layout: row r, 16-byte chunk c lives in 1 KB block
-// (r / 8) * 9 + c / 8 at byte (r % 8) * 128 + 16 * ((c % 8) ^ swz(r % 8)).
-// swz is a permutation of 0..7 (16-byte reads of 8 rows at one chunk hit 8
-// different bank groups) and, within each aligned group of 4 rows, swz >> 1 is
-// a permutation of 0..3 (transpose reads of 4 rows x 32 bytes do not collide).
-__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
-__device__ __forceinline__ uint32_t tile_off(int r, int c) {
-  return ((r >> 3) * 9 + (c >> 3)) * 1024 + (r & 7) * 128 + 16 * ((c & 7) ^ swz(r & 7));
-}
-
-__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
-
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
-__device__ __forceinline__ int tiles_of(int32_t L) { return (L + kTile - 1) / kTile; }
-
-constexpr int kXcds = 8;                                    // MI355X: 8 XCDs of 32 CUs
-// Bijection of [0, G): work-group i runs on XCD i % 8 as its (i / 8)-th
-// group there; XCD x takes the contiguous unit range starting at
-// x * (G / 8) + min(x, G % 8).
-__device__ __forceinline__ int xcd_unit(int i, int G) {
-  const int x = i % kXcds, j = i / kXcds, q = G / kXcds, r = G % kXcds;
-  return x * q + min(x, r) + j;
-}
-
 // wait until at most n tiles' worth of this wave's loads are still in flight
 __device__ __forceinline__ void wait_tiles(int64_t n) {
   if (n >= 3) wait_vmcnt<3 * kLoadsPerWave>();
@@ -131,58 +85,6 @@ __device__ __forceinline__ void wait_tiles(int64_t n) {
   else wait_vmcnt<0>();
 }
 
-// Copy one tile (32 rows starting at `src`) into LDS stage `dst`.  Wave w
-// loads rows 8w..8w+7: nine 1 KB blocks, one per instruction; lane l brings
-// row 8w + l/8, logical chunk 8i + ((l % 8) ^ swz(l / 8)).  Rows at or beyond
-// `valid` re-read row 0 (finite data; their probabilities are 0).
-// The direct-to-LDS loads are written in assembly: the compiler's wait-count
-// bookkeeping treats a pending LDS DMA as a possible writer of every LDS read,
-// which makes it wait for all LDS reads at once instead of only the oldest.
-// Their completion is tracked here by hand (wait_tiles + barrier); being
-// invisible to the compiler only makes its own memory-count waits stricter.
-// M0 (the LDS destination of each load) is declared clobbered and left as the
-// last load set it; no other code in this kernel uses M0.
-// (the compiler notes that M0 is reserved; it is deliberately written here)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void issue_tile(const uint8_t* src, int valid, lds_u8* dst, int wave, int lane) {
-  const int rho = lane >> 3;
-  const int row = 8 * wave + rho;
-  const uint32_t lane_off = (row < valid ? row * kRowBytes : 0) + 16 * ((lane & 7) ^ swz(rho));
-  // LDS base and source are wave-uniform: pin them to scalar registers
-  // (readfirstlane yields a signed int: each half goes through uint32_t before widening)
-  const uint32_t m0 =
-      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst + (uint32_t)(wave * kLoadsPerWave * 1024));
-  const uint64_t sa = (uint64_t)(uintptr_t)src;
-  const uint32_t s_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sa >> 32));
-  const uint32_t s_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sa);
-  const uint64_t sv = ((uint64_t)s_hi << 32) | (uint64_t)s_lo;
-  uint32_t t;
-  static_assert(kLoadsPerWave == 9, "the load sequence below issues nine 1 KB blocks");
-  asm volatile(
-      "s_mov_b32 m0, %[m]\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[o], %[s]\n\t"
-      "v_add_u32 %[t], 0x80, %[o]\n\ts_add_u32 m0, %[m], 0x400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x100, %[o]\n\ts_add_u32 m0, %[m], 0x800\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x180, %[o]\n\ts_add_u32 m0, %[m], 0xc00\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x200, %[o]\n\ts_add_u32 m0, %[m], 0x1000\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x280, %[o]\n\ts_add_u32 m0, %[m], 0x1400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x300, %[o]\n\ts_add_u32 m0, %[m], 0x1800\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x380, %[o]\n\ts_add_u32 m0, %[m], 0x1c00\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x400, %[o]\n\ts_add_u32 m0, %[m], 0x2000\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]"
-      : [t] "=&v"(t)
-      : [o] "v"(lane_off), [s] "s"(sv), [m] "s"(m0)
-      : "memory", "m0", "scc");
-}
-#pragma clang diagnostic pop
 
 __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t* __restrict__ block_table,
                                                           const int32_t* __restrict__ seqlens) {
@@ -258,7 +160,19 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         v_base[x * 2 + hh] = tile_off(row, (dim + 32 * x) >> 3) + ((dim & 7) << 1);
       }
   }
-  const uint32_t p_base = (uint32_t)(uintptr_t)(lds + kOffP) + (lane & 31) * kPRow + 16 * half;
+  // P buffer rows: pair r holds its 32 weights (bf16) as 4 chunks of 16 bytes,
+  // logical chunk c stored at c ^ ((r >> 2) & 3), so 16 consecutive rows at one
+  // chunk cover 16 distinct 16-byte slots.
+  const int psw = ((lane & 31) >> 2) & 3;
+  // writer: row my_pair, tokens 8qq + 4*half .. +3 of the tile (8 bytes at chunk qq)
+  const uint32_t p_wr = (uint32_t)(uintptr_t)(lds + kOffP) + my_pair * kPRow + 8 * half;
+  // reader (PV B operand): row 32pb + lane%32, tokens 16ks + 8*half .. +7, i.e.
+  // chunk (2ks + half) ^ psw = 2 (ks ^ (psw >> 1)) + (half ^ (psw & 1)); the
+  // per-ks offset 32 (ks ^ (psw >> 1)) is the ks = 0 base plus 32 ks, negated
+  // when psw >> 1 is set
+  const uint32_t p_rd = (uint32_t)(uintptr_t)(lds + kOffP) + (lane & 31) * kPRow + 16 * (half ^ (psw & 1)) +
+                        32 * (psw >> 1);
+  const int p_ks_sign = (psw >> 1) ? -1 : 1;
 
   const float sl2 = a.scale_log2;
   lds_f32* s_l = (lds_f32*)(lds + kOffL);
@@ -319,15 +233,13 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         issue_tile(src, valid, lds + (int)(T_issue % kStages) * kTileBytes, wave, lane);
       }
       bool redo = false;                     // a reference jumped during this attempt (wave-uniform)
+      wait_tiles(T_issue - 1 - p0);          // tile p0 has landed
+      lds_barrier();
+      // One barrier per tile, after the weights are written: it publishes P(T)
+      // (buffer T % 2) and tile T+1 (each wave waits for its own loads of it
+      // first), and every wave has finished PV(T-1) by then, so the next tile
+      // load goes into the stage of T-1.
       for (int64_t T = p0; T < p1; ++T) {
-        wait_tiles(T_issue - 1 - T);         // tile T (and the queries) have landed
-        lds_barrier();                       // tile T visible to all; the stage of T-1 is free
-        if (T_issue < p1) {
-          int valid;
-          const uint8_t* src = tile_src(T_issue, &valid);
-          issue_tile(src, valid, lds + (int)(T_issue % kStages) * kTileBytes, wave, lane);
-          ++T_issue;
-        }
         const uint32_t tb = (uint32_t)(uintptr_t)(lds + (int)(T % kStages) * kTileBytes);
         const int tok0 = (int)(T - seq_start) * kTile;
 
@@ -406,23 +318,30 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         }
         l_part += psum;
         {
-          lds_u8* prow = lds + kOffP + my_pair * kPRow;
+          const uint32_t pw = p_wr + (uint32_t)(T & 1) * kPBufBytes;
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
-            u32x2 v2 = {pk[2 * qq], pk[2 * qq + 1]};
-            *(lds_u32x2*)(prow + (8 * qq + 4 * half) * 2) = v2;
+            const u32x2 v2 = {pk[2 * qq], pk[2 * qq + 1]};
+            *(lds_u32x2*)(uintptr_t)(pw + 16 * (qq ^ psw)) = v2;
           }
         }
+        if (T + 1 < p1) wait_tiles(T_issue - 2 - T);   // tile T+1 has landed (later ones may be in flight)
         lds_barrier();
+        if (T_issue < p1) {
+          int valid;
+          const uint8_t* src = tile_src(T_issue, &valid);
+          issue_tile(src, valid, lds + (int)(T_issue % kStages) * kTileBytes, wave, lane);
+          ++T_issue;
+        }
 
         // ---- O^T += V^T P^T: this wave's 128 dims x all 128 pairs
         f32x16 t15 = {};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bf16x8 pf[4];
+          const uint32_t pbuf = p_rd + (uint32_t)(T & 1) * kPBufBytes + (uint32_t)(32 * ks * p_ks_sign);
 #pragma unroll
-          for (int pb = 0; pb < 4; ++pb)
-            pf[pb] = *(const lds_bf16x8*)(uintptr_t)(p_base + 32 * pb * kPRow + 32 * ks);
+          for (int pb = 0; pb < 4; ++pb) pf[pb] = *(const lds_bf16x8*)(uintptr_t)(pbuf + 32 * pb * kPRow);
           // V^T fragments for the 4 dim blocks: two transpose reads each (4 tokens apiece)
           bf16x4 h[8];
 #pragma unroll
@@ -447,10 +366,11 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         for (int i = 0; i < 16; ++i) o15[i] += t15[i];
       }
       wait_vmcnt<0>();
+      lds_barrier();                         // every wave is done with the last tile and P (the flags share P buffer 0)
       if (lane == 0) s_flag[wave] = redo ? 1 : 0;
       lds_barrier();
       const bool any_redo = (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) != 0;
-      lds_barrier();                         // flags read; every wave is done with the last tile and P
+      lds_barrier();                         // flags read
       if (!any_redo) break;
       // Some pair's reference rose by more than 2^16 after it had accumulated
       // weights: run the piece again.  Every reference now lies within 2^16 of

@@ -1,0 +1,119 @@
+// Device helpers shared by the tuned latent-576 decode kernels: operand
+// types, the bf16 cache tile (32 rows x 1152 B) and its swizzled LDS layout,
+// barrier / wait helpers, the XCD-aware unit order, and the direct-to-LDS tile
+// loader.
+#pragma once
+
+#include <math.h>
+
+#include "decode_latent576.h"
+
+namespace mla {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) float lds_f32;
+typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef __attribute__((address_space(3))) int32_t lds_i32;
+
+constexpr int kDc = 512, kDk = 576, kRowBytes = kDk * 2;   // bf16 cache row
+constexpr int kTile = kDecodeTile;                          // 32 tokens
+constexpr int kTileBytes = kTile * kRowBytes;               // 36864
+constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;        // 9 wave-wide 16-byte loads per wave per tile
+
+// LDS tile layout: row r, 16-byte chunk c lives in 1 KB block
+// (r / 8) * 9 + c / 8 at byte (r % 8) * 128 + 16 * ((c % 8) ^ swz(r % 8)).
+// swz is a permutation of 0..7 (16-byte reads of 8 rows at one chunk hit 8
+// different bank groups) and, within each aligned group of 4 rows, swz >> 1 is
+// a permutation of 0..3 (transpose reads of 4 rows x 32 bytes do not collide).
+__device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ uint32_t tile_off(int r, int c) {
+  return ((r >> 3) * 9 + (c >> 3)) * 1024 + (r & 7) * 128 + 16 * ((c & 7) ^ swz(r & 7));
+}
+
+__device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+__device__ __forceinline__ int tiles_of(int32_t L) { return (L + kTile - 1) / kTile; }
+
+constexpr int kXcds = 8;                                    // MI355X: 8 XCDs of 32 CUs
+// Bijection of [0, G): work-group i runs on XCD i % 8 as its (i / 8)-th
+// group there; XCD x takes the contiguous unit range starting at
+// x * (G / 8) + min(x, G % 8).
+__device__ __forceinline__ int xcd_unit(int i, int G) {
+  const int x = i % kXcds, j = i / kXcds, q = G / kXcds, r = G % kXcds;
+  return x * q + min(x, r) + j;
+}
+
+// Copy one tile (32 rows starting at `src`) into LDS stage `dst`.  Wave w
+// loads rows 8w..8w+7: nine 1 KB blocks, one per instruction; lane l brings
+// row 8w + l/8, logical chunk 8i + ((l % 8) ^ swz(l / 8)).  Rows at or beyond
+// `valid` re-read row 0 (finite data; their probabilities are 0).
+// The direct-to-LDS loads are written in assembly: the compiler's wait-count
+// bookkeeping treats a pending LDS DMA as a possible writer of every LDS read,
+// which makes it wait for all LDS reads at once instead of only the oldest.
+// Their completion is tracked here by hand (wait_tiles + barrier); being
+// invisible to the compiler only makes its own memory-count waits stricter.
+// M0 (the LDS destination of each load) is declared clobbered and left as the
+// last load set it; no other code in this kernel uses M0.
+// (the compiler notes that M0 is reserved; it is deliberately written here)
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void issue_tile(const uint8_t* src, int valid, lds_u8* dst, int wave, int lane) {
+  const int rho = lane >> 3;
+  const int row = 8 * wave + rho;
+  const uint32_t lane_off = (row < valid ? row * kRowBytes : 0) + 16 * ((lane & 7) ^ swz(rho));
+  // LDS base and source are wave-uniform: pin them to scalar registers
+  // (readfirstlane yields a signed int: each half goes through uint32_t before widening)
+  const uint32_t m0 =
+      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst + (uint32_t)(wave * kLoadsPerWave * 1024));
+  const uint64_t sa = (uint64_t)(uintptr_t)src;
+  const uint32_t s_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sa >> 32));
+  const uint32_t s_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sa);
+  const uint64_t sv = ((uint64_t)s_hi << 32) | (uint64_t)s_lo;
+  uint32_t t;
+  static_assert(kLoadsPerWave == 9, "the load sequence below issues nine 1 KB blocks");
+  asm volatile(
+      "s_mov_b32 m0, %[m]\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[o], %[s]\n\t"
+      "v_add_u32 %[t], 0x80, %[o]\n\ts_add_u32 m0, %[m], 0x400\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x100, %[o]\n\ts_add_u32 m0, %[m], 0x800\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x180, %[o]\n\ts_add_u32 m0, %[m], 0xc00\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x200, %[o]\n\ts_add_u32 m0, %[m], 0x1000\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x280, %[o]\n\ts_add_u32 m0, %[m], 0x1400\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x300, %[o]\n\ts_add_u32 m0, %[m], 0x1800\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x380, %[o]\n\ts_add_u32 m0, %[m], 0x1c00\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]\n\t"
+      "v_add_u32 %[t], 0x400, %[o]\n\ts_add_u32 m0, %[m], 0x2000\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[s]"
+      : [t] "=&v"(t)
+      : [o] "v"(lane_off), [s] "s"(sv), [m] "s"(m0)
+      : "memory", "m0", "scc");
+}
+
+#pragma clang diagnostic pop
+
+}  // namespace
+}  // namespace mla
