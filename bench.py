@@ -32,7 +32,7 @@ BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
 # summary records a hash of the kernel sources it was measured on, and the
 # figure is reported only while the sources still match.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode576_v3_bs64_ctx8k_traffic.md")
-KERNEL_SOURCES = ["decode_latent576.hip", "decode_latent576.h", "mla_internal.h", "mla_device.h"]
+KERNEL_SOURCES = ["decode_latent576.hip", "decode_tile.h", "decode_latent576.h", "mla_internal.h", "mla_device.h"]
 
 
 def kernel_source_hash():
