@@ -68,6 +68,29 @@ __global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __res
   const int d_k = d_c + d_rope;
   const int gi = lane >> 4, sp = lane & 15, half = lane >> 5;
 
+  // The rotated query part of head s is shared by its d_c / 128 work-groups
+  // (work-group cblk takes tokens t = cblk mod gridDim.y).  The inputs of this
+  // thread's first two rotations are loaded before the slab, so that the fp64
+  // cos/sin run while the slab loads are in flight (loads complete in order).
+  const int pairs = d_rope / 2, ny = gridDim.y;
+  const int n_rope = ((n_tok - cblk + ny - 1) / ny) * pairs;
+  auto rope_item = [&](int i, int* t, int* p) {
+    *t = cblk + ny * (i / pairs);
+    *p = i % pairs;
+  };
+  // (indices clamped so the loads need no branch; unused ones are dropped below)
+  int32_t r_pos[2];
+  uint32_t r_q[2];
+  double r_f[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    int t, p;
+    rope_item(min(tid + 256 * j, max(n_rope - 1, 0)), &t, &p);
+    t = min(t, n_tok - 1);
+    r_pos[j] = pos[t];
+    r_q[j] = *(const uint32_t*)(q_rope + ((int64_t)t * H + s) * d_rope + 2 * p);
+    r_f[j] = freqs.inv_freq[p];
+  }
   // slab loads (W_UK[s][:, cblk*128 .. +127]) and the first block's queries, all in flight together
   const uint16_t* wsrc = w_uk + (int64_t)s * kNope * d_c + cblk * kAbsorbCols;
   u32x4 wv[kChunks];
@@ -84,6 +107,28 @@ __global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __res
   };
   bf16x8 qf[kSteps];
   load_q(0, qf);
+  auto rotate = [&](int32_t pt, uint32_t qv, double f) {
+    float cs, sn, ox, oy;
+    rope_cos_sin(pt, f, &cs, &sn);
+    rope_pair(bf16_bits_to_f32((uint16_t)(qv & 0xffffu)), bf16_bits_to_f32((uint16_t)(qv >> 16)), cs, sn, &ox, &oy);
+    return (uint32_t)f32_to_bf16_bits(ox) | ((uint32_t)f32_to_bf16_bits(oy) << 16);
+  };
+  auto rope_dst = [&](int i) {
+    int t, p;
+    rope_item(i, &t, &p);
+    return (uint32_t*)(q_abs + ((int64_t)t * H + s) * d_k + d_c + 2 * p);
+  };
+  // computed for every lane (clamped items included) so the preloads stay ahead of the slab
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const uint32_t v = rotate(r_pos[j], r_q[j], r_f[j]);
+    if (tid + 256 * j < n_rope) *rope_dst(tid + 256 * j) = v;
+  }
+  for (int i = tid + 512; i < n_rope; i += 256) {   // more than 512 rotations: rest loaded here
+    int t, p;
+    rope_item(i, &t, &p);
+    *rope_dst(i) = rotate(pos[t], *(const uint32_t*)(q_rope + ((int64_t)t * H + s) * d_rope + 2 * p), freqs.inv_freq[p]);
+  }
   // the first block's queries are consumed here, together with the slab, so
   // that both sets of loads share one memory latency
 #pragma unroll
@@ -127,23 +172,6 @@ __global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __res
     }
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) qf[ks] = qn[ks];
-  }
-  // the rotated query part of head s: the d_c / 128 work-groups of the head
-  // share it, work-group cblk taking tokens t = cblk (mod gridDim.y)
-  {
-    const int pairs = d_rope / 2;
-    const int ny = gridDim.y;
-    const int n_mine = (n_tok - cblk + ny - 1) / ny;
-    for (int i = tid; i < n_mine * pairs; i += 256) {
-      const int t = cblk + ny * (i / pairs), p = i % pairs;
-      const int64_t row = (int64_t)t * H + s;
-      float cs, sn, ox, oy;
-      rope_cos_sin(pos[t], freqs.inv_freq[p], &cs, &sn);
-      rope_pair(bf16_bits_to_f32(q_rope[row * d_rope + 2 * p]), bf16_bits_to_f32(q_rope[row * d_rope + 2 * p + 1]),
-                cs, sn, &ox, &oy);
-      q_abs[row * d_k + d_c + 2 * p] = f32_to_bf16_bits(ox);
-      q_abs[row * d_k + d_c + 2 * p + 1] = f32_to_bf16_bits(oy);
-    }
   }
 }
 
