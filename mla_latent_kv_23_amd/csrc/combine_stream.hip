@@ -3,121 +3,107 @@
 // row, M = max_k m_k, L = sum_k 2^(m_k - M) l_k, o = sum_k 2^(m_k - M) O_k / L,
 // lse = (M + log2 L) ln 2.  A piece that saw no key (l_k = 0) has weight 0.
 //
-// One work-group per (sequence, 16 rows); thread t owns row t/16 and 32
-// consecutive latent dims, so each row's 2 KB per partial is read by 16
-// consecutive lanes.
+// One work-group per (sequence, 4 rows), one wave per row: lane i owns latent
+// dims 4i .. 4i+3 and 256 + 4i .. +3, so each load instruction reads 1 KB of
+// one row contiguously, and the loads of four pieces are in flight at once.
 #include "mla_internal.h"
 
 namespace mla {
 namespace {
 
-constexpr int kRowsPerBlock = 16;
+constexpr int kRowsPerBlock = 4;
 constexpr int kDc = 512;
 constexpr int kGroup = 4;   // pieces whose loads are in flight together
 
 typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __global__ void __launch_bounds__(256) combine_stream_kernel(const float* __restrict__ ws_o,
                                                              const float* __restrict__ ws_stats,
                                                              const int32_t* __restrict__ seqlens, int n_seq,
                                                              int rows_per_seq, SplitLayout lay,
                                                              uint16_t* __restrict__ o_lat, float* __restrict__ lse) {
-  __shared__ int32_t s_scan[8];
-  __shared__ int64_t s_range[4];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int b = blockIdx.x;
-  // tiles before sequence b and in total (same clamped lengths as the decode kernel)
-  const int chunk = (n_seq + 255) / 256;
-  const int lo = min(tid * chunk, n_seq), hi = min(lo + chunk, n_seq);
+  const int r = blockIdx.y * kRowsPerBlock + wave;
+  if (r >= rows_per_seq) return;
+  // Each wave finds its sequence's pieces by itself (no barrier): tiles before
+  // sequence b and in total, with the decode kernel's clamped lengths.
   int before = 0, all = 0;
-  for (int i = lo; i < hi; ++i) {
+  for (int i = lane; i < n_seq; i += 64) {
     const int32_t L = min(max(seqlens[i], 0), lay.max_len);
     const int nt = (L + lay.tile - 1) / lay.tile;
     all += nt;
     if (i < b) before += nt;
   }
+#pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
     before += __shfl_xor(before, off, 64);
     all += __shfl_xor(all, off, 64);
   }
-  if (lane == 0) {
-    s_scan[wave] = before;
-    s_scan[4 + wave] = all;
-  }
-  __syncthreads();
-  if (tid == 0) {
-    const int64_t start = (int64_t)s_scan[0] + s_scan[1] + s_scan[2] + s_scan[3];
-    const int64_t total = (int64_t)s_scan[4] + s_scan[5] + s_scan[6] + s_scan[7];
-    const int32_t L = min(max(seqlens[b], 0), lay.max_len);
-    const int64_t nb = (L + lay.tile - 1) / lay.tile;
-    int64_t wf = 0, wl = 0;
-    if (nb > 0) {
-      wf = unit_of_tile(start, total, lay.n_splits);
-      wl = unit_of_tile(start + nb - 1, total, lay.n_splits);
-    }
-    s_range[0] = wf;
-    s_range[1] = (nb == 0 || wf == wl) ? 0 : wl - wf + 1;   // 0: the decode kernel wrote this sequence
-    s_range[2] = total;
-  }
-  __syncthreads();
-  const int64_t wf = s_range[0], count = s_range[1], total = s_range[2];
-  if (count == 0) return;
-  const int r = blockIdx.y * kRowsPerBlock + (tid >> 4);
-  if (r >= rows_per_seq) return;
-  const int d0 = (tid & 15) * 32;
+  const int64_t total = all;
+  const int32_t Lb = min(max(seqlens[b], 0), lay.max_len);
+  const int64_t nb = (Lb + lay.tile - 1) / lay.tile;
+  if (nb == 0) return;
+  const int64_t wf = unit_of_tile(before, total, lay.n_splits);
+  const int64_t wl = unit_of_tile(before + nb - 1, total, lay.n_splits);
+  if (wf == wl) return;                        // the decode kernel wrote this sequence
+  const int64_t count = wl - wf + 1;
 
-  // Online merge over the pieces, four at a time: the stats and the 32 values
-  // of all four pieces are loaded before any is used (one memory latency per
-  // group), then folded in against a running maximum m:
+  // Online merge over the pieces, four at a time: the stats and values of the
+  // group are loaded before any is used (one memory latency per group), then
+  // folded in against a running maximum m:
   //   acc <- acc 2^(m - m') + 2^(m_k - m') O_k,  tot likewise with l_k.
+  // Pieces are taken 64 at a time, lane j telling whether unit wf + k0 + j
+  // owns a tile (a unit that owns none left nothing in its slot).
   float m = -INFINITY, tot = 0.f;
-  float acc[32];
+  f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+  for (int64_t k64 = 0; k64 < count; k64 += 64) {
+    const int64_t w_l = wf + k64 + lane;
+    const bool owns = k64 + lane < count &&
+                      unit_first_tile(w_l, total, lay.n_splits) < unit_first_tile(w_l + 1, total, lay.n_splits);
+    const uint64_t owners = __ballot(owns);
+    const int64_t n_here = min(count - k64, (int64_t)64);
+    for (int k0 = 0; k0 < n_here; k0 += kGroup) {
+      f32x2 st[kGroup];
+      f32x4 v[kGroup][2];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) acc[i] = 0.f;
-  for (int64_t k0 = 0; k0 < count; k0 += kGroup) {
-    float sm[kGroup], sl[kGroup];
-    f32x4 v[kGroup][8];
+      for (int j = 0; j < kGroup; ++j) {
+        if (k0 + j < n_here) {
+          const int64_t row = (wf + k64 + k0 + j + b) * rows_per_seq + r;
+          st[j] = *(const f32x2*)(ws_stats + row * 2);
+          const f32x4* src = (const f32x4*)(ws_o + row * kDc) + lane;
+          v[j][0] = src[0];
+          v[j][1] = src[64];
+        }
+      }
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      const int64_t w = wf + min(k0 + j, count - 1);   // clamped: a repeated piece is masked below
-      const float* st = ws_stats + ((w + b) * rows_per_seq + r) * 2;
-      sm[j] = st[0];
-      sl[j] = st[1];
-      const f32x4* src = (const f32x4*)(ws_o + ((w + b) * rows_per_seq + r) * kDc + d0);
+      for (int j = 0; j < kGroup; ++j) {
+        if (k0 + j >= n_here) break;
+        if (!((owners >> (k0 + j)) & 1) || !(st[j][1] > 0.f)) continue;
+        const float mn = fmaxf(m, st[j][0]);
+        const float keep = exp2f(m - mn);          // 0 while nothing is accumulated (m = -inf)
+        const float wgt = exp2f(st[j][0] - mn);
+        tot = fmaf(tot, keep, wgt * st[j][1]);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) v[j][i] = src[i];
-    }
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int j = 0; j < kGroup; ++j) {
-      const int64_t w = wf + k0 + j;
-      if (k0 + j >= count) break;
-      // a unit that owns no tile left nothing in its slot
-      if (unit_first_tile(w, total, lay.n_splits) == unit_first_tile(w + 1, total, lay.n_splits)) continue;
-      if (!(sl[j] > 0.f)) continue;
-      const float mn = fmaxf(m, sm[j]);
-      const float keep = exp2f(m - mn);          // 0 while nothing is accumulated (m = -inf)
-      const float wgt = exp2f(sm[j] - mn);
-      tot = fmaf(tot, keep, wgt * sl[j]);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) acc[4 * i + e] = fmaf(acc[4 * i + e], keep, wgt * v[j][i][e]);
-      m = mn;
+          for (int e = 0; e < 4; ++e) acc[h][e] = fmaf(acc[h][e], keep, wgt * v[j][h][e]);
+        m = mn;
+      }
     }
   }
   const float inv = tot > 0.f ? 1.0f / tot : 0.f;
-  u32x4* dst = (u32x4*)(o_lat + ((int64_t)b * rows_per_seq + r) * kDc + d0);
+  u32x2* dst = (u32x2*)(o_lat + ((int64_t)b * rows_per_seq + r) * kDc) + lane;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    u32x4 v;
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      v[e] = (uint32_t)f32_to_bf16_bits(acc[8 * i + 2 * e] * inv) |
-             ((uint32_t)f32_to_bf16_bits(acc[8 * i + 2 * e + 1] * inv) << 16);
-    dst[i] = v;
+  for (int h = 0; h < 2; ++h) {
+    u32x2 o;
+    o[0] = (uint32_t)f32_to_bf16_bits(acc[h][0] * inv) | ((uint32_t)f32_to_bf16_bits(acc[h][1] * inv) << 16);
+    o[1] = (uint32_t)f32_to_bf16_bits(acc[h][2] * inv) | ((uint32_t)f32_to_bf16_bits(acc[h][3] * inv) << 16);
+    dst[64 * h] = o;
   }
-  if ((tid & 15) == 0)
+  if (lane == 0)
     lse[(int64_t)b * rows_per_seq + r] = tot > 0.f ? (m + log2f(tot)) * 0.69314718055994530942f : -INFINITY;
 }
 
