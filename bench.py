@@ -7,7 +7,9 @@ Prints one JSON line.  `value` is whole-step throughput (query tokens per
 second) with every input resident in HBM.  `roofline` reports the decode
 kernel (the dominant one) against the HBM bound: algorithmic bytes = the
 cache read once (1152 B per cached token), divided by the decode launch time
-measured with HIP events around each decode launch inside the timed region.
+measured with HIP events around each decode launch inside the timed region
+(events created without the system-scope fence, so that recording them does
+not write back and invalidate the caches between kernels).
 `cpu_baseline` times the CPU oracle (non-absorbed form, float64) on a bounded
 sample of the same workload.
 """
@@ -78,6 +80,44 @@ def parse():
                     help="instead of the benchmark, run a plain device copy of this many MiB (5 launches): "
                          "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
     return ap.parse_args()
+
+
+class TimingEvent:
+    """A HIP event for timing only: hipEventDisableSystemFence, recorded on a
+    given torch stream (torch's own events carry a system-scope fence, whose
+    cache write-back and invalidation stall the next kernel by a few us)."""
+    _rt = None
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self):
+        import ctypes
+        if TimingEvent._rt is None:
+            rt = ctypes.CDLL("libamdhip64.so.7")   # the HIP runtime torch has loaded
+            rt.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+            rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            TimingEvent._rt = rt
+        self._ct = ctypes
+        self.h = ctypes.c_void_p()
+        self._ok(TimingEvent._rt.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE))
+
+    @staticmethod
+    def _ok(code):
+        if code != 0:
+            raise RuntimeError(f"HIP event call failed with code {code}")
+
+    def record(self, stream):
+        self._ok(TimingEvent._rt.hipEventRecord(self.h, self._ct.c_void_p(stream.cuda_stream)))
+
+    def elapsed_time(self, end) -> float:
+        ms = self._ct.c_float()
+        self._ok(TimingEvent._rt.hipEventElapsedTime(self._ct.byref(ms), self.h, end.h))
+        return ms.value
+
+    def __del__(self):
+        if TimingEvent._rt is not None and self.h:
+            TimingEvent._rt.hipEventDestroy(self.h)
 
 
 def calib_copy(mib):
@@ -171,7 +211,7 @@ def main():
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
-    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    evs = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
