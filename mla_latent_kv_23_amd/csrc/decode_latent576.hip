@@ -45,6 +45,11 @@ static_assert(kKAhead % 4 == 0, "K prefetch depth is a multiple of the 4 per-lan
 
 constexpr int kOffP = kStages * kTileBytes;                 // 147456: two P buffers (tile T in buffer T % 2)
 constexpr int kLdsBytes = kOffP + 2 * kPBufBytes;           // 163840
+// fp8 cache: two bf16 tile buffers (tile T in buffer T % 2), then a 3-slot
+// staging ring for the raw tiles, ending where the P buffers start
+constexpr int kF8Slots = 3;
+constexpr int kOffF = 2 * kTileBytes;
+static_assert(kOffF + kF8Slots * kF8StageBytes == kOffP, "fp8 buffers use the bf16 ring's space");
 // Small scratch shares P buffer 0; it is used only while no weights are live
 // there: the sequence scan before the first tile, the redo flags after the
 // last PV of an attempt, the (l, m) rows in the piece epilogue.
@@ -86,6 +91,14 @@ __device__ __forceinline__ void wait_tiles(int64_t n) {
 }
 
 
+__device__ __forceinline__ void wait_tiles_fp8(int64_t n) {
+  if (n >= 3) wait_vmcnt<3 * kF8LoadsPerWave>();
+  else if (n == 2) wait_vmcnt<2 * kF8LoadsPerWave>();
+  else if (n == 1) wait_vmcnt<kF8LoadsPerWave>();
+  else wait_vmcnt<0>();
+}
+
+template <bool kFp8>
 __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t* __restrict__ block_table,
                                                           const int32_t* __restrict__ seqlens) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
@@ -219,6 +232,41 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       }
       return a.pool + (int64_t)blk * a.block_bytes + (int64_t)(tok0 % a.block_size) * kRowBytes;
     };
+    // rows of tile T that hold tokens of the sequence (0 for a padding block entry)
+    auto tile_valid = [&](int64_t T) -> int {
+      const int tok0 = (int)(T - seq_start) * kTile;
+      return bt_row[tok0 / a.block_size] < 0 ? 0 : min(kTile, L - tok0);
+    };
+    // issue this wave's share of the loads of tile T: bf16 straight into ring
+    // stage T % kStages; fp8 into staging slot T % 3 (expanded later)
+    auto load_tile = [&](int64_t T) {
+      if constexpr (!kFp8) {
+        int valid;
+        const uint8_t* src = tile_src(T, &valid);
+        issue_tile(src, valid, lds + (int)(T % kStages) * kTileBytes, wave, lane);
+      } else {
+        const int tok0 = (int)(T - seq_start) * kTile;
+        const int32_t blk = bt_row[tok0 / a.block_size];
+        const uint8_t* bp = blk < 0 ? a.pool : a.pool + (int64_t)blk * a.block_bytes;
+        issue_tile_fp8(bp, blk < 0 ? 0 : tok0 % a.block_size, a.block_size, tile_valid(T),
+                       lds + kOffF + (int)(T % kF8Slots) * kF8StageBytes, wave, lane);
+      }
+    };
+    // wait until at most n tiles' loads of this wave are still in flight
+    auto wait_tile = [&](int64_t n) {
+      if constexpr (!kFp8) wait_tiles(n);
+      else wait_tiles_fp8(n);
+    };
+    // fp8: staged tile T -> bf16 buffer T % 2
+    auto expand = [&](int64_t T) {
+      expand_tile_fp8(lds + kOffF + (int)(T % kF8Slots) * kF8StageBytes, lds + (int)(T & 1) * kTileBytes, wave,
+                      lane);
+    };
+    // LDS address of tile T's bf16 image
+    auto tile_base = [&](int64_t T) -> uint32_t {
+      const int slot = kFp8 ? (int)(T & 1) : (int)(T % kStages);
+      return (uint32_t)(uintptr_t)(lds + slot * kTileBytes);
+    };
 
     for (;;) {                               // attempts: a second one only after a reference jump
 #pragma unroll
@@ -227,56 +275,41 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       for (int i = 0; i < 16; ++i) o15[i] = 0.f;
       l_part = 0.f;
       int64_t T_issue = p0;                  // loads in flight cover [T, T_issue)
-      for (int st = 0; st < kStages - 1 && T_issue < p1; ++st, ++T_issue) {
-        int valid;
-        const uint8_t* src = tile_src(T_issue, &valid);
-        issue_tile(src, valid, lds + (int)(T_issue % kStages) * kTileBytes, wave, lane);
-      }
+      for (int st = 0; st < kStages - 1 && T_issue < p1; ++st) load_tile(T_issue++);
       bool redo = false;                     // a reference jumped during this attempt (wave-uniform)
-      wait_tiles(T_issue - 1 - p0);          // tile p0 has landed
+      wait_tile(T_issue - 1 - p0);           // tile p0 has landed
       lds_barrier();
-      // One barrier per tile, after the weights are written: it publishes P(T)
-      // (buffer T % 2) and tile T+1 (each wave waits for its own loads of it
-      // first), and every wave has finished PV(T-1) by then, so the next tile
-      // load goes into the stage of T-1.
-      for (int64_t T = p0; T < p1; ++T) {
-        const uint32_t tb = (uint32_t)(uintptr_t)(lds + (int)(T % kStages) * kTileBytes);
+      if constexpr (kFp8) {
+        expand(p0);
+        lds_barrier();
+      }
+
+      // ---- softmax of tile T against the reference max (exp2 domain); the
+      // weights go to P buffer T % 2.  The scale is positive (checked by the
+      // API), so the max of the raw scores gives the max of the scaled ones and
+      // the scale folds into one FMA per weight.
+      auto softmax = [&](const f32x16& sacc, const float (&s_rope)[16], int64_t T) {
         const int tok0 = (int)(T - seq_start) * kTile;
-
-        // ---- S^T = K Q^T for this wave's 32 pairs: lane holds pair my_pair, tokens 8(i/4)+4*half+i%4.
-        // K-step k reads logical chunk 2k + half of row lane%32: chunk group k/4
-        // adds 1 KB, so four per-lane bases (by k%4) plus immediates suffice.
-        f32x16 sacc = {};
-        {
-          // kKAhead K fragments in flight ahead of the MFMA chain (the LDS is
-          // shared by the four waves, whose reads queue behind each other)
-          bf16x8 kf[kKAhead];
+        float sv[16], sc[16];
+        if constexpr (kFp8) {
+          // this lane's 16 token scales (rows past the tile's valid ones hold
+          // no data: scale 0 and score -inf)
+          const lds_u8* scl = lds + kOffF + (int)(T % kF8Slots) * kF8StageBytes + kF8OffScales + 1024 * wave;
+          const int nv = tile_valid(T);
 #pragma unroll
-          for (int k = 0; k < kKAhead; ++k) kf[k] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (k / 4));
+          for (int g = 0; g < 4; ++g) {
+            const f32x4 s4 = *(const lds_f32x4*)(scl + 4 * (8 * g + 4 * half));
 #pragma unroll
-          for (int k = 0; k < kQSteps; ++k) {
-            const bf16x8 cur = kf[k % kKAhead];
-            if (k + kKAhead < kQSteps)
-              kf[k % kKAhead] =
-                  *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * ((k + kKAhead) / 4));
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, q[k], sacc, 0, 0, 0);
+            for (int e = 0; e < 4; ++e) {
+              const bool in = 8 * g + 4 * half + e < nv;
+              sc[4 * g + e] = in ? s4[e] : 0.f;
+              sv[4 * g + e] = in ? fmaf(sacc[4 * g + e], s4[e], s_rope[4 * g + e]) : -INFINITY;
+            }
           }
-          // issue order: kKAhead reads, then (MFMA, read) pairs, then the last kKAhead MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
+        } else {
 #pragma unroll
-          for (int k = 0; k < kQSteps - kKAhead; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-          }
-          __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
+          for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
         }
-
-        // ---- softmax against the reference max (exp2 domain).  The scale is
-        // positive (checked by the API), so the max of the raw scores gives the
-        // max of the scaled ones and the scale folds into one FMA per weight.
-        float sv[16];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
         // causal / length mask: only a tile reaching past the first query row's
         // last visible token needs it (wave-uniform test)
         if (tok0 + kTile > L - a.q_per_seq + 1) {
@@ -312,29 +345,28 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         for (int i = 0; i < 16; i += 2) {
           const f32x2 pv = {__builtin_amdgcn_exp2f(fmaf(sv[i], sl2, neg_m)),
                             __builtin_amdgcn_exp2f(fmaf(sv[i + 1], sl2, neg_m))};
-          const bf16x2 pb2 = __builtin_convertvector(pv, bf16x2);              // round to nearest even
-          psum = __builtin_amdgcn_fdot2_f32_bf16(pb2, ones, psum, false);     // sum of the rounded weights
-          pk[i / 2] = *(const uint32_t*)&pb2;
-        }
-        l_part += psum;
-        {
-          const uint32_t pw = p_wr + (uint32_t)(T & 1) * kPBufBytes;
-#pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
-            const u32x2 v2 = {pk[2 * qq], pk[2 * qq + 1]};
-            *(lds_u32x2*)(uintptr_t)(pw + 16 * (qq ^ psw)) = v2;
+          if constexpr (kFp8) {
+            // the value is code x scale: the scale goes into the PV weight
+            psum += pv[0] + pv[1];
+            const bf16x2 pb2 = __builtin_convertvector(f32x2{pv[0] * sc[i], pv[1] * sc[i + 1]}, bf16x2);
+            pk[i / 2] = *(const uint32_t*)&pb2;
+          } else {
+            const bf16x2 pb2 = __builtin_convertvector(pv, bf16x2);              // round to nearest even
+            psum = __builtin_amdgcn_fdot2_f32_bf16(pb2, ones, psum, false);     // sum of the rounded weights
+            pk[i / 2] = *(const uint32_t*)&pb2;
           }
         }
-        if (T + 1 < p1) wait_tiles(T_issue - 2 - T);   // tile T+1 has landed (later ones may be in flight)
-        lds_barrier();
-        if (T_issue < p1) {
-          int valid;
-          const uint8_t* src = tile_src(T_issue, &valid);
-          issue_tile(src, valid, lds + (int)(T_issue % kStages) * kTileBytes, wave, lane);
-          ++T_issue;
+        l_part += psum;
+        const uint32_t pw = p_wr + (uint32_t)(T & 1) * kPBufBytes;
+#pragma unroll
+        for (int qq = 0; qq < 4; ++qq) {
+          const u32x2 v2 = {pk[2 * qq], pk[2 * qq + 1]};
+          *(lds_u32x2*)(uintptr_t)(pw + 16 * (qq ^ psw)) = v2;
         }
+      };
 
-        // ---- O^T += V^T P^T: this wave's 128 dims x all 128 pairs
+      // ---- O^T += V^T P^T for tile T: this wave's 128 dims x all 128 pairs
+      auto pv = [&](uint32_t tb, int64_t T) {
         f32x16 t15 = {};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -364,6 +396,70 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         }
 #pragma unroll
         for (int i = 0; i < 16; ++i) o15[i] += t15[i];
+      };
+
+      // bf16: one barrier per tile, after the weights are written: it
+      // publishes P(T) (buffer T % 2) and tile T+1 (each wave waits for its own
+      // loads of it first), and every wave has finished PV(T-1) by then, so the
+      // next tile load goes into the stage of T-1.
+      // fp8: two barriers per tile.  The first (after the weights are written)
+      // publishes P(T) and the staged tile T+1; the expansion of tile T happened
+      // before the previous second barrier, so the next staging load goes into
+      // the slot of T, and tile T+1 is expanded into the bf16 buffer of T-1
+      // (whose PV also finished before it).  The second publishes the expanded
+      // tile T+1 and ends PV(T).
+      for (int64_t T = p0; T < p1; ++T) {
+        const uint32_t tb = tile_base(T);
+        // ---- S^T = K Q^T for this wave's 32 pairs: lane holds pair my_pair, tokens 8(i/4)+4*half+i%4.
+        // K-step k reads logical chunk 2k + half of row lane%32: chunk group k/4
+        // adds 1 KB, so four per-lane bases (by k%4) plus immediates suffice.
+        // fp8: the 4 RoPE k-steps (32..35) run first into their own sum, since
+        // only the latent part of a key is scaled (z = s_t <q_lat, code> + <q_R, k_R>).
+        f32x16 sacc = {};
+        float s_rope[16];
+        {
+          // kKAhead K fragments in flight ahead of the MFMA chain (the LDS is
+          // shared by the four waves, whose reads queue behind each other)
+          bf16x8 kf[kKAhead];
+#pragma unroll
+          for (int k = 0; k < kKAhead; ++k) {
+            const int kk = kFp8 ? (k + 32) % kQSteps : k;   // (kk % 4 == k % 4)
+            kf[k] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (kk / 4));
+          }
+#pragma unroll
+          for (int k = 0; k < kQSteps; ++k) {
+            const int kk = kFp8 ? (k + 32) % kQSteps : k;
+            const int kn = kFp8 ? (k + kKAhead + 32) % kQSteps : k + kKAhead;
+            const bf16x8 cur = kf[k % kKAhead];
+            if (k + kKAhead < kQSteps)
+              kf[k % kKAhead] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (kn / 4));
+            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, q[kk], sacc, 0, 0, 0);
+            if constexpr (kFp8) {
+              if (k == 3) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) s_rope[i] = sacc[i];
+                sacc = f32x16{};
+              }
+            }
+          }
+          // issue order: kKAhead reads, then (MFMA, read) pairs, then the last kKAhead MFMAs
+          __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
+#pragma unroll
+          for (int k = 0; k < kQSteps - kKAhead; ++k) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
+        }
+        softmax(sacc, s_rope, T);
+        if (T + 1 < p1) wait_tile(T_issue - 2 - T);   // (staged) tile T+1 has landed (later ones may be in flight)
+        lds_barrier();
+        if (T_issue < p1) load_tile(T_issue++);
+        if constexpr (kFp8) {
+          if (T + 1 < p1) expand(T + 1);
+        }
+        pv(tb, T);
+        if constexpr (kFp8) lds_barrier();
       }
       wait_vmcnt<0>();
       lds_barrier();                         // every wave is done with the last tile and P (the flags share P buffer 0)
@@ -457,7 +553,8 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
 }  // namespace
 
 bool decode576_supported(const mla_dims& d, int32_t q_per_seq) {
-  if (d.d_c != 512 || d.d_rope != 64 || d.act_dtype != MLA_BF16 || d.cache_dtype != MLA_BF16) return false;
+  if (d.d_c != 512 || d.d_rope != 64 || d.act_dtype != MLA_BF16) return false;
+  if (d.cache_dtype != MLA_BF16 && d.cache_dtype != MLA_FP8_E4M3) return false;
   if (d.block_size % kTile != 0) return false;
   if (q_per_seq <= 0 || kPairs % q_per_seq != 0) return false;
   const int hpw = kPairs / q_per_seq;
@@ -490,7 +587,10 @@ mla_status launch_decode576(const mla_dims& d, const DecodePlan& plan, int32_t n
   a.heads_per_wg = kPairs / q_per_seq;
   a.scale_log2 = d.softmax_scale * 1.4426950408889634f;
   dim3 grid(plan.n_splits, d.n_heads / a.heads_per_wg);
-  hipLaunchKernelGGL(decode576_kernel, grid, dim3(256), 0, st, a, block_table, seqlens);
+  if (d.cache_dtype == MLA_FP8_E4M3)
+    hipLaunchKernelGGL(decode576_kernel<true>, grid, dim3(256), 0, st, a, block_table, seqlens);
+  else
+    hipLaunchKernelGGL(decode576_kernel<false>, grid, dim3(256), 0, st, a, block_table, seqlens);
   return launch_status();
 }
 

@@ -1,7 +1,7 @@
 // Device helpers shared by the tuned latent-576 decode kernels: operand
 // types, the bf16 cache tile (32 rows x 1152 B) and its swizzled LDS layout,
-// barrier / wait helpers, the XCD-aware unit order, and the direct-to-LDS tile
-// loader.
+// barrier / wait helpers, the XCD-aware unit order, the direct-to-LDS tile
+// loaders (bf16 tiles, and raw fp8 tiles) and the fp8 -> bf16 tile expansion.
 #pragma once
 
 #include <math.h>
@@ -26,6 +26,7 @@ typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
 typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
 
 constexpr int kDc = 512, kDk = 576, kRowBytes = kDk * 2;   // bf16 cache row
 constexpr int kTile = kDecodeTile;                          // 32 tokens
@@ -113,7 +114,96 @@ __device__ __forceinline__ void issue_tile(const uint8_t* src, int valid, lds_u8
       : "memory", "m0", "scc");
 }
 
+// An fp8 cache tile (E4M3FN codes, one fp32 scale per token, bf16 k_R; the
+// block layout [bs][512] codes | [bs] scales | [bs][64] k_R) is staged raw and
+// then expanded into the bf16 tile layout above.  Staging layout (24 KB):
+//   codes  [0, 16384):     1 KB block 4w + i holds rows 8w .. 8w+7, bytes
+//                          128i .. 128i+127 of each (lane l: row 8w + l/8,
+//                          bytes 128i + 16(l % 8) .. +15);
+//   k_R    [16384, 20480): 1 KB block w holds rows 8w .. 8w+7 (lane l: row
+//                          8w + l/8, bytes 16(l % 8) .. +15);
+//   scales [20480, 24576): wave w's own copy of the 32 scales at 20480 + 1024w.
+constexpr int kF8Codes = kTile * kDc;                       // 16384
+constexpr int kF8OffRope = kF8Codes;
+constexpr int kF8OffScales = kF8OffRope + kTile * 128;      // 20480
+constexpr int kF8StageBytes = kF8OffScales + 4 * 1024;      // 24576
+constexpr int kF8LoadsPerWave = 6;                          // 4 code blocks, 1 k_R block, 1 scale copy
+
+// Copy fp8 tile rows [slot, slot + 32) of the cache block at `blk` (block_size
+// tokens) into staging `dst`.  Rows at or beyond `valid` re-read row 0 (codes
+// and k_R; their scales are whatever the block holds and must not be used).
+__device__ __forceinline__ void issue_tile_fp8(const uint8_t* blk, int slot, int block_size, int valid, lds_u8* dst,
+                                               int wave, int lane) {
+  const int row = 8 * wave + (lane >> 3);
+  const bool in = row < valid;
+  const uint32_t off_c = (in ? row * kDc : 0) + 16 * (lane & 7);
+  const uint32_t off_r = (in ? row * 128 : 0) + 16 * (lane & 7);
+  const uint32_t off_s = 16 * (lane & 7);
+  const uint32_t base = (uint32_t)(uintptr_t)dst;
+  const uint32_t m_c = (uint32_t)__builtin_amdgcn_readfirstlane(base + (uint32_t)(wave * 4096));
+  const uint32_t m_r = (uint32_t)__builtin_amdgcn_readfirstlane(base + (uint32_t)(kF8OffRope + wave * 1024));
+  const uint32_t m_s = (uint32_t)__builtin_amdgcn_readfirstlane(base + (uint32_t)(kF8OffScales + wave * 1024));
+  auto sreg = [](const uint8_t* p) -> uint64_t {
+    const uint64_t a = (uint64_t)(uintptr_t)p;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+  };
+  const uint64_t s_c = sreg(blk + (int64_t)slot * kDc);
+  const uint64_t s_r = sreg(blk + (int64_t)block_size * (kDc + 4) + (int64_t)slot * 128);
+  const uint64_t s_s = sreg(blk + (int64_t)block_size * kDc + (int64_t)slot * 4);
+  uint32_t t;
+  asm volatile(
+      "s_mov_b32 m0, %[mc]\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[vc], %[sc]\n\t"
+      "v_add_u32 %[t], 0x80, %[vc]\n\ts_add_u32 m0, %[mc], 0x400\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[sc]\n\t"
+      "v_add_u32 %[t], 0x100, %[vc]\n\ts_add_u32 m0, %[mc], 0x800\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[sc]\n\t"
+      "v_add_u32 %[t], 0x180, %[vc]\n\ts_add_u32 m0, %[mc], 0xc00\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[t], %[sc]\n\t"
+      "s_mov_b32 m0, %[mr]\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[vr], %[sr]\n\t"
+      "s_mov_b32 m0, %[ms]\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %[vs], %[ss]"
+      : [t] "=&v"(t)
+      : [vc] "v"(off_c), [vr] "v"(off_r), [vs] "v"(off_s), [sc] "s"(s_c), [sr] "s"(s_r), [ss] "s"(s_s),
+        [mc] "s"(m_c), [mr] "s"(m_r), [ms] "s"(m_s)
+      : "memory", "m0", "scc");
+}
+
 #pragma clang diagnostic pop
+
+// Expand a staged fp8 tile into the bf16 tile layout at `dst`: latent dim d
+// of row r becomes bf16(code) (every E4M3FN value is exactly a bf16), k_R is
+// copied; the per-token scale is applied to the scores and weights instead.
+// Thread (wave w, lane l) converts the 64 codes its wave's loads brought to
+// lane l (row 8w + l/8, dims 128i + 16(l % 8) .. +15 for i = 0..3) and copies
+// k_R chunk l % 8 of the same row.
+__device__ __forceinline__ void expand_tile_fp8(const lds_u8* stage, lds_u8* dst, int wave, int lane) {
+  const int r = 8 * wave + (lane >> 3), m = lane & 7;
+  const u32x4 kr = *(const lds_u32x4*)(stage + kF8OffRope + 1024 * wave + 16 * lane);
+  u32x4 codes[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) codes[i] = *(const lds_u32x4*)(stage + 1024 * (4 * wave + i) + 16 * lane);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t w[8];
+#pragma unroll
+    for (int d = 0; d < 4; ++d) {
+      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(codes[i][d], false);   // codes 4d, 4d+1
+      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(codes[i][d], true);    // codes 4d+2, 4d+3
+      const bf16x2 b0 = __builtin_convertvector(lo, bf16x2);                   // exact
+      const bf16x2 b1 = __builtin_convertvector(hi, bf16x2);
+      w[2 * d] = *(const uint32_t*)&b0;
+      w[2 * d + 1] = *(const uint32_t*)&b1;
+    }
+    // dims 128i + 16m .. +15 are logical chunks 16i + 2m and 16i + 2m + 1
+    *(lds_u32x4*)(dst + tile_off(r, 16 * i + 2 * m)) = u32x4{w[0], w[1], w[2], w[3]};
+    *(lds_u32x4*)(dst + tile_off(r, 16 * i + 2 * m + 1)) = u32x4{w[4], w[5], w[6], w[7]};
+  }
+  *(lds_u32x4*)(dst + tile_off(r, 64 + m)) = kr;
+}
 
 }  // namespace
 }  // namespace mla

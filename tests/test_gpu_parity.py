@@ -136,14 +136,16 @@ def test_chain_vs_non_absorbed_oracle(name, cuda_device):
     U.assert_close(lse, ref["lse"], w.act_dtype, "lse")
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
 @pytest.mark.parametrize("lens", [[31, 32, 33], [63, 64, 65], [1, 2, 127], [96, 4097]])
-def test_decode_tile_edges(lens, cuda_device):
+def test_decode_tile_edges(lens, cache, cuda_device):
     """Lengths around the 32-token tile and 64-token block edges, single-token
-    sequences and padded block-table entries (the pool is NaN-poisoned)."""
+    sequences and padded block-table entries (the pool is NaN-poisoned), for
+    the bf16 cache and the fp8 cache (E4M3FN codes, per-token scale)."""
     import mla_latent_kv_23_amd as M
-    w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=len(lens))
+    w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=len(lens), cache_dtype=cache)
     inp = S.make_inputs(w, 4242, seqlens=torch.tensor(lens, dtype=torch.int32), spare_blocks=3)
-    U.say(f"[edges] {lens}")
+    U.say(f"[edges] {cache} {lens}")
     d = U.dims_of(w)
     pos = S.query_positions(inp["seqlens"], 1).numpy()
     q_abs = O.absorb_q(inp["q_nope"].double().numpy(), inp["q_rope"].double().numpy(),
@@ -159,25 +161,26 @@ def test_decode_tile_edges(lens, cuda_device):
         cu = inp["cu_seqlens"].numpy()
         for b, Lb in enumerate(lens):
             c, kr = O.cached_token_values(inp["c_kv"][cu[b]:cu[b] + Lb].double().numpy(),
-                                          inp["k_rope"][cu[b]:cu[b] + Lb].double().numpy(), np.arange(Lb), "bf16",
+                                          inp["k_rope"][cu[b]:cu[b] + Lb].double().numpy(), np.arange(Lb), cache,
                                           w.rope_base)
             want_o, want_lse = O.decode_absorbed_form(q_r[b], c, kr, pos[b], w.softmax_scale)
             U.assert_close(o_lat[b], want_o, "bf16", f"o_lat L={Lb} splits={ns}")
             U.assert_close(lse[b], want_lse, "bf16", f"lse L={Lb} splits={ns}")
 
 
-def test_decode_large_logit_jump(cuda_device):
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_decode_large_logit_jump(cache, cuda_device):
     """Late keys with much larger scores than the first tile: the kernel's per-pair
     reference max must move (second pass) and still match the oracle."""
     import mla_latent_kv_23_amd as M
-    w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=2)
+    w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=2, cache_dtype=cache)
     inp = S.make_inputs(w, 99, seqlens=torch.tensor([700, 300], dtype=torch.int32))
     cu = inp["cu_seqlens"]
     # tokens 600.. of sequence 0 get a 64x larger latent: scores jump by far more than 2^16 in exp2 units
     c = inp["c_kv"].float()
     c[cu[0] + 600:cu[0] + 700] *= 64.0
     inp["c_kv"] = c.to(torch.bfloat16)
-    U.say("[jump]")
+    U.say(f"[jump] {cache}")
     d = U.dims_of(w)
     pos = S.query_positions(inp["seqlens"], 1).numpy()
     q_abs = O.absorb_q(inp["q_nope"].double().numpy(), inp["q_rope"].double().numpy(),
@@ -194,7 +197,7 @@ def test_decode_large_logit_jump(cuda_device):
             Lb = int(inp["seqlens"][b])
             cc, kr = O.cached_token_values(inp["c_kv"][cu[b]:cu[b] + Lb].double().numpy(),
                                            inp["k_rope"][cu[b]:cu[b] + Lb].double().numpy(), np.arange(Lb),
-                                           "bf16", w.rope_base)
+                                           cache, w.rope_base)
             want_o, want_lse = O.decode_absorbed_form(q_r[b], cc, kr, pos[b], w.softmax_scale)
             # relative bars: the outputs here are large (latents scaled by 64)
             mx, rel = U.errors(o_lat[b], want_o, "bf16")
