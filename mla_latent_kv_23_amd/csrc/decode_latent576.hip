@@ -98,7 +98,7 @@ __device__ __forceinline__ void wait_tiles_fp8(int64_t n) {
   else wait_vmcnt<0>();
 }
 
-template <bool kFp8>
+template <bool kFp8, int kPB>
 __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t* __restrict__ block_table,
                                                           const int32_t* __restrict__ seqlens) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
@@ -146,10 +146,17 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
   int b_first = __builtin_amdgcn_readfirstlane(misc[0]);
   int b_first_start = __builtin_amdgcn_readfirstlane(misc[1]);
 
-  // ---- per-wave identity of its 32 QK pairs; each lane owns pair 32*wave + lane%32
+  // ---- per-wave identity of its 32 QK pairs; each lane owns pair 32*wave + lane%32.
+  // The work-group serves 32 * kPB pairs; waves 0 .. kPB-1 run QK and the
+  // softmax for theirs, all four run PV.  With kPB < 4 a pair past the last
+  // query row (heads x rows fewer than the pairs) is padding: it repeats the
+  // last row's work and stores nothing.  kPB = 4 is only used without padding.
   const int hpw = a.heads_per_wg;
+  const bool qk_wave = kPB == 4 || wave < kPB;
   const int my_pair = 32 * wave + (lane & 31);
-  const int my_j = my_pair / hpw;
+  const int my_j_raw = my_pair / hpw;
+  const bool pad = kPB == 4 ? false : my_j_raw >= a.q_per_seq;
+  const int my_j = kPB == 4 ? my_j_raw : min(my_j_raw, a.q_per_seq - 1);
   const int my_s = hg * hpw + my_pair % hpw;
   const int half = lane >> 5;
   const int rows_per_seq = a.q_per_seq * a.n_heads;
@@ -192,13 +199,16 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
   lds_f32* s_m = (lds_f32*)(lds + kOffM);
   lds_i32* s_flag = (lds_i32*)(lds + kOffFlag);
 
-  // O^T tiles [db][pb] for dims 128*wave + 32*db, pairs 32*pb.  Tiles 0..14 are
-  // MFMA accumulators (AGPRs); tile 15 is kept in plain VGPRs (o15) and gets
-  // each tile's contribution added with vector ALU ops, so that the MFMA
-  // accumulators (15 O tiles + the S tile) fit the 256 AGPRs.  The
-  // accumulators are only ever MFMA-updated, zeroed, or stored raw.
-  f32x16 o[15];
-  float o15[16];
+  // O^T tiles [db][pb] for dims 128*wave + 32*db, pairs 32*pb.  With 16
+  // tiles (kPB = 4), tiles 0..14 are MFMA accumulators (AGPRs) and tile 15 is
+  // kept in plain VGPRs (o15), getting each tile's contribution added with
+  // vector ALU ops, so that the MFMA accumulators (15 O tiles + the S tile) fit
+  // the 256 AGPRs.  The accumulators are only ever MFMA-updated, zeroed, or
+  // stored raw.
+  constexpr bool kSplitTile = kPB == 4;
+  constexpr int kOAcc = kSplitTile ? 15 : 4 * kPB;
+  f32x16 o[kOAcc];
+  float o15[kSplitTile ? 16 : 1];
   bf16x8 q[kQSteps];
 
   // ---- the pieces: one per sequence overlapping [T0, T1)
@@ -213,7 +223,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     const int32_t* bt_row = block_table + (int64_t)b * a.max_blocks;
 
     // queries of this sequence: B operand fragments, pair my_pair, dims 16k + 8*half .. +7
-    {
+    if (qk_wave) {
       const int64_t row = ((int64_t)b * a.q_per_seq + my_j) * a.n_heads + my_s;
       const bf16x8* src = (const bf16x8*)(a.q_abs + row * kDk) + half;
 #pragma unroll
@@ -270,9 +280,11 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
 
     for (;;) {                               // attempts: a second one only after a reference jump
 #pragma unroll
-      for (int i = 0; i < 15; ++i) o[i] = f32x16{};
+      for (int i = 0; i < kOAcc; ++i) o[i] = f32x16{};
+      if constexpr (kSplitTile) {
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o15[i] = 0.f;
+        for (int i = 0; i < 16; ++i) o15[i] = 0.f;
+      }
       l_part = 0.f;
       int64_t T_issue = p0;                  // loads in flight cover [T, T_issue)
       for (int st = 0; st < kStages - 1 && T_issue < p1; ++st) load_tile(T_issue++);
@@ -370,10 +382,10 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         f32x16 t15 = {};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
-          bf16x8 pf[4];
+          bf16x8 pf[kPB];
           const uint32_t pbuf = p_rd + (uint32_t)(T & 1) * kPBufBytes + (uint32_t)(32 * ks * p_ks_sign);
 #pragma unroll
-          for (int pb = 0; pb < 4; ++pb) pf[pb] = *(const lds_bf16x8*)(uintptr_t)(pbuf + 32 * pb * kPRow);
+          for (int pb = 0; pb < kPB; ++pb) pf[pb] = *(const lds_bf16x8*)(uintptr_t)(pbuf + 32 * pb * kPRow);
           // V^T fragments for the 4 dim blocks: two transpose reads each (4 tokens apiece)
           bf16x4 h[8];
 #pragma unroll
@@ -388,14 +400,16 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
             const bf16x4 lo = h[(db >> 1) * 4 + (db & 1) * 2], hi = h[(db >> 1) * 4 + (db & 1) * 2 + 1];
             const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-            for (int pb = 0; pb < 4; ++pb) {
-              if (db * 4 + pb == 15) t15 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], t15, 0, 0, 0);
-              else o[db * 4 + pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], o[db * 4 + pb], 0, 0, 0);
+            for (int pb = 0; pb < kPB; ++pb) {
+              if (kSplitTile && db * kPB + pb == 15) t15 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], t15, 0, 0, 0);
+              else o[db * kPB + pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], o[db * kPB + pb], 0, 0, 0);
             }
           }
         }
+        if constexpr (kSplitTile) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) o15[i] += t15[i];
+          for (int i = 0; i < 16; ++i) o15[i] += t15[i];
+        }
       };
 
       // bf16: one barrier per tile, after the weights are written: it
@@ -410,48 +424,50 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       // tile T+1 and ends PV(T).
       for (int64_t T = p0; T < p1; ++T) {
         const uint32_t tb = tile_base(T);
-        // ---- S^T = K Q^T for this wave's 32 pairs: lane holds pair my_pair, tokens 8(i/4)+4*half+i%4.
-        // K-step k reads logical chunk 2k + half of row lane%32: chunk group k/4
-        // adds 1 KB, so four per-lane bases (by k%4) plus immediates suffice.
-        // fp8: the 4 RoPE k-steps (32..35) run first into their own sum, since
-        // only the latent part of a key is scaled (z = s_t <q_lat, code> + <q_R, k_R>).
-        f32x16 sacc = {};
-        float s_rope[16];
-        {
-          // kKAhead K fragments in flight ahead of the MFMA chain (the LDS is
-          // shared by the four waves, whose reads queue behind each other)
-          bf16x8 kf[kKAhead];
+        if (qk_wave) {
+          // ---- S^T = K Q^T for this wave's 32 pairs: lane holds pair my_pair, tokens 8(i/4)+4*half+i%4.
+          // K-step k reads logical chunk 2k + half of row lane%32: chunk group k/4
+          // adds 1 KB, so four per-lane bases (by k%4) plus immediates suffice.
+          // fp8: the 4 RoPE k-steps (32..35) run first into their own sum, since
+          // only the latent part of a key is scaled (z = s_t <q_lat, code> + <q_R, k_R>).
+          f32x16 sacc = {};
+          float s_rope[16];
+          {
+            // kKAhead K fragments in flight ahead of the MFMA chain (the LDS is
+            // shared by the four waves, whose reads queue behind each other)
+            bf16x8 kf[kKAhead];
 #pragma unroll
-          for (int k = 0; k < kKAhead; ++k) {
-            const int kk = kFp8 ? (k + 32) % kQSteps : k;   // (kk % 4 == k % 4)
-            kf[k] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (kk / 4));
-          }
+            for (int k = 0; k < kKAhead; ++k) {
+              const int kk = kFp8 ? (k + 32) % kQSteps : k;   // (kk % 4 == k % 4)
+              kf[k] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (kk / 4));
+            }
 #pragma unroll
-          for (int k = 0; k < kQSteps; ++k) {
-            const int kk = kFp8 ? (k + 32) % kQSteps : k;
-            const int kn = kFp8 ? (k + kKAhead + 32) % kQSteps : k + kKAhead;
-            const bf16x8 cur = kf[k % kKAhead];
-            if (k + kKAhead < kQSteps)
-              kf[k % kKAhead] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (kn / 4));
-            sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, q[kk], sacc, 0, 0, 0);
-            if constexpr (kFp8) {
-              if (k == 3) {
+            for (int k = 0; k < kQSteps; ++k) {
+              const int kk = kFp8 ? (k + 32) % kQSteps : k;
+              const int kn = kFp8 ? (k + kKAhead + 32) % kQSteps : k + kKAhead;
+              const bf16x8 cur = kf[k % kKAhead];
+              if (k + kKAhead < kQSteps)
+                kf[k % kKAhead] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (kn / 4));
+              sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, q[kk], sacc, 0, 0, 0);
+              if constexpr (kFp8) {
+                if (k == 3) {
 #pragma unroll
-                for (int i = 0; i < 16; ++i) s_rope[i] = sacc[i];
-                sacc = f32x16{};
+                  for (int i = 0; i < 16; ++i) s_rope[i] = sacc[i];
+                  sacc = f32x16{};
+                }
               }
             }
-          }
-          // issue order: kKAhead reads, then (MFMA, read) pairs, then the last kKAhead MFMAs
-          __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
+            // issue order: kKAhead reads, then (MFMA, read) pairs, then the last kKAhead MFMAs
+            __builtin_amdgcn_sched_group_barrier(0x100, kKAhead, 0);
 #pragma unroll
-          for (int k = 0; k < kQSteps - kKAhead; ++k) {
-            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            for (int k = 0; k < kQSteps - kKAhead; ++k) {
+              __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+              __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+            }
+            __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
           }
-          __builtin_amdgcn_sched_group_barrier(0x008, kKAhead, 0);
+          softmax(sacc, s_rope, T);
         }
-        softmax(sacc, s_rope, T);
         if (T + 1 < p1) wait_tile(T_issue - 2 - T);   // (staged) tile T+1 has landed (later ones may be in flight)
         lds_barrier();
         if (T_issue < p1) load_tile(T_issue++);
@@ -486,8 +502,8 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
       l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
-    if (lane < 32) {
-      if (!whole) {
+    if (lane < 32 && qk_wave) {
+      if (!whole && !pad) {
         const int my_row = my_j * a.n_heads + my_s;
         a.ws_stats[(slot_row0 + my_row) * 2] = m_ref;
         a.ws_stats[(slot_row0 + my_row) * 2 + 1] = l_tot;
@@ -496,9 +512,10 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       s_m[my_pair] = m_ref;
     }
 #pragma unroll
-    for (int hp = 0; hp < 2; ++hp) {               // pairs 64*hp .. 64*hp+63
+    for (int hp = 0; hp < (kPB + 1) / 2; ++hp) {   // pairs 64*hp .. 64*hp+63
+      constexpr int kHalfPairs = kPB == 1 ? 32 : 64;
 #pragma unroll
-      for (int pbl = 0; pbl < 2; ++pbl) {
+      for (int pbl = 0; pbl < kHalfPairs / 32; ++pbl) {
         const int pb = 2 * hp + pbl;
         lds_u8* xrow = lds + (32 * pbl + (lane & 31)) * kXRow + (128 * wave + 4 * half) * 4;
 #pragma unroll
@@ -506,19 +523,20 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
             f32x4 v;
-            if (db * 4 + pb == 15) v = f32x4{o15[4 * qq], o15[4 * qq + 1], o15[4 * qq + 2], o15[4 * qq + 3]};
-            else v = f32x4{o[db * 4 + pb][4 * qq], o[db * 4 + pb][4 * qq + 1], o[db * 4 + pb][4 * qq + 2],
-                           o[db * 4 + pb][4 * qq + 3]};
+            if (kSplitTile && db * kPB + pb == 15) v = f32x4{o15[4 * qq], o15[4 * qq + 1], o15[4 * qq + 2], o15[4 * qq + 3]};
+            else v = f32x4{o[db * kPB + pb][4 * qq], o[db * kPB + pb][4 * qq + 1], o[db * kPB + pb][4 * qq + 2],
+                           o[db * kPB + pb][4 * qq + 3]};
             *(lds_f32x4*)(xrow + (32 * db + 8 * qq) * 4) = v;
           }
       }
-      lds_barrier();                              // the 64 rows (and s_l, s_m) are in LDS
+      lds_barrier();                              // the rows (and s_l, s_m) are in LDS
       // thread t: 16-byte chunk t % 128 of rows t / 128 + 2k
       const int c = tid & 127;
 #pragma unroll 4
-      for (int k = 0; k < 32; ++k) {
+      for (int k = 0; k < kHalfPairs / 2; ++k) {
         const int r = (tid >> 7) + 2 * k;
         const int pair = 64 * hp + r;
+        if (kPB != 4 && pair / hpw >= a.q_per_seq) continue;   // padding
         const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
         const f32x4 v = *(const lds_f32x4*)(lds + r * kXRow + c * 16);
         if (!whole) {
@@ -534,7 +552,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       }
       lds_barrier();                              // the staging rows are free again
     }
-    if (whole && tid < kPairs) {
+    if (whole && tid < 32 * kPB && (kPB == 4 || tid / hpw < a.q_per_seq)) {
       const int pair = tid;
       const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
       const float l = s_l[pair], m = s_m[pair];
@@ -552,13 +570,36 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
 
 }  // namespace
 
+namespace {
+
+// Pair blocks per work-group (kPB: 32 (query row, head) pairs each) and heads
+// per work-group (hpw; grid.y = H / hpw head groups) for a shape: the fewest
+// blocks that hold min(H, 128 / q_per_seq) heads x q_per_seq rows, kPB = 4
+// only without padding.
+bool decode576_shape(const mla_dims& d, int32_t q_per_seq, int* kpb, int* hpw) {
+  if (q_per_seq <= 0) return false;
+  for (int pb : {4, 2, 1}) {
+    const int pairs = 32 * pb;
+    if (pairs % q_per_seq != 0) continue;
+    const int h = d.n_heads < pairs / q_per_seq ? d.n_heads : pairs / q_per_seq;
+    if (d.n_heads % h != 0) continue;
+    if (pb == 4 && h * q_per_seq != pairs) continue;      // kPB = 4 is built without padding
+    if (pb > 1 && h * q_per_seq <= pairs / 2) continue;   // fewer blocks hold them
+    *kpb = pb;
+    *hpw = h;
+    return true;
+  }
+  return false;
+}
+
+}  // namespace
+
 bool decode576_supported(const mla_dims& d, int32_t q_per_seq) {
   if (d.d_c != 512 || d.d_rope != 64 || d.act_dtype != MLA_BF16) return false;
   if (d.cache_dtype != MLA_BF16 && d.cache_dtype != MLA_FP8_E4M3) return false;
   if (d.block_size % kTile != 0) return false;
-  if (q_per_seq <= 0 || kPairs % q_per_seq != 0) return false;
-  const int hpw = kPairs / q_per_seq;
-  return d.n_heads % hpw == 0;
+  int kpb, hpw;
+  return decode576_shape(d, q_per_seq, &kpb, &hpw);
 }
 
 int64_t decode576_default_units(int32_t n_seq, int32_t q_per_seq, int cu_count) {
@@ -584,13 +625,16 @@ mla_status launch_decode576(const mla_dims& d, const DecodePlan& plan, int32_t n
   a.q_per_seq = q_per_seq;
   a.n_heads = d.n_heads;
   a.units = plan.n_splits;
-  a.heads_per_wg = kPairs / q_per_seq;
+  int kpb = 0, hpw = 0;
+  if (!decode576_shape(d, q_per_seq, &kpb, &hpw)) return MLA_ERR_UNSUPPORTED;
+  a.heads_per_wg = hpw;
   a.scale_log2 = d.softmax_scale * 1.4426950408889634f;
-  dim3 grid(plan.n_splits, d.n_heads / a.heads_per_wg);
-  if (d.cache_dtype == MLA_FP8_E4M3)
-    hipLaunchKernelGGL(decode576_kernel<true>, grid, dim3(256), 0, st, a, block_table, seqlens);
-  else
-    hipLaunchKernelGGL(decode576_kernel<false>, grid, dim3(256), 0, st, a, block_table, seqlens);
+  dim3 grid(plan.n_splits, d.n_heads / hpw);
+  const bool f8 = d.cache_dtype == MLA_FP8_E4M3;
+  void (*kern)(Args, const int32_t*, const int32_t*) =
+      f8 ? (kpb == 4 ? decode576_kernel<true, 4> : kpb == 2 ? decode576_kernel<true, 2> : decode576_kernel<true, 1>)
+         : (kpb == 4 ? decode576_kernel<false, 4> : kpb == 2 ? decode576_kernel<false, 2> : decode576_kernel<false, 1>);
+  hipLaunchKernelGGL(kern, grid, dim3(256), 0, st, a, block_table, seqlens);
   return launch_status();
 }
 

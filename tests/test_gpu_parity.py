@@ -137,6 +137,41 @@ def test_chain_vs_non_absorbed_oracle(name, cuda_device):
 
 
 @pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("heads,sq", [(16, 1), (16, 2), (32, 1), (64, 1), (64, 2), (96, 1)])
+def test_decode_head_counts(heads, sq, cache, cuda_device):
+    """The tuned decode with fewer (query row, head) pairs than a full
+    128-pair work-group: one, two or three head groups of 32 or 64 pairs,
+    with padding pairs (16 heads x 1 row in 32 pairs) that must store nothing."""
+    import mla_latent_kv_23_amd as M
+    w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=3, n_heads=heads, q_per_seq=sq, cache_dtype=cache)
+    lens = [300, 33, 1000]
+    inp = S.make_inputs(w, 777 + heads + sq, seqlens=torch.tensor(lens, dtype=torch.int32))
+    U.say(f"[heads] {cache} H={heads} sq={sq}")
+    d = U.dims_of(w)
+    pos = S.query_positions(inp["seqlens"], sq).numpy()
+    q_abs = O.absorb_q(inp["q_nope"].double().numpy(), inp["q_rope"].double().numpy(),
+                       pos[:, :, None] * np.ones((1, 1, w.n_heads), np.int64), inp["w_uk"].double().numpy(),
+                       w.rope_base)
+    q_dev = U.to_act(q_abs, "bf16", cuda_device)
+    q_r = q_dev.double().cpu().numpy()
+    pool = U.gpu_pool(w, inp, cuda_device, poison=0xFF)
+    bt, L = inp["block_table"].to(cuda_device), inp["seqlens"].to(cuda_device)
+    cu = inp["cu_seqlens"].numpy()
+    for ns in [0, 1, 7]:
+        o_lat = torch.full((3, sq, heads, w.d_c), float("nan"), dtype=torch.bfloat16, device=cuda_device)
+        lse = torch.full((3, sq, heads), float("nan"), dtype=torch.float32, device=cuda_device)
+        o_lat, lse, ws = M.decode(d, q_dev, pool, bt, L, num_splits=ns, o_latent=o_lat, lse=lse)
+        M.combine(d, L, bt.shape[1], ws, o_lat, lse, num_splits=ns)
+        for b, Lb in enumerate(lens):
+            c, kr = O.cached_token_values(inp["c_kv"][cu[b]:cu[b] + Lb].double().numpy(),
+                                          inp["k_rope"][cu[b]:cu[b] + Lb].double().numpy(), np.arange(Lb), cache,
+                                          w.rope_base)
+            want_o, want_lse = O.decode_absorbed_form(q_r[b], c, kr, pos[b], w.softmax_scale)
+            U.assert_close(o_lat[b], want_o, "bf16", f"o_lat L={Lb} splits={ns}")
+            U.assert_close(lse[b], want_lse, "bf16", f"lse L={Lb} splits={ns}")
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
 @pytest.mark.parametrize("lens", [[31, 32, 33], [63, 64, 65], [1, 2, 127], [96, 4097]])
 def test_decode_tile_edges(lens, cache, cuda_device):
     """Lengths around the 32-token tile and 64-token block edges, single-token
