@@ -269,8 +269,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     };
     // fp8: staged tile T -> bf16 buffer T % 2
     auto expand = [&](int64_t T) {
-      expand_tile_fp8(lds + kOffF + (int)(T % kF8Slots) * kF8StageBytes, lds + (int)(T & 1) * kTileBytes, wave,
-                      lane);
+      expand_tile_fp8(lds + kOffF + (int)(T % kF8Slots) * kF8StageBytes, lds + (int)(T & 1) * kTileBytes, wave);
     };
     // LDS address of tile T's bf16 image
     auto tile_base = [&](int64_t T) -> uint32_t {

@@ -176,12 +176,23 @@ __device__ __forceinline__ void issue_tile_fp8(const uint8_t* blk, int slot, int
 
 // Expand a staged fp8 tile into the bf16 tile layout at `dst`: latent dim d
 // of row r becomes bf16(code) (every E4M3FN value is exactly a bf16), k_R is
-// copied; the per-token scale is applied to the scores and weights instead.
+// copied; the per-token scale is applied to the scores and weights instead
+// (`v_cvt_scalef32_pk_bf16_fp8` with scale 1 decodes all 256 codes exactly).
 // Thread (wave w, lane l) converts the 64 codes its wave's loads brought to
 // lane l (row 8w + l/8, dims 128i + 16(l % 8) .. +15 for i = 0..3) and copies
 // k_R chunk l % 8 of the same row.
-__device__ __forceinline__ void expand_tile_fp8(const lds_u8* stage, lds_u8* dst, int wave, int lane) {
-  const int r = 8 * wave + (lane >> 3), m = lane & 7;
+__device__ __forceinline__ void expand_tile_fp8(const lds_u8* stage, lds_u8* dst, int wave) {
+  // the lane index and the offsets below are recomputed at every call (a few
+  // VALU ops): kept across the tile loop they would be spilled, and a scratch
+  // reload waits for every load in flight, the tile loads included
+  int lane;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
+  const int r = 8 * wave + (lane >> 3), m = lane & 7, sw = swz(r & 7);
+  // logical chunk 16i + 2m + e of row r sits at tile_off(r, 16i + 2m + e) =
+  // base_e + 2048 i (block 2i + m/4 of the row group, position (2(m % 4) + e) ^ swz)
+  const uint32_t row_base = ((r >> 3) * 9 + (m >> 2)) * 1024 + (r & 7) * 128;
+  const uint32_t base0 = row_base + 16 * ((2 * (m & 3)) ^ sw);
+  const uint32_t base1 = row_base + 16 * ((2 * (m & 3) + 1) ^ sw);
   const u32x4 kr = *(const lds_u32x4*)(stage + kF8OffRope + 1024 * wave + 16 * lane);
   u32x4 codes[4];
 #pragma unroll
@@ -191,16 +202,15 @@ __device__ __forceinline__ void expand_tile_fp8(const lds_u8* stage, lds_u8* dst
     uint32_t w[8];
 #pragma unroll
     for (int d = 0; d < 4; ++d) {
-      const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(codes[i][d], false);   // codes 4d, 4d+1
-      const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(codes[i][d], true);    // codes 4d+2, 4d+3
-      const bf16x2 b0 = __builtin_convertvector(lo, bf16x2);                   // exact
-      const bf16x2 b1 = __builtin_convertvector(hi, bf16x2);
+      // codes 4d, 4d+1 and 4d+2, 4d+3 straight to bf16 pairs (scale 1: exact)
+      const bf16x2 b0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i][d], 1.0f, false);
+      const bf16x2 b1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[i][d], 1.0f, true);
       w[2 * d] = *(const uint32_t*)&b0;
       w[2 * d + 1] = *(const uint32_t*)&b1;
     }
     // dims 128i + 16m .. +15 are logical chunks 16i + 2m and 16i + 2m + 1
-    *(lds_u32x4*)(dst + tile_off(r, 16 * i + 2 * m)) = u32x4{w[0], w[1], w[2], w[3]};
-    *(lds_u32x4*)(dst + tile_off(r, 16 * i + 2 * m + 1)) = u32x4{w[4], w[5], w[6], w[7]};
+    *(lds_u32x4*)(dst + base0 + 2048 * i) = u32x4{w[0], w[1], w[2], w[3]};
+    *(lds_u32x4*)(dst + base1 + 2048 * i) = u32x4{w[4], w[5], w[6], w[7]};
   }
   *(lds_u32x4*)(dst + tile_off(r, 64 + m)) = kr;
 }
