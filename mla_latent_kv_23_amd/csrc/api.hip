@@ -66,7 +66,7 @@ DecodePlan make_plan(const mla_dims& d, int32_t n_seq, int32_t q_per_seq, int32_
   if (tuned_decode_applies(d, q_per_seq)) {
     p.kind = 1;
     const int64_t tiles_bound = static_cast<int64_t>(n_seq) * ((max_len + kDecodeTile - 1) / kDecodeTile);
-    int64_t units = num_splits > 0 ? num_splits : decode576_default_units(n_seq, q_per_seq, device_cu_count());
+    int64_t units = num_splits > 0 ? num_splits : decode576_default_units(d, q_per_seq, device_cu_count());
     if (units > tiles_bound) units = tiles_bound;
     if (units < 1) units = 1;
     p.n_splits = static_cast<int32_t>(units);

@@ -8,7 +8,7 @@ namespace mla {
 constexpr int kDecodeTile = 32;   // key tokens per pipeline stage of the tuned decode kernel
 
 bool decode576_supported(const mla_dims& d, int32_t q_per_seq);
-int64_t decode576_default_units(int32_t n_seq, int32_t q_per_seq, int cu_count);
+int64_t decode576_default_units(const mla_dims& d, int32_t q_per_seq, int cu_count);
 mla_status launch_decode576(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
                             const void* q_abs, const void* pool, const int32_t* block_table, int32_t max_blocks,
                             const int32_t* seqlens, void* ws, void* o_lat, float* lse, hipStream_t st);

@@ -601,10 +601,13 @@ bool decode576_supported(const mla_dims& d, int32_t q_per_seq) {
   return decode576_shape(d, q_per_seq, &kpb, &hpw);
 }
 
-int64_t decode576_default_units(int32_t n_seq, int32_t q_per_seq, int cu_count) {
-  (void)n_seq;
-  (void)q_per_seq;
-  return cu_count;   // one resident work-group per CU
+int64_t decode576_default_units(const mla_dims& d, int32_t q_per_seq, int cu_count) {
+  // one resident work-group per CU: the head groups of a unit (grid.y) run
+  // side by side on one XCD and read its tiles through the same L2
+  int kpb = 0, hpw = 0;
+  if (!decode576_shape(d, q_per_seq, &kpb, &hpw)) return cu_count;
+  const int groups = d.n_heads / hpw;
+  return cu_count / groups > 0 ? cu_count / groups : 1;
 }
 
 mla_status launch_decode576(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
