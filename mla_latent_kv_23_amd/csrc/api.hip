@@ -96,7 +96,8 @@ DecodePlan make_plan(const mla_dims& d, int32_t n_seq, int32_t q_per_seq, int32_
     p.needs_combine = p.n_splits > 1 ? 1 : 0;
   }
   const int64_t rows_per_slot = static_cast<int64_t>(q_per_seq) * d.n_heads;
-  p.ws_stats_offset_floats = static_cast<int64_t>(p.n_slots) * rows_per_slot * d.d_c;
+  // partials: bf16 for the tuned decode's stream layout, fp32 otherwise
+  p.ws_stats_offset_floats = static_cast<int64_t>(p.n_slots) * rows_per_slot * d.d_c / (p.layout.mode == 1 ? 2 : 1);
   p.ws_bytes =
       p.n_slots ? static_cast<size_t>(p.ws_stats_offset_floats + 2LL * p.n_slots * rows_per_slot) * sizeof(float) : 0;
   return p;

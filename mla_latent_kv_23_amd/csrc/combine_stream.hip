@@ -1,4 +1,4 @@
-// Log-sum-exp merge of the raw partials left by the tuned decode kernel (the
+// Log-sum-exp merge of the raw bf16 partials left by the tuned decode kernel (the
 // key range of a sequence split over several work-groups): for each query
 // row, M = max_k m_k, L = sum_k 2^(m_k - M) l_k, o = sum_k 2^(m_k - M) O_k / L,
 // lse = (M + log2 L) ln 2.  A piece that saw no key (l_k = 0) has weight 0.
@@ -19,7 +19,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-__global__ void __launch_bounds__(256) combine_stream_kernel(const float* __restrict__ ws_o,
+__global__ void __launch_bounds__(256) combine_stream_kernel(const uint16_t* __restrict__ ws_o,
                                                              const float* __restrict__ ws_stats,
                                                              const int32_t* __restrict__ seqlens, int n_seq,
                                                              int rows_per_seq, SplitLayout lay,
@@ -67,15 +67,15 @@ __global__ void __launch_bounds__(256) combine_stream_kernel(const float* __rest
     const int64_t n_here = min(count - k64, (int64_t)64);
     for (int k0 = 0; k0 < n_here; k0 += kGroup) {
       f32x2 st[kGroup];
-      f32x4 v[kGroup][2];
+      u32x2 raw[kGroup][2];   // 4 bf16 each
 #pragma unroll
       for (int j = 0; j < kGroup; ++j) {
         if (k0 + j < n_here) {
           const int64_t row = (wf + k64 + k0 + j + b) * rows_per_seq + r;
           st[j] = *(const f32x2*)(ws_stats + row * 2);
-          const f32x4* src = (const f32x4*)(ws_o + row * kDc) + lane;
-          v[j][0] = src[0];
-          v[j][1] = src[64];
+          const u32x2* src = (const u32x2*)(ws_o + row * kDc) + lane;
+          raw[j][0] = src[0];
+          raw[j][1] = src[64];
         }
       }
 #pragma unroll
@@ -89,7 +89,11 @@ __global__ void __launch_bounds__(256) combine_stream_kernel(const float* __rest
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) acc[h][e] = fmaf(acc[h][e], keep, wgt * v[j][h][e]);
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w2 = raw[j][h][e >> 1];
+            const float x = __uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16));
+            acc[h][e] = fmaf(acc[h][e], keep, wgt * x);
+          }
         m = mn;
       }
     }
@@ -112,8 +116,8 @@ __global__ void __launch_bounds__(256) combine_stream_kernel(const float* __rest
 mla_status launch_combine_stream(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
                                  const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st) {
   const int rows = q_per_seq * d.n_heads;
-  const float* ws_o = static_cast<const float*>(ws);
-  const float* ws_stats = ws_o + plan.ws_stats_offset_floats;
+  const uint16_t* ws_o = static_cast<const uint16_t*>(ws);
+  const float* ws_stats = static_cast<const float*>(ws) + plan.ws_stats_offset_floats;
   dim3 grid(n_seq, (rows + kRowsPerBlock - 1) / kRowsPerBlock);
   hipLaunchKernelGGL(combine_stream_kernel, grid, dim3(256), 0, st, ws_o, ws_stats, seqlens, n_seq, rows,
                      plan.layout, static_cast<uint16_t*>(o_lat), lse);

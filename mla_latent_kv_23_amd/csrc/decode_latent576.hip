@@ -75,7 +75,7 @@ struct Args {
   const uint8_t* pool;          // paged cache, block_bytes per block
   uint16_t* o_final;            // [n_seq][q_per_seq][H][512] bf16
   float* lse_final;             // [n_seq][q_per_seq][H]
-  float* ws_o;                  // partials [slots][q_per_seq*H][512], raw (relative to 2^m)
+  uint16_t* ws_o;               // partials [slots][q_per_seq*H][512] bf16, raw (relative to 2^m)
   float* ws_stats;              // partials [slots][q_per_seq*H][2] = (m in log2 units, l)
   int64_t block_bytes;
   int32_t max_blocks, block_size, n_seq, q_per_seq, n_heads, units, heads_per_wg;
@@ -539,7 +539,10 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
         const f32x4 v = *(const lds_f32x4*)(lds + r * kXRow + c * 16);
         if (!whole) {
-          *(f32x4*)(a.ws_o + (slot_row0 + row_in_seq) * kDc + 4 * c) = v;
+          u32x2 pk2;
+          pk2[0] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+          pk2[1] = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+          *(u32x2*)(a.ws_o + (slot_row0 + row_in_seq) * kDc + 4 * c) = pk2;
         } else {
           const float l = s_l[pair];
           const float inv = l > 0.f ? 1.0f / l : 0.f;
@@ -618,7 +621,7 @@ mla_status launch_decode576(const mla_dims& d, const DecodePlan& plan, int32_t n
   a.pool = static_cast<const uint8_t*>(pool);
   a.o_final = static_cast<uint16_t*>(o_lat);
   a.lse_final = lse;
-  a.ws_o = static_cast<float*>(ws);
+  a.ws_o = static_cast<uint16_t*>(ws);
   a.ws_stats = static_cast<float*>(ws) + plan.ws_stats_offset_floats;
   a.block_bytes = static_cast<int64_t>(mla_cache_block_bytes(&d));
   a.max_blocks = max_blocks;

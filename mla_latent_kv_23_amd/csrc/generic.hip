@@ -223,43 +223,30 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
 // ----------------------------------------------------------------------------
 template <typename T>
 __global__ void __launch_bounds__(256) combine_kernel(
-    const float* __restrict__ ws_o, const float* __restrict__ ws_stats, const int32_t* __restrict__ seqlens,
-    int n_seq, int q_per_seq, int H, int d_c, SplitLayout lay, T* __restrict__ o_lat, float* __restrict__ lse) {
+    const float* __restrict__ ws_o, const float* __restrict__ ws_stats, int n_splits, int q_per_seq, int H, int d_c,
+    T* __restrict__ o_lat, float* __restrict__ lse) {
+  // per-sequence splits (the generic decode's layout): slots b * n_splits + k,
+  // normalised partials, stats[0] = lse_k; a split that saw no key has lse_k = -inf
   __shared__ float w_sh[kMaxCombineSlots];
   __shared__ float scale_sh, lse_sh;
   const int row = blockIdx.x;
   const int s = row % H, j = (row / H) % q_per_seq, b = row / (H * q_per_seq);
-  const SlotRange r = slot_range(lay, seqlens, n_seq, b);
-  if (r.count == 0) return;                  // the decode kernel wrote this row itself
-  const int first = r.first, count = min(r.count, kMaxCombineSlots);
+  const int64_t first = static_cast<int64_t>(b) * n_splits;
+  const int count = min(n_splits, kMaxCombineSlots);
   const int64_t per_slot = static_cast<int64_t>(q_per_seq) * H;
   const int64_t rr = j * H + s;
   if (threadIdx.x == 0) {
     float m = -INFINITY;
-    for (int k = 0; k < count; ++k) {
-      if (!slot_used(lay, r, k)) continue;
-      const float* st = ws_stats + ((first + k) * per_slot + rr) * 2;
-      if (lay.mode == 0 || st[1] > 0.f) m = fmaxf(m, st[0]);
-    }
+    for (int k = 0; k < count; ++k) m = fmaxf(m, ws_stats[((first + k) * per_slot + rr) * 2]);
     const float msafe = (m == -INFINITY) ? 0.f : m;
     float tot = 0.f;
     for (int k = 0; k < count; ++k) {
-      float w = 0.f;
-      if (slot_used(lay, r, k)) {
-        const float* st = ws_stats + ((first + k) * per_slot + rr) * 2;
-        if (lay.mode == 0) {
-          w = expf(st[0] - msafe);
-          tot += w;
-        } else if (st[1] > 0.f) {
-          w = exp2f(st[0] - msafe);
-          tot += w * st[1];
-        }
-      }
+      const float w = expf(ws_stats[((first + k) * per_slot + rr) * 2] - msafe);   // 0 for an empty split
+      tot += w;
       w_sh[k] = w;
     }
     scale_sh = tot > 0.f ? 1.0f / tot : 0.f;
-    if (lay.mode == 0) lse_sh = (tot > 0.f) ? msafe + logf(tot) : -INFINITY;
-    else lse_sh = (tot > 0.f) ? (msafe + log2f(tot)) * 0.69314718055994530942f : -INFINITY;
+    lse_sh = (tot > 0.f) ? msafe + logf(tot) : -INFINITY;
   }
   __syncthreads();
   const float inv = scale_sh;
@@ -366,17 +353,17 @@ mla_status launch_decode_generic(const mla_dims& d, const DecodePlan& plan, int3
 
 mla_status launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
                           const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st) {
-  if (plan.layout.mode == 1 && d.act_dtype == MLA_BF16 && d.d_c == 512)
+  if (plan.layout.mode == 1)   // only the tuned decode (bf16, d_c = 512) leaves this layout
     return launch_combine_stream(d, plan, n_seq, q_per_seq, seqlens, ws, o_lat, lse, st);
   const float* ws_o = static_cast<const float*>(ws);
   const float* ws_stats = ws_o + plan.ws_stats_offset_floats;
   dim3 grid(n_seq * q_per_seq * d.n_heads);
   if (d.act_dtype == MLA_F32)
-    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, ws_o, ws_stats, seqlens, n_seq, q_per_seq,
-                       d.n_heads, d.d_c, plan.layout, (float*)o_lat, lse);
+    hipLaunchKernelGGL(combine_kernel<float>, grid, dim3(256), 0, st, ws_o, ws_stats, plan.n_splits, q_per_seq,
+                       d.n_heads, d.d_c, (float*)o_lat, lse);
   else
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, st, ws_o, ws_stats, seqlens, n_seq,
-                       q_per_seq, d.n_heads, d.d_c, plan.layout, (uint16_t*)o_lat, lse);
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, grid, dim3(256), 0, st, ws_o, ws_stats, plan.n_splits, q_per_seq,
+                       d.n_heads, d.d_c, (uint16_t*)o_lat, lse);
   return launch_status();
 }
 

@@ -12,11 +12,14 @@ namespace mla {
 
 constexpr int kMaxCombineSlots = 1024;   // partial results merged per (sequence, row, head)
 
-// Workspace: partial outputs o[slot][q_per_seq * H][d_c] (fp32), then per-row
+// Workspace: partial outputs o[slot][q_per_seq * H][d_c], then per-row
 // statistics stats[slot][q_per_seq * H][2] (fp32).
-//   kPerSequence partials are normalised: o = sum p v / sum p, stats[0] = lse.
-//   kStreamTiles partials are raw: o = sum 2^(z - m) v, stats = (m, sum 2^(z - m)),
-//   with z the scaled score in log2 units.
+//   kPerSequence partials are fp32 and normalised: o = sum p v / sum p,
+//   stats[0] = lse.
+//   kStreamTiles partials are bf16 and raw: o = sum 2^(z - m) v, stats =
+//   (m, sum 2^(z - m)), with z the scaled score in log2 units (the statistics
+//   carry the scale, so one more rounding of o only adds 2^-9 relative noise,
+//   averaged over the pieces by the merge).
 // Where the partial results of sequence b live in the workspace.
 //   kPerSequence: n_splits slots per sequence, slots b*n_splits .. +n_splits-1,
 //                 split k covers keys [k*ceil(L/n), (k+1)*ceil(L/n)).
@@ -51,52 +54,6 @@ __host__ __device__ __forceinline__ int64_t unit_of_tile(int64_t T, int64_t N, i
   return ((T + 1) * G - 1) / N;
 }
 
-// Slot range of sequence b; for kStreamTiles `count` spans units first..last.
-struct SlotRange {
-  int first, count;        // slots first .. first+count-1 (count 0: no partials)
-  int64_t unit0, n_tiles;  // kStreamTiles: unit of slot `first`, total tiles
-};
-
-// Whether slot first+k of a range holds a partial (kStreamTiles units with no
-// tile at all write nothing).
-__device__ __forceinline__ bool slot_used(const SplitLayout& lay, const SlotRange& r, int k) {
-  if (lay.mode == 0) return true;
-  const int64_t w = r.unit0 + k;
-  return unit_first_tile(w, r.n_tiles, lay.n_splits) < unit_first_tile(w + 1, r.n_tiles, lay.n_splits);
-}
-
-__device__ __forceinline__ SlotRange slot_range(const SplitLayout& lay, const int32_t* seqlens, int n_seq, int b) {
-  SlotRange r;
-  if (lay.mode == 0) {
-    r.first = b * lay.n_splits;
-    r.count = lay.n_splits;
-    r.unit0 = 0;
-    r.n_tiles = 0;
-    return r;
-  }
-  int64_t start = 0, total = 0, nb = 0;
-  for (int i = 0; i < n_seq; ++i) {
-    const int32_t L = min(max(seqlens[i], 0), lay.max_len);
-    const int64_t nt = (static_cast<int64_t>(L) + lay.tile - 1) / lay.tile;
-    if (i < b) start += nt;
-    if (i == b) nb = nt;
-    total += nt;
-  }
-  if (nb == 0) {                 // nothing to merge for an empty sequence
-    r.first = 0;
-    r.count = 0;
-    r.unit0 = 0;
-    r.n_tiles = total;
-    return r;
-  }
-  const int64_t wf = unit_of_tile(start, total, lay.n_splits);
-  const int64_t wl = unit_of_tile(start + nb - 1, total, lay.n_splits);
-  r.first = static_cast<int>(wf + b);
-  r.count = (wf == wl) ? 0 : static_cast<int>(wl - wf + 1);
-  r.unit0 = wf;
-  r.n_tiles = total;
-  return r;
-}
 
 RopeFreqs make_rope_freqs(const mla_dims& d);
 mla_status launch_status();
