@@ -238,6 +238,26 @@ def decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scal
     return o, o_lat, lse
 
 
+def prefill_mha_form(q_nope, q_rope, c_kv, k_rope_raw, w_uk, w_uv, scale, base,
+                     heads: Optional[Sequence[int]] = None):
+    """Prefill of one sequence in the MHA form ([P1] 双重投影, training/prefill
+    column: every head attends with k = [c W_UK^T | k_R], v = c W_UV^T).
+
+    All T tokens are both queries and keys: token i sits at position i (R3 with
+    an empty history) and sees tokens 0..i.  q_nope [T, H, d_nope], q_rope
+    [T, H, d_R] and k_rope_raw [T, d_R] are unrotated; c_kv [T, d_c] is the
+    latent as produced (no cache rounding).  The rotated shared key enters the
+    attention rounded to bf16, as it is stored in a bf16 cache (R4).
+    Returns o [T, h, d_v] and lse [T, h] over the chosen heads.
+    """
+    T = np.asarray(c_kv).shape[0]
+    pos = np.arange(T)
+    kr = store_value(rope(k_rope_raw, pos, base), "bf16")
+    o, _, lse = decode_mha_form(q_nope, q_rope, np.asarray(c_kv, dtype=F64), kr, pos, w_uk, w_uv, scale, base,
+                                heads)
+    return o, lse
+
+
 def absorb_q(q_nope, q_rope, q_pos, w_uk, base):
     """Absorbed query [.., H, d_c + d_R] = [W_UK[s]^T q_nope | RoPE(q_R)] ([P1] 双重投影 right column)."""
     q_nope = np.asarray(q_nope, dtype=F64)

@@ -357,3 +357,75 @@ def test_generator_block_table_and_positions():
     for b in range(5):
         assert bool((t[b, :nb[b]] >= 0).all()) and bool((t[b, nb[b]:] == -1).all())
     assert torch.equal(inp["tok_pos"][inp["cu_seqlens"][1]:inp["cu_seqlens"][2]], torch.arange(int(L[1]), dtype=torch.int32))
+
+
+# ---------------------------------------------------------------- prefill (MHA form) pins
+
+def _prefill_problem(seed, T, H=3, d_c=16, d_nope=8, d_rope=4, d_v=6):
+    r = _rng(seed)
+    return dict(q_nope=r.standard_normal((T, H, d_nope)), q_rope=r.standard_normal((T, H, d_rope)),
+                c=r.standard_normal((T, d_c)), kr=r.standard_normal((T, d_rope)),
+                w_uk=r.standard_normal((H, d_nope, d_c)) / 4, w_uv=r.standard_normal((H, d_v, d_c)) / 4,
+                scale=1 / math.sqrt(d_nope + d_rope), base=10000.0)
+
+
+def test_prefill_single_token_returns_its_value():
+    P = _prefill_problem(70, T=1)
+    o, lse = O.prefill_mha_form(P["q_nope"], P["q_rope"], P["c"], P["kr"], P["w_uk"], P["w_uv"], P["scale"],
+                                P["base"])
+    for s in range(3):
+        assert np.allclose(o[0, s], P["w_uv"][s] @ P["c"][0], rtol=1e-13)
+    # one key: lse is that key's scaled score
+    z0 = [P["scale"] * np.dot(np.concatenate([P["q_nope"][0, s], O.rope(P["q_rope"][0:1, s], np.array([0]),
+                                                                          P["base"])[0]]),
+                              np.concatenate([P["w_uk"][s] @ P["c"][0],
+                                              O.store_value(O.rope(P["kr"][0:1], np.array([0]), P["base"]), "bf16")[0]]))
+          for s in range(3)]
+    assert np.allclose(lse[0], z0, rtol=1e-12)
+
+
+def test_prefill_matches_torch_causal_sdpa():
+    """Against torch's causal scaled-dot-product attention (float64, CPU) on the
+    explicitly decompressed per-head keys and values."""
+    P = _prefill_problem(71, T=37)
+    T = 37
+    o, lse = O.prefill_mha_form(P["q_nope"], P["q_rope"], P["c"], P["kr"], P["w_uk"], P["w_uv"], P["scale"],
+                                P["base"])
+    pos = np.arange(T)
+    qr = O.rope(P["q_rope"], pos[:, None], P["base"])
+    kr = O.store_value(O.rope(P["kr"], pos, P["base"]), "bf16")
+    for s in range(3):
+        q = torch.from_numpy(np.concatenate([P["q_nope"][:, s], qr[:, s]], axis=1))[None, None]
+        k = torch.from_numpy(np.concatenate([P["c"] @ P["w_uk"][s].T, kr], axis=1))[None, None]
+        v = torch.from_numpy(P["c"] @ P["w_uv"][s].T)[None, None]
+        want = torch.nn.functional.scaled_dot_product_attention(q, k, v, is_causal=True, scale=P["scale"])
+        assert np.allclose(o[:, s], want[0, 0].numpy(), rtol=1e-11, atol=1e-12)
+
+
+def test_prefill_rows_are_decodes_of_their_prefix():
+    """Row i of a prefill equals decoding the first i+1 tokens with one query
+    at position i (the decode oracle, pinned above, on a bf16-stored k_R)."""
+    P = _prefill_problem(72, T=19)
+    o, lse = O.prefill_mha_form(P["q_nope"], P["q_rope"], P["c"], P["kr"], P["w_uk"], P["w_uv"], P["scale"],
+                                P["base"])
+    for i in [0, 1, 7, 18]:
+        kr_c = O.store_value(O.rope(P["kr"][:i + 1], np.arange(i + 1), P["base"]), "bf16")
+        od, _, ld = O.decode_mha_form(P["q_nope"][i:i + 1], P["q_rope"][i:i + 1], P["c"][:i + 1], kr_c,
+                                      np.array([i]), P["w_uk"], P["w_uv"], P["scale"], P["base"])
+        assert np.allclose(o[i], od[0], rtol=1e-12, atol=1e-13)
+        assert np.allclose(lse[i], ld[0], rtol=1e-12)
+
+
+def test_prefill_is_causal():
+    """Changing tokens after row i leaves rows 0..i unchanged."""
+    P = _prefill_problem(73, T=16)
+    o1, _ = O.prefill_mha_form(P["q_nope"], P["q_rope"], P["c"], P["kr"], P["w_uk"], P["w_uv"], P["scale"],
+                               P["base"])
+    P2 = {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in P.items()}
+    P2["c"][9:] += 5.0
+    P2["kr"][9:] -= 3.0
+    P2["q_nope"][9:] *= 2.0
+    o2, _ = O.prefill_mha_form(P2["q_nope"], P2["q_rope"], P2["c"], P2["kr"], P2["w_uk"], P2["w_uv"], P2["scale"],
+                               P2["base"])
+    assert np.array_equal(o1[:9], o2[:9])
+    assert not np.allclose(o1[9:], o2[9:])
