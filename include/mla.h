@@ -200,6 +200,36 @@ mla_status mla_combine(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
 mla_status mla_up_proj(const mla_dims* dims, int32_t n_tok, const void* o_latent,
                        const void* w_uv, void* out, mla_stream_t stream);
 
+/*
+ * mla_prefill -- causal attention over whole prompts in the MHA form
+ * ("Transformer升级之路：21、MLA好在哪里？（下）", 双重投影, training/prefill
+ * column: each head gets its own key k = [c W_k^(s) | k_R] and value
+ * v = c W_v^(s); 总而言之: the shared RoPE key is concatenated; "DeepSeek-V3
+ * 解读", 为什么需要解耦 RoPE: q_R and k_R are rotated).  Per head s and token i
+ * of a sequence (position i, seeing tokens 0..i of the same sequence):
+ *   key_t   = [W_UK[s] c_t | RoPE(k_rope_t, t)],  value_t = W_UV[s] c_t
+ *   query_i = [q_nope[i,s] | RoPE(q_rope[i,s], i)]
+ *   z_t = softmax_scale <query_i, key_t>,  out[i,s] = sum_t softmax(z)_t value_t,
+ *   lse[i,s] = ln sum_t exp(z_t).
+ * The rotated keys and queries, the decompressed keys and values and the
+ * softmax weights are rounded to bf16 as MFMA operands (fp32 accumulation).
+ * Sequences are packed: cu_seqlens [n_seq + 1] (device int32, trusted: 0 =
+ * cu[0] <= cu[1] <= ... <= cu[n_seq] = total_tokens, every length <= max_seqlen,
+ * a host value); q_nope [T, H, d_nope], q_rope [T, H, d_rope] (unrotated),
+ * c_kv [T, d_c], k_rope [T, d_rope] (unrotated), w_uk [H, d_nope, d_c],
+ * w_uv [H, d_v, d_c], all bf16; out [T, H, d_v] (bf16) and lse [T, H] (float32)
+ * are written.  workspace: at least mla_prefill_workspace_bytes (the
+ * decompressed keys and values and the rotated parts live there), 16-byte
+ * aligned.  Supported: bf16, d_c 512, d_nope 128, d_rope 64, d_v 128 (else
+ * MLA_ERR_UNSUPPORTED).  T = 0 launches nothing.
+ */
+size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t total_tokens);
+mla_status mla_prefill(const mla_dims* dims, int32_t n_seq, const int32_t* cu_seqlens,
+                       int32_t total_tokens, int32_t max_seqlen, const void* q_nope,
+                       const void* q_rope, const void* c_kv, const void* k_rope,
+                       const void* w_uk, const void* w_uv, void* workspace,
+                       size_t workspace_bytes, void* out, float* lse, mla_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

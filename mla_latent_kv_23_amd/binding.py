@@ -62,6 +62,8 @@ SIGNATURES = {
     "mla_decode_needs_combine": (_I32, [_DP, _I32, _I32, _I32, _I32]),
     "mla_combine": (ctypes.c_int, [_DP, _I32, _I32, _P, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "mla_up_proj": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P]),
+    "mla_prefill_workspace_bytes": (_SZ, [_DP, _I32]),
+    "mla_prefill": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
 }
 
 
@@ -193,3 +195,31 @@ def up_proj(d: Dims, o_latent, w_uv, out=None, stream=None):
         ctypes.byref(d), n_tok, _ptr(o_latent, "o_latent", at), _ptr(w_uv, "w_uv", at), _ptr(out, "out", at),
         _stream(stream)))
     return out
+
+
+def prefill_workspace_bytes(d: Dims, total_tokens: int) -> int:
+    return load_library().mla_prefill_workspace_bytes(ctypes.byref(d), total_tokens)
+
+
+def prefill(d: Dims, q_nope, q_rope, c_kv, k_rope, cu_seqlens, max_seqlen: int, w_uk, w_uv, workspace=None,
+            out=None, lse=None, stream=None):
+    """Causal prefill of packed sequences in the MHA form.  q_nope [T, H, d_nope],
+    q_rope [T, H, d_rope], c_kv [T, d_c], k_rope [T, d_rope]; cu_seqlens [n_seq + 1]
+    int32 on the device.  Returns (out [T, H, d_v], lse [T, H], workspace)."""
+    at = act_torch_dtype(d)
+    T = q_nope.shape[0]
+    n_seq = cu_seqlens.shape[0] - 1
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((T, d.n_heads, d.d_v), dtype=at, device=dev)
+    if lse is None:
+        lse = torch.empty((T, d.n_heads), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(prefill_workspace_bytes(d, T), 1), dtype=torch.uint8, device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("mla_prefill", load_library().mla_prefill(
+        ctypes.byref(d), n_seq, _ptr(cu_seqlens, "cu_seqlens", torch.int32), T, max_seqlen,
+        _ptr(q_nope, "q_nope", at), _ptr(q_rope, "q_rope", at), _ptr(c_kv, "c_kv", at), _ptr(k_rope, "k_rope", at),
+        _ptr(w_uk, "w_uk", at), _ptr(w_uv, "w_uv", at), _ptr(workspace, "workspace"), ws_bytes,
+        _ptr(out, "out", at), _ptr(lse, "lse", torch.float32), _stream(stream)))
+    return out, lse, workspace

@@ -228,4 +228,32 @@ mla_status mla_up_proj(const mla_dims* d, int32_t n_tok, const void* o_latent, c
   return launch_up_proj_generic(*d, n_tok, o_latent, w_uv, out, st);
 }
 
+size_t mla_prefill_workspace_bytes(const mla_dims* d, int32_t total_tokens) {
+  if (dims_supported(d) != MLA_OK || !prefill_supported(*d) || total_tokens < 0) return 0;
+  return prefill_workspace_bytes(*d, total_tokens);
+}
+
+mla_status mla_prefill(const mla_dims* d, int32_t n_seq, const int32_t* cu_seqlens, int32_t total_tokens,
+                       int32_t max_seqlen, const void* q_nope, const void* q_rope, const void* c_kv,
+                       const void* k_rope, const void* w_uk, const void* w_uv, void* workspace,
+                       size_t workspace_bytes, void* out, float* lse, mla_stream_t stream) {
+  const mla_status s = dims_supported(d);
+  if (s != MLA_OK) return s;
+  if (!prefill_supported(*d)) return MLA_ERR_UNSUPPORTED;
+  if (n_seq <= 0 || total_tokens < 0 || max_seqlen < 0) return MLA_ERR_INVALID_ARG;
+  if (total_tokens == 0) return MLA_OK;
+  if (!cu_seqlens || !q_nope || !q_rope || !c_kv || !k_rope || !w_uk || !w_uv || !out || !lse)
+    return MLA_ERR_INVALID_ARG;
+  if (max_seqlen == 0 || max_seqlen > total_tokens) return MLA_ERR_INVALID_ARG;
+  // 32-bit index math inside the kernels: tokens x heads x 128 and the grid
+  if (static_cast<int64_t>(total_tokens) * d->n_heads * 128 > 2147483647LL) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(n_seq) * d->n_heads * ((max_seqlen + 127) / 128) > 2147483647LL) return MLA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < prefill_workspace_bytes(*d, total_tokens)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uk) ||
+      !aligned16(w_uv) || !aligned16(workspace) || !aligned16(out))
+    return MLA_ERR_INVALID_ARG;
+  return launch_prefill(*d, n_seq, cu_seqlens, total_tokens, max_seqlen, q_nope, q_rope, c_kv, k_rope, w_uk, w_uv,
+                        workspace, out, lse, static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

@@ -73,6 +73,12 @@ mla_status launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t n_s
                           const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st);
 mla_status launch_combine_stream(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
                                  const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st);
+bool prefill_supported(const mla_dims& d);
+size_t prefill_workspace_bytes(const mla_dims& d, int64_t total_tokens);
+mla_status launch_prefill(const mla_dims& d, int32_t n_seq, const int32_t* cu_seqlens, int32_t total_tokens,
+                          int32_t max_seqlen, const void* q_nope, const void* q_rope, const void* c_kv,
+                          const void* k_rope, const void* w_uk, const void* w_uv, void* ws, void* out, float* lse,
+                          hipStream_t st);
 mla_status launch_up_proj_generic(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv,
                                   void* out, hipStream_t st);
 

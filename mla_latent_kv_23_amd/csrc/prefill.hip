@@ -1,0 +1,459 @@
+// Prefill in the MHA form ("Transformer升级之路：21、MLA好在哪里？（下）",
+// 双重投影, training/prefill column): every head attends with its own key
+// [k_C | k_R], k_C = W_UK[s] c (d_nope = 128) and k_R the shared rotated key
+// (d_R = 64), and its own value v = W_UV[s] c (d_v = 128); the query is
+// [q_nope | RoPE(q_R)].  Sequences are packed (cu_seqlens); token i of a
+// sequence sits at position i and attends to tokens 0..i.
+//
+// Three launches:
+//  1. prefill_rope_kernel: q_R' [T, H, 64] and k_R' [T, 64] in bf16, by the
+//     RoPE rule of the absorb and append kernels (fp64 angle, fp32 cos/sin,
+//     fp64 rotation, one rounding); cos/sin once per (token, pair).
+//  2. prefill_decompress_kernel: k_C [T, H, 128] and v [T, H, 128] in bf16, a
+//     bf16 MFMA GEMM with fp32 accumulation: a 128-dim x 128-token tile of one
+//     head per work-group, the 512-long contraction in chunks of 64 through LDS.
+//  3. prefill_attn_kernel: causal flash attention per (sequence, head, block of
+//     128 queries), one wave per 32 queries:
+//     * key blocks of 64 rows [k_C | k_R | v] (640 B) are staged in LDS with
+//       direct-to-LDS loads, two stages, in 1 KB blocks of 8 rows x 8 chunks
+//       with the chunk XOR-swizzled by the row (the decode kernel's layout);
+//     * S^T = K Q^T on MFMA 32x32x16 (queries in registers as the B operand);
+//       the A operand reads key rows in the order that makes S^T come out in
+//       the B-operand layout of PV (row R holds key R with bits 2 and 3
+//       swapped), so the weights never leave the wave;
+//     * online softmax in the exp2 domain with a lazy reference: the output is
+//       rescaled only when a query's running max rises by more than 2^8;
+//     * O^T += V^T P^T on MFMA, V^T from the staged rows by transpose reads.
+#include "decode_tile.h"
+
+namespace mla {
+namespace {
+
+constexpr int kPfDc = 512, kPfDn = 128, kPfDr = 64, kPfDv = 128;
+
+// ---------------------------------------------------------------- 1. RoPE
+
+__global__ void __launch_bounds__(256) prefill_rope_kernel(const uint16_t* __restrict__ q_rope,
+                                                           const uint16_t* __restrict__ k_rope,
+                                                           const int32_t* __restrict__ cu, int n_seq, int H,
+                                                           uint16_t* __restrict__ qr_out, uint16_t* __restrict__ kr_out,
+                                                           RopeFreqs f) {
+  __shared__ float s_cs[kPfDr / 2], s_sn[kPfDr / 2];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  if (tid < kPfDr / 2) {
+    // the sequence holding token t: the last b with cu[b] <= t
+    int lo = 0, hi = n_seq;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (cu[mid] <= t) lo = mid;
+      else hi = mid;
+    }
+    float cs, sn;
+    rope_cos_sin(t - cu[lo], f.inv_freq[tid], &cs, &sn);
+    s_cs[tid] = cs;
+    s_sn[tid] = sn;
+  }
+  __syncthreads();
+  for (int i = tid; i < H * (kPfDr / 2); i += 256) {
+    const int s = i / (kPfDr / 2), p = i % (kPfDr / 2);
+    const int64_t at = ((int64_t)t * H + s) * kPfDr + 2 * p;
+    const uint32_t x2 = *(const uint32_t*)(q_rope + at);
+    float ox, oy;
+    rope_pair(bf16_bits_to_f32((uint16_t)(x2 & 0xffffu)), bf16_bits_to_f32((uint16_t)(x2 >> 16)), s_cs[p], s_sn[p], &ox,
+              &oy);
+    *(uint32_t*)(qr_out + at) = (uint32_t)f32_to_bf16_bits(ox) | ((uint32_t)f32_to_bf16_bits(oy) << 16);
+  }
+  if (tid < kPfDr / 2) {
+    const int64_t at = (int64_t)t * kPfDr + 2 * tid;
+    const uint32_t x2 = *(const uint32_t*)(k_rope + at);
+    float ox, oy;
+    rope_pair(bf16_bits_to_f32((uint16_t)(x2 & 0xffffu)), bf16_bits_to_f32((uint16_t)(x2 >> 16)), s_cs[tid],
+              s_sn[tid], &ox, &oy);
+    *(uint32_t*)(kr_out + at) = (uint32_t)f32_to_bf16_bits(ox) | ((uint32_t)f32_to_bf16_bits(oy) << 16);
+  }
+}
+
+// ---------------------------------------------------------------- 2. decompression
+
+constexpr int kDcTok = 128;                  // tokens per tile
+constexpr int kDcChunk = 64;                 // contraction chunk
+constexpr int kDcRow = kDcChunk * 2 + 16;    // LDS row bytes, padded: 16 rows at one 16-byte slot hit distinct banks
+constexpr int kDcBuf = 2 * 128 * kDcRow;     // one buffer: 128 weight rows, then 128 token rows
+
+__device__ __forceinline__ u32x2 pf_pack4(float a, float b, float c, float d) {
+  u32x2 r;
+  r[0] = (uint32_t)f32_to_bf16_bits(a) | ((uint32_t)f32_to_bf16_bits(b) << 16);
+  r[1] = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
+  return r;
+}
+
+// grid (ceil(T / 128), H, 2): z = 0 writes k_C with W_UK, z = 1 writes v with W_UV.
+// out^T tile (128 dims x 128 tokens) = W[s] (dims x 512) c^T (512 x tokens);
+// wave w computes dims 64(w % 2) .. +63 x tokens 64(w / 2) .. +63 (2 x 2 MFMA tiles).
+__global__ void __launch_bounds__(256) prefill_decompress_kernel(const uint16_t* __restrict__ c_kv,
+                                                                 const uint16_t* __restrict__ w_uk,
+                                                                 const uint16_t* __restrict__ w_uv,
+                                                                 uint16_t* __restrict__ kc, uint16_t* __restrict__ vv,
+                                                                 int T, int H) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[2 * kDcBuf];
+  lds_u8* lds = (lds_u8*)lds_raw;
+  const int s = blockIdx.y, t0 = blockIdx.x * kDcTok;
+  const uint16_t* W = (blockIdx.z == 0 ? w_uk : w_uv) + (int64_t)s * kPfDv * kPfDc;
+  uint16_t* out = blockIdx.z == 0 ? kc : vv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
+  const int wm = wave & 1, wn = wave >> 1;
+
+  // staging: piece p = tid + 256 j (j < 4) is 16 bytes, row p / 8, part p % 8 of the chunk
+  u32x4 wreg[4], creg[4];
+  auto load_chunk = [&](int kc0) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = tid + 256 * j, row = p >> 3, part = p & 7;
+      wreg[j] = *(const u32x4*)(W + (int64_t)row * kPfDc + kc0 + 8 * part);
+      const int t = min(t0 + row, T - 1);
+      creg[j] = *(const u32x4*)(c_kv + (int64_t)t * kPfDc + kc0 + 8 * part);
+    }
+  };
+  auto store_chunk = [&](int buf) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int p = tid + 256 * j, row = p >> 3, part = p & 7;
+      *(lds_u32x4*)(lds + buf * kDcBuf + row * kDcRow + 16 * part) = wreg[j];
+      *(lds_u32x4*)(lds + buf * kDcBuf + (128 + row) * kDcRow + 16 * part) = creg[j];
+    }
+  };
+
+  f32x16 acc[2][2];
+#pragma unroll
+  for (int a = 0; a < 2; ++a)
+#pragma unroll
+    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
+
+  load_chunk(0);
+  store_chunk(0);
+  __syncthreads();
+  constexpr int kChunks = kPfDc / kDcChunk;
+  for (int ch = 0; ch < kChunks; ++ch) {
+    if (ch + 1 < kChunks) load_chunk((ch + 1) * kDcChunk);
+    const lds_u8* base = lds + (ch & 1) * kDcBuf;
+#pragma unroll
+    for (int ks = 0; ks < kDcChunk / 16; ++ks) {
+      bf16x8 af[2], bf[2];
+#pragma unroll
+      for (int x = 0; x < 2; ++x) {
+        af[x] = *(const lds_bf16x8*)(base + (64 * wm + 32 * x + (lane & 31)) * kDcRow + (16 * ks + 8 * half) * 2);
+        bf[x] = *(const lds_bf16x8*)(base + (128 + 64 * wn + 32 * x + (lane & 31)) * kDcRow + (16 * ks + 8 * half) * 2);
+      }
+#pragma unroll
+      for (int a = 0; a < 2; ++a)
+#pragma unroll
+        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    }
+    if (ch + 1 < kChunks) store_chunk((ch + 1) & 1);
+    __syncthreads();
+  }
+  // tile (a, b): lane holds token 64 wn + 32 b + lane % 32, dims 64 wm + 32 a + 8 (i / 4) + 4 half + i % 4
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int t = t0 + 64 * wn + 32 * b + (lane & 31);
+    if (t >= T) continue;
+    uint16_t* dst = out + ((int64_t)t * H + s) * kPfDv + 64 * wm + 4 * half;
+#pragma unroll
+    for (int a = 0; a < 2; ++a)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(u32x2*)(dst + 32 * a + 8 * g) =
+            pf_pack4(acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
+  }
+}
+
+// ---------------------------------------------------------------- 3. attention
+
+constexpr int kQBlk = 128;                   // queries per work-group (32 per wave)
+constexpr int kKBlk = 64;                    // keys per stage
+constexpr int kRowBlocks = 5;                // 1 KB blocks per 8 staged rows: k_C (2) | k_R (1) | v (2)
+constexpr int kStage = kKBlk / 8 * kRowBlocks * 1024;   // 40960
+constexpr int kQk = (kPfDn + kPfDr) / 16;    // 12 QK k-steps
+constexpr int kKf = 8;                       // K fragments in flight ahead of the MFMA chain
+
+// staged row r, 16-byte chunk c (c < 16: k_C, 16..23: k_R, 24..39: v)
+__device__ __forceinline__ uint32_t stage_off(int r, int c) {
+  return ((r >> 3) * kRowBlocks + (c >> 3)) * 1024 + (r & 7) * 128 + 16 * ((c & 7) ^ swz(r & 7));
+}
+
+struct PrefillArgs {
+  const uint16_t* q_nope;     // [T][H][128]
+  const uint16_t* q_rot;      // [T][H][64] rotated
+  const uint16_t* k_c;        // [T][H][128]
+  const uint16_t* k_rot;      // [T][64] rotated
+  const uint16_t* v;          // [T][H][128]
+  const int32_t* cu;          // [n_seq + 1]
+  uint16_t* out;              // [T][H][128]
+  float* lse;                 // [T][H]
+  int n_seq, H, n_qblk;       // n_qblk = ceil(max_seqlen / 128)
+  float scale_log2;
+};
+
+// one direct-to-LDS load of 16 bytes per lane: LDS m0 + 16 lane <- src + voff
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t voff, uint32_t m0) {
+  const uint64_t a = (uint64_t)(uintptr_t)src;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t sv = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane(m0);
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v], %[s]"
+               :
+               : [v] "v"(voff), [s] "s"(sv), [m] "s"(m)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+__global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillArgs a) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[2 * kStage];
+  lds_u8* lds = (lds_u8*)lds_raw;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, lr = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int H = a.H;
+
+  // work order: all query blocks of one (sequence, head) on one XCD, the
+  // heaviest (last) block first, so that the head's keys stay in its L2
+  const int total = a.n_seq * H * a.n_qblk;
+  const int k = xcd_unit(blockIdx.x, total);
+  const int pair = k / a.n_qblk, qb = a.n_qblk - 1 - k % a.n_qblk;
+  const int b = pair / H, s = pair % H;
+  const int cu0 = a.cu[b], L = a.cu[b + 1] - cu0;
+  const int q0 = qb * kQBlk;
+  if (q0 >= L) return;
+  const int qw = q0 + 32 * wave;                       // this wave's first query
+  const int q = min(qw + lr, L - 1);                   // this lane's query (past the end: a copy of the last)
+
+  // queries: B operand, query q, dims 16k + 8 half .. +7 (k < 8: q_nope, else the rotated part)
+  bf16x8 qf[kQk];
+  {
+    const bf16x8* qn = (const bf16x8*)(a.q_nope + ((int64_t)(cu0 + q) * H + s) * kPfDn) + half;
+    const bf16x8* qr = (const bf16x8*)(a.q_rot + ((int64_t)(cu0 + q) * H + s) * kPfDr) + half;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) qf[kk] = qn[2 * kk];
+#pragma unroll
+    for (int kk = 8; kk < kQk; ++kk) qf[kk] = qr[2 * (kk - 8)];
+  }
+  __builtin_amdgcn_s_waitcnt(0);             // queries resident before any stage load is queued
+
+  // per-lane LDS offsets.  K (A operand of QK): row R = lr of a 32-key half reads
+  // key R with bits 2 and 3 swapped; k-step kk reads chunk 2 kk + half.
+  const int kr_row = (lr & ~12) | ((lr & 4) << 1) | ((lr & 8) >> 1);
+  uint32_t kb[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) kb[m] = stage_off(kr_row, 2 * m + half);
+  // V^T (A operand of PV), dims 32 db + lane % 32, keys 16 ks + 8 half .. +7, as
+  // two transpose reads (4 keys each); base by (db & 1, hh), + (db >> 1) KB, + 10 KB ks
+  uint32_t vb[4];
+  {
+    const int gi = lane >> 4, sp = lane & 15;
+    const int rr0 = 8 * (gi >> 1) + (sp >> 2);
+#pragma unroll
+    for (int x = 0; x < 2; ++x)
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {
+        const int vdim = 32 * x + 16 * (gi & 1) + 4 * (sp & 3);
+        vb[x * 2 + hh] = stage_off(rr0 + 4 * hh, 24 + (vdim >> 3)) + ((vdim & 7) << 1);
+      }
+  }
+
+  // stage loads: wave w brings rows 16w .. 16w+15 of the block, five 1 KB
+  // blocks per 8 rows; lane l: row 16w + 8g + l/8, logical chunk 8cb + ((l % 8) ^ swz(l / 8))
+  const int last_key = min(L, q0 + kQBlk) - 1;
+  const int n_kblk = last_key / kKBlk + 1;
+  auto load_stage = [&](int kbk) {
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds + (kbk & 1) * kStage);
+    const int key0 = kbk * kKBlk;
+    const int64_t row0 = cu0 + key0;
+#pragma unroll
+    for (int g = 0; g < 2; ++g) {
+      const int r = 16 * wave + 8 * g + (lane >> 3);
+      const int re = key0 + r < L ? r : 0;       // past the end: the block's first key (finite, masked)
+      const int sl = (lane & 7) ^ swz(lane >> 3);
+      const uint32_t m0 = dst + (uint32_t)(((2 * wave + g) * kRowBlocks) * 1024);
+      // k_C chunks 0..15 and v chunks 24..39 (per-head rows of 256 B), k_R chunks 16..23 (128 B rows)
+      const uint32_t hoff = (uint32_t)((re * H + s) * (kPfDn * 2)) + 16 * sl;
+      dma16(a.k_c + row0 * H * kPfDn, hoff, m0);
+      dma16(a.k_c + row0 * H * kPfDn, hoff + 128, m0 + 1024);
+      dma16(a.k_rot + row0 * kPfDr, (uint32_t)(re * (kPfDr * 2)) + 16 * sl, m0 + 2048);
+      dma16(a.v + row0 * H * kPfDv, hoff, m0 + 3072);
+      dma16(a.v + row0 * H * kPfDv, hoff + 128, m0 + 4096);
+    }
+  };
+
+  const float sl2 = a.scale_log2;
+  float m_ref = -INFINITY, l_part = 0.f;
+  f32x16 o[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+
+  load_stage(0);
+  for (int kbk = 0; kbk < n_kblk; ++kbk) {
+    wait_vmcnt<0>();                         // this wave's share of stage kbk has landed
+    lds_barrier();                           // ... and everyone's; stage kbk-1 is free
+    if (kbk + 1 < n_kblk) load_stage(kbk + 1);
+    const uint32_t tb = (uint32_t)(uintptr_t)(lds + (kbk & 1) * kStage);
+
+    // ---- S^T for the two 32-key halves
+    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      bf16x8 kf[kKf];
+#pragma unroll
+      for (int kk = 0; kk < kKf; ++kk) kf[kk] = *(const lds_bf16x8*)(uintptr_t)(tb + kb[kk % 4] + 1024 * (kk / 4) + 20480 * t);
+#pragma unroll
+      for (int kk = 0; kk < kQk; ++kk) {
+        const bf16x8 cur = kf[kk % kKf];
+        if (kk + kKf < kQk)
+          kf[kk % kKf] = *(const lds_bf16x8*)(uintptr_t)(tb + kb[kk % 4] + 1024 * ((kk + kKf) / 4) + 20480 * t);
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[kk], sacc[t], 0, 0, 0);
+      }
+    }
+
+    // ---- softmax: lane holds query q, keys 64 kbk + 32 t + 16 (i / 8) + 8 half + i % 8
+    float sv[2][16];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) sv[t][i] = sacc[t][i];
+    if (kbk * kKBlk + kKBlk - 1 > qw) {      // a block reaching this wave's diagonal (wave-uniform)
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int key = kbk * kKBlk + 32 * t + 16 * (i / 8) + 8 * half + (i % 8);
+          sv[t][i] = key <= q ? sv[t][i] : -INFINITY;
+        }
+    }
+    float bmax = sv[0][0];
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, sv[t][i]);
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+      bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+    }
+    const float tmax = bmax * sl2;
+    const bool raise = tmax > m_ref + 8.0f;  // also when nothing is accumulated yet (m_ref = -inf)
+    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+      const float m_new = raise ? tmax : m_ref;
+      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) o[i] *= alpha;
+      l_part *= alpha;
+      m_ref = m_new;
+    }
+    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
+    bf16x8 pb[4];                            // B operand of PV k-step 2t + j: regs 8j .. 8j+7 of half t
+    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    float psum = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        bf16x8 v8;
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const f32x2 pv = {__builtin_amdgcn_exp2f(fmaf(sv[t][8 * j + e], sl2, neg_m)),
+                            __builtin_amdgcn_exp2f(fmaf(sv[t][8 * j + e + 1], sl2, neg_m))};
+          const bf16x2 p2 = __builtin_convertvector(pv, bf16x2);
+          psum = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, psum, false);
+          v8[e] = p2[0];
+          v8[e + 1] = p2[1];
+        }
+        pb[2 * t + j] = v8;
+      }
+    l_part += psum;
+
+    // ---- O^T += V^T P^T: 4 dim blocks x 4 key steps
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) {
+        const uint32_t base = tb + 10240 * ks + 1024 * (db >> 1);
+        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(base + vb[(db & 1) * 2]));
+        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(base + vb[(db & 1) * 2 + 1]));
+        const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], o[db], 0, 0, 0);
+      }
+  }
+
+  // ---- normalise and store: O^T tile db, lane holds query qw + lr, dims 32 db + 8 (i / 4) + 4 half + i % 4
+  float l_tot;
+  {
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+  }
+  if (qw + lr < L) {
+    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+    uint16_t* dst = a.out + ((int64_t)(cu0 + qw + lr) * H + s) * kPfDv + 4 * half;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int g = 0; g < 4; ++g)
+        *(u32x2*)(dst + 32 * db + 8 * g) =
+            pf_pack4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+    if (half == 0)
+      a.lse[(int64_t)(cu0 + qw + lr) * H + s] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
+  }
+}
+
+}  // namespace
+
+bool prefill_supported(const mla_dims& d) {
+  return d.act_dtype == MLA_BF16 && d.d_c == kPfDc && d.d_nope == kPfDn && d.d_rope == kPfDr && d.d_v == kPfDv;
+}
+
+size_t prefill_workspace_bytes(const mla_dims& d, int64_t total_tokens) {
+  // k_C, v [T][H][128], q_R' [T][H][64], k_R' [T][64], bf16 each, 256-byte aligned pieces
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t T = (size_t)total_tokens, H = (size_t)d.n_heads;
+  return up(T * H * kPfDn * 2) + up(T * H * kPfDv * 2) + up(T * H * kPfDr * 2) + up(T * kPfDr * 2);
+}
+
+mla_status launch_prefill(const mla_dims& d, int32_t n_seq, const int32_t* cu_seqlens, int32_t total_tokens,
+                          int32_t max_seqlen, const void* q_nope, const void* q_rope, const void* c_kv,
+                          const void* k_rope, const void* w_uk, const void* w_uv, void* ws, void* out, float* lse,
+                          hipStream_t st) {
+  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
+  const size_t T = (size_t)total_tokens, H = (size_t)d.n_heads;
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  uint16_t* kc = reinterpret_cast<uint16_t*>(p);
+  p += up(T * H * kPfDn * 2);
+  uint16_t* vv = reinterpret_cast<uint16_t*>(p);
+  p += up(T * H * kPfDv * 2);
+  uint16_t* qr = reinterpret_cast<uint16_t*>(p);
+  p += up(T * H * kPfDr * 2);
+  uint16_t* kr = reinterpret_cast<uint16_t*>(p);
+
+  const RopeFreqs f = make_rope_freqs(d);
+  hipLaunchKernelGGL(prefill_rope_kernel, dim3(total_tokens), dim3(256), 0, st, static_cast<const uint16_t*>(q_rope),
+                     static_cast<const uint16_t*>(k_rope), cu_seqlens, n_seq, d.n_heads, qr, kr, f);
+  hipLaunchKernelGGL(prefill_decompress_kernel, dim3((total_tokens + kDcTok - 1) / kDcTok, d.n_heads, 2), dim3(256), 0,
+                     st, static_cast<const uint16_t*>(c_kv), static_cast<const uint16_t*>(w_uk),
+                     static_cast<const uint16_t*>(w_uv), kc, vv, total_tokens, d.n_heads);
+  PrefillArgs a;
+  a.q_nope = static_cast<const uint16_t*>(q_nope);
+  a.q_rot = qr;
+  a.k_c = kc;
+  a.k_rot = kr;
+  a.v = vv;
+  a.cu = cu_seqlens;
+  a.out = static_cast<uint16_t*>(out);
+  a.lse = lse;
+  a.n_seq = n_seq;
+  a.H = d.n_heads;
+  a.n_qblk = (max_seqlen + kQBlk - 1) / kQBlk;
+  a.scale_log2 = d.softmax_scale * 1.4426950408889634f;
+  const int64_t grid = (int64_t)n_seq * d.n_heads * a.n_qblk;
+  hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)grid), dim3(256), 0, st, a);
+  return launch_status();
+}
+
+}  // namespace mla

@@ -154,6 +154,32 @@ def make_inputs(w: Workload, seed: int, *, spare_blocks: int = 1,
     return out
 
 
+def make_prefill_inputs(w: Workload, seed: int, seqlens: torch.Tensor) -> dict:
+    """Draw one prefill's worth of packed inputs: every token is both a query
+    and a key of its own sequence (same value recipe as make_inputs).
+
+    Keys:
+      q_nope [T, H, d_nope], q_rope [T, H, d_R], c_kv [T, d_c], k_rope [T, d_R]  (act dtype, unrotated)
+      w_uk [H, d_nope, d_c], w_uv [H, d_v, d_c]                                    (act dtype)
+      seqlens [B] int32, cu_seqlens [B+1] int32
+    """
+    gen = torch.Generator().manual_seed(seed)
+    seqlens = seqlens.to(torch.int32)
+    H, dt, T = w.n_heads, TORCH_DTYPE[w.act_dtype], int(seqlens.sum())
+    out = {}
+    out["q_nope"] = _normal(gen, (T, H, w.d_nope)).to(dt)
+    out["q_rope"] = _normal(gen, (T, H, w.d_rope)).to(dt)
+    out["c_kv"] = _normal(gen, (T, w.d_c)).to(dt)
+    out["k_rope"] = _normal(gen, (T, w.d_rope)).to(dt)
+    std = 1.0 / math.sqrt(w.d_c)
+    out["w_uk"] = _normal(gen, (H, w.d_nope, w.d_c), std).to(dt)
+    out["w_uv"] = _normal(gen, (H, w.d_v, w.d_c), std).to(dt)
+    cu = torch.zeros(len(seqlens) + 1, dtype=torch.int32)
+    cu[1:] = torch.cumsum(seqlens, 0).to(torch.int32)
+    out["seqlens"], out["cu_seqlens"] = seqlens, cu
+    return out
+
+
 def new_token_rows(inp: dict, q_per_seq: int) -> torch.Tensor:
     """Indices (into the token arrays) of the last `q_per_seq` tokens of each sequence."""
     cu, L = inp["cu_seqlens"], inp["seqlens"].to(torch.int64)

@@ -429,3 +429,16 @@ def test_prefill_is_causal():
                                P2["base"])
     assert np.array_equal(o1[:9], o2[:9])
     assert not np.allclose(o1[9:], o2[9:])
+
+
+def test_prefill_operand_rounding_is_a_small_perturbation():
+    """Rounding the attention operands to bf16 moves the result by about the
+    bf16 resolution, and rounding nothing reproduces the exact oracle."""
+    P = _prefill_problem(74, T=29)
+    args = (P["q_nope"], P["q_rope"], P["c"], P["kr"], P["w_uk"], P["w_uv"], P["scale"], P["base"])
+    o, lse = O.prefill_mha_form(*args)
+    o_r, lse_r = O.prefill_mha_form(*args, operand_dtype="bf16")
+    rel = np.linalg.norm(o_r - o) / np.linalg.norm(o)
+    assert 1e-5 < rel < 2e-2
+    o_n, _ = O.prefill_mha_form(*args, operand_dtype=None)
+    assert np.array_equal(o_n, o)
