@@ -76,6 +76,10 @@ def parse():
                     help="sequences of the workload the CPU oracle is timed on (0 = skip)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode+combine calls (for profiling)")
+    ap.add_argument("--prefill", action="store_true",
+                    help="time the MHA-form prefill (mla_prefill) of packed prompts instead of a decode step")
+    ap.add_argument("--prefill-seqs", default="4096,4096,4096,4096",
+                    help="prompt lengths of the prefill workload (comma separated)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB (5 launches): "
                          "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -140,6 +144,9 @@ def main():
         sys.exit(2)
     if args.calib_copy_mib > 0:
         calib_copy(args.calib_copy_mib)
+        return
+    if args.prefill:
+        bench_prefill(args)
         return
     import torch
 
@@ -259,6 +266,73 @@ def main():
                      "kernel": "decode576_kernel", "bytes_per_launch": cache_bytes,
                      "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)},
         "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def bench_prefill(args):
+    """Prefill of packed prompts in the MHA form at V3 shape (128 heads): one
+    mla_prefill call (RoPE prep, K/V decompression, causal attention) per step."""
+    import torch
+
+    import mla_latent_kv_23_amd as M
+    import mla_synth as S
+
+    lens = [int(x) for x in args.prefill_seqs.split(",")]
+    w = S.WORKLOADS["v3_bs64_ctx8k"]
+    dev = torch.device("cuda:0")
+    t0 = time.time()
+    inp = S.make_prefill_inputs(w, 4321, torch.tensor(lens, dtype=torch.int32))
+    d = M.make_dims(n_heads=w.n_heads, d_c=w.d_c, d_rope=w.d_rope, d_nope=w.d_nope, d_v=w.d_v,
+                    block_size=w.block_size, softmax_scale=w.softmax_scale, rope_base=w.rope_base,
+                    act_dtype=w.act_dtype, cache_dtype=w.cache_dtype)
+    x = {k: inp[k].to(dev) for k in ("q_nope", "q_rope", "c_kv", "k_rope", "w_uk", "w_uv", "cu_seqlens")}
+    T, H = sum(lens), w.n_heads
+    out = torch.empty((T, H, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
+    ws = torch.empty(M.prefill_workspace_bytes(d, T), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def step():
+        M.prefill(d, x["q_nope"], x["q_rope"], x["c_kv"], x["k_rope"], x["cu_seqlens"], max(lens), x["w_uk"],
+                  x["w_uv"], workspace=ws, out=out, lse=lse, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+    start, end = TimingEvent(), TimingEvent()
+    start.record(stream)
+    for _ in range(args.steps):
+        step()
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    # algorithmic FLOPs: causal attention 2 (192 + 128) per visible (query, key) pair and head,
+    # plus the K and V decompression 2 x 2 x 512 x 128 per token and head
+    visible = sum(L * (L + 1) // 2 for L in lens)
+    attn_flops = visible * H * 2 * ((w.d_nope + w.d_rope) + w.d_v)
+    dec_flops = T * H * 2 * 2 * w.d_c * w.d_nope
+    tflops = (attn_flops + dec_flops) / (ms * 1e-3) / 1e12
+    rec = {
+        "metric": "MLA prefill prompt tokens/sec (MHA form, causal), V3 shape",
+        "value": round(T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(d_c)) weights)",
+        "config": {"workload": "prefill_v3", "prompt_lengths": lens, "n_heads": H, "d_c": w.d_c,
+                   "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v, "parallelism": "single GPU"},
+        "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_step": attn_flops + dec_flops},
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(rec), flush=True)

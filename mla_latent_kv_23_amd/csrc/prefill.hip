@@ -210,7 +210,7 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t voff, uint32_t m
 }
 #pragma clang diagnostic pop
 
-__global__ void __launch_bounds__(256, 1) prefill_attn_kernel(PrefillArgs a) {
+__global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[2 * kStage];
   lds_u8* lds = (lds_u8*)lds_raw;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, lr = lane & 31;
