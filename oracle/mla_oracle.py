@@ -44,6 +44,8 @@ Readings where the pages are silent or garbled (each one is a choice):
   R6  weights are stored W_UK [H, d_nope, d_c], W_UV [H, d_v, d_c], so that
       k_C = W_UK[s] c and v = W_UV[s] c.
   R7  lse is the natural log of the sum of exp over the scaled scores.
+  R16 gated MLA: out = sigmoid(g) * o elementwise per head, with the gate
+      logits g [tokens, heads, d_v] given (the pages name the gate only).
 """
 from __future__ import annotations
 
@@ -294,6 +296,20 @@ def decode_absorbed_form(q_abs, c_cached, kr_cached, q_pos, scale):
 def up_proj(o_lat, w_uv):
     """o[.., s, :] = W_UV[s] o_lat[.., s, :] ([P1] 双重投影: o = [o^(1) W_v^(1), ...])."""
     return np.einsum("...hc,hvc->...hv", np.asarray(o_lat, dtype=F64), np.asarray(w_uv, dtype=F64))
+
+
+def output_gate(o, gate_logits):
+    """Gated MLA: each head's attention output is scaled elementwise by a
+    logistic gate, o * 1 / (1 + e^-g) ([P1], reader comments: gated MLA is MLA
+    with an output gate).  Reading R16: the gate logits g have o's shape and are
+    an input (computed upstream from the hidden state)."""
+    o = np.asarray(o, dtype=F64)
+    g = np.asarray(gate_logits, dtype=F64)
+    # the logistic function in the form that never overflows: for g >= 0,
+    # 1 / (1 + e^-g); for g < 0, e^g / (1 + e^g)
+    e = np.exp(-np.abs(g))
+    sig = np.where(g >= 0, 1.0 / (1.0 + e), e / (1.0 + e))
+    return o * sig
 
 
 def lse_merge(o_parts: Sequence[np.ndarray], lse_parts: Sequence[np.ndarray]):

@@ -442,3 +442,31 @@ def test_prefill_operand_rounding_is_a_small_perturbation():
     assert 1e-5 < rel < 2e-2
     o_n, _ = O.prefill_mha_form(*args, operand_dtype=None)
     assert np.array_equal(o_n, o)
+
+
+# ---------------------------------------------------------------- output gate (gated MLA)
+
+def test_output_gate_closed_forms():
+    r = _rng(21)
+    o = r.standard_normal((3, 4, 8))
+    # sigma(0) = 1/2 and sigma(ln 3) = 3/4 exactly (e^-ln3 = 1/3)
+    assert np.allclose(O.output_gate(o, np.zeros_like(o)), o / 2, rtol=0, atol=1e-15)
+    assert np.allclose(O.output_gate(o, np.full_like(o, math.log(3.0))), 0.75 * o, rtol=1e-15, atol=1e-15)
+    # saturation without overflow: a large positive logit passes o, a large negative one closes the gate
+    with np.errstate(over="raise", invalid="raise", divide="raise"):
+        assert np.array_equal(O.output_gate(o, np.full_like(o, 800.0)), o)
+        assert np.array_equal(O.output_gate(o, np.full_like(o, -800.0)), np.zeros_like(o))
+
+
+def test_output_gate_symmetry_and_library_logistic():
+    from scipy.special import expit
+    r = _rng(22)
+    o = r.standard_normal((5, 3, 16))
+    g = r.standard_normal((5, 3, 16)) * 6
+    # sigma(g) + sigma(-g) = 1, so the two gated outputs add up to the ungated one
+    assert np.allclose(O.output_gate(o, g) + O.output_gate(o, -g), o, rtol=0, atol=1e-14)
+    # the logistic function of scipy
+    assert np.allclose(O.output_gate(o, g), o * expit(g), rtol=1e-14, atol=1e-15)
+    # the gate only shrinks: |out| <= |o| elementwise, with the sign of o
+    out = O.output_gate(o, g)
+    assert np.all(np.abs(out) <= np.abs(o)) and np.all(out * o >= 0)
