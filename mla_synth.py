@@ -180,6 +180,31 @@ def make_prefill_inputs(w: Workload, seed: int, seqlens: torch.Tensor) -> dict:
     return out
 
 
+def make_chunk_prefill_inputs(w: Workload, seed: int, seqlens: torch.Tensor, qlens: torch.Tensor) -> dict:
+    """Chunked prefill over the paged cache: sequence b holds seqlens[b] cached
+    tokens (make_inputs' recipe and block tables), of which the last qlens[b]
+    are the chunk's queries.  Adds q_nope [Tq, H, d_nope], q_rope [Tq, H, d_R]
+    (act dtype, unrotated), cu_q and cu_k [B+1] int32 and qlens [B] int32."""
+    seqlens, qlens = seqlens.to(torch.int32), qlens.to(torch.int32)
+    assert bool((qlens <= seqlens).all()) and bool((qlens >= 0).all())
+    out = make_inputs(w, seed, seqlens=seqlens)
+    gen = torch.Generator().manual_seed(seed + 1)
+    dt, Tq = TORCH_DTYPE[w.act_dtype], int(qlens.sum())
+    out["q_nope"] = _normal(gen, (Tq, w.n_heads, w.d_nope)).to(dt)
+    out["q_rope"] = _normal(gen, (Tq, w.n_heads, w.d_rope)).to(dt)
+    out["qlens"] = qlens
+    cu_q = torch.zeros(len(qlens) + 1, dtype=torch.int32)
+    cu_q[1:] = torch.cumsum(qlens, 0).to(torch.int32)
+    out["cu_q"], out["cu_k"] = cu_q, out["cu_seqlens"].to(torch.int32)
+    return out
+
+
+def make_gate_logits(w: Workload, seed: int, n_tok: int) -> torch.Tensor:
+    """Output-gate logits of gated MLA, [n_tok, H, d_v] in the act dtype, N(0, 1)."""
+    gen = torch.Generator().manual_seed(seed)
+    return _normal(gen, (n_tok, w.n_heads, w.d_v)).to(TORCH_DTYPE[w.act_dtype])
+
+
 def new_token_rows(inp: dict, q_per_seq: int) -> torch.Tensor:
     """Indices (into the token arrays) of the last `q_per_seq` tokens of each sequence."""
     cu, L = inp["cu_seqlens"], inp["seqlens"].to(torch.int64)

@@ -268,6 +268,21 @@ def prefill_mha_form(q_nope, q_rope, c_kv, k_rope_raw, w_uk, w_uv, scale, base,
     return o, lse
 
 
+def prefill_chunk_mha_form(q_nope, q_rope, c_cached, kr_cached, w_uk, w_uv, scale, base,
+                           heads: Optional[Sequence[int]] = None, operand_dtype: Optional[str] = None):
+    """Chunked prefill of one sequence in the MHA form ([P1] 双重投影,
+    training/prefill column): its last Lq tokens are the queries and attend to
+    all L cached tokens up to their own position (R3: query j at L - Lq + j).
+    q_nope [Lq, H, d_nope], q_rope [Lq, H, d_R] (unrotated); c_cached [L, d_c]
+    and kr_cached [L, d_R] are the values as cached.  Returns o [Lq, h, d_v]
+    and lse [Lq, h]."""
+    L, Lq = np.asarray(c_cached).shape[0], np.asarray(q_nope).shape[0]
+    q_pos = L - Lq + np.arange(Lq)
+    o, _, lse = decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scale, base, heads,
+                                operand_dtype)
+    return o, lse
+
+
 def absorb_q(q_nope, q_rope, q_pos, w_uk, base):
     """Absorbed query [.., H, d_c + d_R] = [W_UK[s]^T q_nope | RoPE(q_R)] ([P1] 双重投影 right column)."""
     q_nope = np.asarray(q_nope, dtype=F64)

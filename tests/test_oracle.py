@@ -444,6 +444,24 @@ def test_prefill_operand_rounding_is_a_small_perturbation():
     assert np.array_equal(o_n, o)
 
 
+def test_prefill_chunk_rows_equal_whole_prompt_rows():
+    """A chunk of the last Lq tokens attending to the whole prompt gives the
+    last Lq rows of the whole prompt's prefill, for every split point."""
+    P = _prefill_problem(75, T=23)
+    o, lse = O.prefill_mha_form(P["q_nope"], P["q_rope"], P["c"], P["kr"], P["w_uk"], P["w_uv"], P["scale"],
+                                P["base"])
+    kr_c = O.store_value(O.rope(P["kr"], np.arange(23), P["base"]), "bf16")
+    for lq in [1, 5, 22, 23]:
+        oc, lc = O.prefill_chunk_mha_form(P["q_nope"][23 - lq:], P["q_rope"][23 - lq:], P["c"], kr_c, P["w_uk"],
+                                          P["w_uv"], P["scale"], P["base"])
+        assert np.allclose(oc, o[23 - lq:], rtol=1e-12, atol=1e-13)
+        assert np.allclose(lc, lse[23 - lq:], rtol=1e-12)
+    # a chunk's rows do not depend on tokens after the chunk's own positions
+    oc2, _ = O.prefill_chunk_mha_form(P["q_nope"][10:12], P["q_rope"][10:12], P["c"][:12], kr_c[:12], P["w_uk"],
+                                      P["w_uv"], P["scale"], P["base"])
+    assert np.allclose(oc2, o[10:12], rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------- output gate (gated MLA)
 
 def test_output_gate_closed_forms():
