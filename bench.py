@@ -76,10 +76,15 @@ def parse():
                     help="sequences of the workload the CPU oracle is timed on (0 = skip)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode+combine calls (for profiling)")
+    ap.add_argument("--gated", action="store_true",
+                    help="gated MLA: the up-projection applies a sigmoid output gate (mla_up_proj_gated)")
     ap.add_argument("--prefill", action="store_true",
                     help="time the MHA-form prefill (mla_prefill) of packed prompts instead of a decode step")
     ap.add_argument("--prefill-seqs", default="4096,4096,4096,4096",
                     help="prompt lengths of the prefill workload (comma separated)")
+    ap.add_argument("--prefill-chunk", type=int, default=0,
+                    help="with --prefill: chunked prefill, the last N tokens of each prompt are the queries and "
+                         "the whole prompt is read from the paged cache (mla_prefill_paged)")
     ap.add_argument("--calib-copy-mib", type=int, default=0,
                     help="instead of the benchmark, run a plain device copy of this many MiB (5 launches): "
                          "the reference for scaling the FETCH_SIZE / WRITE_SIZE counters")
@@ -179,6 +184,7 @@ def main():
         new_c_kv=inp["c_kv"][new_rows].to(dev), new_k_rope=inp["k_rope"][new_rows].to(dev),
         new_seq_id=inp["tok_seq"][new_rows].to(dev), new_pos=inp["tok_pos"][new_rows].to(dev),
         block_table=table, seqlens=seqlens, pool=pool, w_uk=inp["w_uk"].to(dev), w_uv=inp["w_uv"].to(dev))
+    gate = S.make_gate_logits(w, S.SEEDS[w.name] + 7, n_tok).to(dev) if args.gated else None
     step = M.DecodeStep(d, B, sq, table.shape[1], num_splits=args.num_splits, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
@@ -210,7 +216,8 @@ def main():
         if step.needs_combine:
             M.combine(dd, seqlens, table.shape[1], step.workspace, step.o_latent, step.lse, args.num_splits,
                       stream=stream)
-        M.up_proj(dd, step.o_latent.view(n_tok, H, -1), step_inputs["w_uv"], out=step.out, stream=stream)
+        M.up_proj(dd, step.o_latent.view(n_tok, H, -1), step_inputs["w_uv"], out=step.out, stream=stream,
+                  gate=gate)
 
     if args.decode_only:   # the queries must exist once
         M.absorb_q(d, step_inputs["q_nope"], step_inputs["q_rope"], step_inputs["q_pos"], step_inputs["w_uk"],
@@ -257,7 +264,8 @@ def main():
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(d_c)) weights)",
         "config": {"workload": w.name, "batch": B, "q_per_seq": sq, "n_heads": H, "d_c": w.d_c,
                    "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v, "seqlen": w.seqlen,
-                   "block_size": w.block_size, "cache_dtype": w.cache_dtype, "parallelism": "single GPU"},
+                   "block_size": w.block_size, "cache_dtype": w.cache_dtype, "output_gate": bool(args.gated),
+                   "parallelism": "single GPU"},
         "decode_ms": round(dec_ms, 4),
         "decode_hbm_gbps": round(dec_gbps, 1),
         "decode_tflops": round(dec_tflops, 1),
@@ -272,31 +280,51 @@ def main():
 
 
 def bench_prefill(args):
-    """Prefill of packed prompts in the MHA form at V3 shape (128 heads): one
-    mla_prefill call (RoPE prep, K/V decompression, causal attention) per step."""
+    """Prefill at V3 shape (128 heads) in the MHA form, one call per step:
+    whole prompts with mla_prefill (RoPE prep, K/V decompression, causal
+    attention), or, with --prefill-chunk N, the last N tokens of each prompt
+    attending to the whole prompt in the paged cache with mla_prefill_paged."""
     import torch
 
     import mla_latent_kv_23_amd as M
     import mla_synth as S
 
     lens = [int(x) for x in args.prefill_seqs.split(",")]
+    chunk = args.prefill_chunk
     w = S.WORKLOADS["v3_bs64_ctx8k"]
     dev = torch.device("cuda:0")
     t0 = time.time()
-    inp = S.make_prefill_inputs(w, 4321, torch.tensor(lens, dtype=torch.int32))
     d = M.make_dims(n_heads=w.n_heads, d_c=w.d_c, d_rope=w.d_rope, d_nope=w.d_nope, d_v=w.d_v,
                     block_size=w.block_size, softmax_scale=w.softmax_scale, rope_base=w.rope_base,
                     act_dtype=w.act_dtype, cache_dtype=w.cache_dtype)
-    x = {k: inp[k].to(dev) for k in ("q_nope", "q_rope", "c_kv", "k_rope", "w_uk", "w_uv", "cu_seqlens")}
-    T, H = sum(lens), w.n_heads
-    out = torch.empty((T, H, w.d_v), dtype=torch.bfloat16, device=dev)
-    lse = torch.empty((T, H), dtype=torch.float32, device=dev)
-    ws = torch.empty(M.prefill_workspace_bytes(d, T), dtype=torch.uint8, device=dev)
+    H, Tk = w.n_heads, sum(lens)
+    qlens = [min(chunk, L) for L in lens] if chunk > 0 else lens
+    Tq = sum(qlens)
     stream = torch.cuda.current_stream()
+    gate = S.make_gate_logits(w, 4323, Tq).to(dev) if args.gated else None
+    out = torch.empty((Tq, H, w.d_v), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((Tq, H), dtype=torch.float32, device=dev)
+    if chunk > 0:
+        inp = S.make_chunk_prefill_inputs(w, 4322, torch.tensor(lens, dtype=torch.int32),
+                                          torch.tensor(qlens, dtype=torch.int32))
+        pool = torch.empty((inp["n_blocks"] * M.cache_block_bytes(d),), dtype=torch.uint8, device=dev)
+        table = inp["block_table"].to(dev)
+        M.append_cache(d, inp["c_kv"].to(dev), inp["k_rope"].to(dev), inp["tok_seq"].to(dev), inp["tok_pos"].to(dev),
+                       table, pool)
+        x = {k: inp[k].to(dev) for k in ("q_nope", "q_rope", "w_uk", "w_uv", "cu_q", "cu_k")}
+        ws = torch.empty(M.prefill_paged_workspace_bytes(d, Tq, Tk), dtype=torch.uint8, device=dev)
 
-    def step():
-        M.prefill(d, x["q_nope"], x["q_rope"], x["c_kv"], x["k_rope"], x["cu_seqlens"], max(lens), x["w_uk"],
-                  x["w_uv"], workspace=ws, out=out, lse=lse, stream=stream)
+        def step():
+            M.prefill_paged(d, x["q_nope"], x["q_rope"], x["cu_q"], max(qlens), x["cu_k"], Tk, pool, table,
+                            x["w_uk"], x["w_uv"], workspace=ws, out=out, lse=lse, stream=stream, gate=gate)
+    else:
+        inp = S.make_prefill_inputs(w, 4321, torch.tensor(lens, dtype=torch.int32))
+        x = {k: inp[k].to(dev) for k in ("q_nope", "q_rope", "c_kv", "k_rope", "w_uk", "w_uv", "cu_seqlens")}
+        ws = torch.empty(M.prefill_workspace_bytes(d, Tk), dtype=torch.uint8, device=dev)
+
+        def step():
+            M.prefill(d, x["q_nope"], x["q_rope"], x["c_kv"], x["k_rope"], x["cu_seqlens"], max(lens), x["w_uk"],
+                      x["w_uv"], workspace=ws, out=out, lse=lse, stream=stream, gate=gate)
 
     for _ in range(args.warmup):
         step()
@@ -310,14 +338,15 @@ def bench_prefill(args):
     torch.cuda.synchronize()
     ms = start.elapsed_time(end) / args.steps
     # algorithmic FLOPs: causal attention 2 (192 + 128) per visible (query, key) pair and head,
-    # plus the K and V decompression 2 x 2 x 512 x 128 per token and head
-    visible = sum(L * (L + 1) // 2 for L in lens)
+    # plus the K and V decompression 2 x 2 x 512 x 128 per cached token and head
+    visible = sum(Lq * (L - Lq) + Lq * (Lq + 1) // 2 for L, Lq in zip(lens, qlens))
     attn_flops = visible * H * 2 * ((w.d_nope + w.d_rope) + w.d_v)
-    dec_flops = T * H * 2 * 2 * w.d_c * w.d_nope
+    dec_flops = Tk * H * 2 * 2 * w.d_c * w.d_nope
     tflops = (attn_flops + dec_flops) / (ms * 1e-3) / 1e12
     rec = {
-        "metric": "MLA prefill prompt tokens/sec (MHA form, causal), V3 shape",
-        "value": round(T / (ms * 1e-3), 1),
+        "metric": ("MLA chunked prefill query tokens/sec (MHA form over the paged cache), V3 shape" if chunk > 0
+                   else "MLA prefill prompt tokens/sec (MHA form, causal), V3 shape"),
+        "value": round(Tq / (ms * 1e-3), 1),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -328,8 +357,9 @@ def bench_prefill(args):
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) activations, N(0,1/sqrt(d_c)) weights)",
-        "config": {"workload": "prefill_v3", "prompt_lengths": lens, "n_heads": H, "d_c": w.d_c,
-                   "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v, "parallelism": "single GPU"},
+        "config": {"workload": "prefill_chunk_v3" if chunk > 0 else "prefill_v3", "prompt_lengths": lens,
+                   "query_tokens_per_prompt": qlens, "n_heads": H, "d_c": w.d_c, "d_rope": w.d_rope,
+                   "d_nope": w.d_nope, "d_v": w.d_v, "output_gate": bool(args.gated), "parallelism": "single GPU"},
         "roofline": {"bound": "mfma", "achieved": round(tflops, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                      "frac": round(tflops / BF16_PEAK_TFLOPS, 4), "traffic": None,
                      "flops_per_step": attn_flops + dec_flops},

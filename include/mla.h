@@ -201,6 +201,20 @@ mla_status mla_up_proj(const mla_dims* dims, int32_t n_tok, const void* o_latent
                        const void* w_uv, void* out, mla_stream_t stream);
 
 /*
+ * mla_up_proj_gated -- the up-projection with an output gate (gated MLA: MLA
+ * with an elementwise output gate on each head's attention output, named in
+ * the reader comments of "Transformer升级之路：21、MLA好在哪里？（下）").
+ *   out[t, s, v] = sigmoid(gate[t, s, v]) * sum_c w_uv[s, v, c] * o_latent[t, s, c]
+ * gate [n_tok, H, d_v] holds the gate logits (act dtype; computed upstream
+ * from the hidden state).  The product is formed in float32 (sigmoid(g) =
+ * 1 / (1 + e^-g)) and rounded once to the act dtype.  Other arguments and the
+ * error behaviour as mla_up_proj; a null gate with n_tok > 0 is
+ * MLA_ERR_INVALID_ARG.
+ */
+mla_status mla_up_proj_gated(const mla_dims* dims, int32_t n_tok, const void* o_latent,
+                             const void* w_uv, const void* gate, void* out, mla_stream_t stream);
+
+/*
  * mla_prefill -- causal attention over whole prompts in the MHA form
  * ("Transformer升级之路：21、MLA好在哪里？（下）", 双重投影, training/prefill
  * column: each head gets its own key k = [c W_k^(s) | k_R] and value
@@ -218,7 +232,9 @@ mla_status mla_up_proj(const mla_dims* dims, int32_t n_tok, const void* o_latent
  * a host value); q_nope [T, H, d_nope], q_rope [T, H, d_rope] (unrotated),
  * c_kv [T, d_c], k_rope [T, d_rope] (unrotated), w_uk [H, d_nope, d_c],
  * w_uv [H, d_v, d_c], all bf16; out [T, H, d_v] (bf16) and lse [T, H] (float32)
- * are written.  workspace: at least mla_prefill_workspace_bytes (the
+ * are written.  gate: null, or [T, H, d_v] bf16 output-gate logits (gated
+ * MLA, as mla_up_proj_gated): out = sigmoid(gate) * o in float32 before the
+ * rounding; lse is not gated.  workspace: at least mla_prefill_workspace_bytes (the
  * decompressed keys and values and the rotated parts live there), 16-byte
  * aligned.  Supported: bf16, d_c 512, d_nope 128, d_rope 64, d_v 128 (else
  * MLA_ERR_UNSUPPORTED).  T = 0 launches nothing.
@@ -227,8 +243,39 @@ size_t mla_prefill_workspace_bytes(const mla_dims* dims, int32_t total_tokens);
 mla_status mla_prefill(const mla_dims* dims, int32_t n_seq, const int32_t* cu_seqlens,
                        int32_t total_tokens, int32_t max_seqlen, const void* q_nope,
                        const void* q_rope, const void* c_kv, const void* k_rope,
-                       const void* w_uk, const void* w_uv, void* workspace,
+                       const void* w_uk, const void* w_uv, const void* gate, void* workspace,
                        size_t workspace_bytes, void* out, float* lse, mla_stream_t stream);
+
+/*
+ * mla_prefill_paged -- chunked prefill: the MHA form of mla_prefill, with the
+ * keys and values decompressed from the paged latent cache, so a chunk of new
+ * tokens attends to the prompt's cached prefix as well as to itself
+ * (positions and visibility as in mla_decode: "Transformer升级之路：21、
+ * MLA好在哪里？（下）", 双重投影, training/prefill column, for the form; the
+ * FlashMLA snippet of the Tencent Cloud article for the paged cache).
+ * Sequence b has Lq_b = cu_q[b+1] - cu_q[b] query tokens (its newest ones,
+ * already appended with mla_append_cache) and Lk_b = cu_k[b+1] - cu_k[b]
+ * cached tokens, Lq_b <= Lk_b.  Query j sits at position Lk_b - Lq_b + j and
+ * sees cached tokens 0..Lk_b - Lq_b + j:
+ *   key_t   = [W_UK[s] c_t | k_R'_t],  value_t = W_UV[s] c_t   (c_t, k_R'_t: cache row of token t)
+ *   query_j = [q_nope[j,s] | RoPE(q_rope[j,s], Lk_b - Lq_b + j)]
+ * cu_q, cu_k [n_seq + 1]: device int32, trusted (0 = cu[0] <= ... <=
+ * cu[n_seq] = total_q / total_k, Lq_b <= Lk_b, every Lq_b <= max_q, a host
+ * value).  cache_pool and block_table [n_seq, max_blocks] as mla_decode; the
+ * blocks covering tokens 0..Lk_b - 1 must be valid (trusted).  q_nope
+ * [total_q, H, d_nope], q_rope [total_q, H, d_rope] (unrotated), w_uk, w_uv,
+ * gate (null or [total_q, H, d_v]), out [total_q, H, d_v] and lse [total_q, H]
+ * as mla_prefill.  workspace: at least mla_prefill_paged_workspace_bytes,
+ * 16-byte aligned.  Supported: the dims of mla_prefill with a bf16 cache (else
+ * MLA_ERR_UNSUPPORTED).  total_q = 0 launches nothing.
+ */
+size_t mla_prefill_paged_workspace_bytes(const mla_dims* dims, int32_t total_q, int32_t total_k);
+mla_status mla_prefill_paged(const mla_dims* dims, int32_t n_seq, const int32_t* cu_q,
+                             int32_t total_q, int32_t max_q, const int32_t* cu_k, int32_t total_k,
+                             const void* q_nope, const void* q_rope, const void* cache_pool,
+                             const int32_t* block_table, int32_t max_blocks, const void* w_uk,
+                             const void* w_uv, const void* gate, void* workspace,
+                             size_t workspace_bytes, void* out, float* lse, mla_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -5,7 +5,7 @@ include/mla.h); this package is its Python binding.
 """
 from .binding import (  # noqa: F401
     BF16, F32, FP8_E4M3, Dims, MLAError, absorb_q, append_cache, cache_block_bytes, combine, decode,
-    decode_needs_combine, decode_workspace_bytes, load_library, make_dims, prefill, prefill_workspace_bytes,
-    up_proj,
+    decode_needs_combine, decode_workspace_bytes, load_library, make_dims, prefill, prefill_paged,
+    prefill_paged_workspace_bytes, prefill_workspace_bytes, up_proj,
 )
 from .pipeline import DecodeStep  # noqa: F401

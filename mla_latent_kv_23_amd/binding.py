@@ -62,8 +62,12 @@ SIGNATURES = {
     "mla_decode_needs_combine": (_I32, [_DP, _I32, _I32, _I32, _I32]),
     "mla_combine": (ctypes.c_int, [_DP, _I32, _I32, _P, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "mla_up_proj": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P]),
+    "mla_up_proj_gated": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P, _P]),
     "mla_prefill_workspace_bytes": (_SZ, [_DP, _I32]),
-    "mla_prefill": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
+    "mla_prefill": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
+    "mla_prefill_paged_workspace_bytes": (_SZ, [_DP, _I32, _I32]),
+    "mla_prefill_paged": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
+                                         _SZ, _P, _P, _P]),
 }
 
 
@@ -185,15 +189,22 @@ def combine(d: Dims, seqlens, max_blocks: int, workspace, o_latent, lse, num_spl
     return o_latent, lse
 
 
-def up_proj(d: Dims, o_latent, w_uv, out=None, stream=None):
-    """out[t, s] = W_UV[s] o_latent[t, s]; o_latent [n_tok, H, d_c]."""
+def up_proj(d: Dims, o_latent, w_uv, out=None, stream=None, gate=None):
+    """out[t, s] = W_UV[s] o_latent[t, s]; o_latent [n_tok, H, d_c].  With
+    gate [n_tok, H, d_v] (logits), out is multiplied by sigmoid(gate)
+    elementwise (mla_up_proj_gated)."""
     at = act_torch_dtype(d)
     n_tok = o_latent.shape[0]
     if out is None:
         out = torch.empty((n_tok, d.n_heads, d.d_v), dtype=at, device=o_latent.device)
-    _check("mla_up_proj", load_library().mla_up_proj(
-        ctypes.byref(d), n_tok, _ptr(o_latent, "o_latent", at), _ptr(w_uv, "w_uv", at), _ptr(out, "out", at),
-        _stream(stream)))
+    if gate is None:
+        _check("mla_up_proj", load_library().mla_up_proj(
+            ctypes.byref(d), n_tok, _ptr(o_latent, "o_latent", at), _ptr(w_uv, "w_uv", at), _ptr(out, "out", at),
+            _stream(stream)))
+    else:
+        _check("mla_up_proj_gated", load_library().mla_up_proj_gated(
+            ctypes.byref(d), n_tok, _ptr(o_latent, "o_latent", at), _ptr(w_uv, "w_uv", at),
+            _ptr(gate, "gate", at), _ptr(out, "out", at), _stream(stream)))
     return out
 
 
@@ -202,10 +213,11 @@ def prefill_workspace_bytes(d: Dims, total_tokens: int) -> int:
 
 
 def prefill(d: Dims, q_nope, q_rope, c_kv, k_rope, cu_seqlens, max_seqlen: int, w_uk, w_uv, workspace=None,
-            out=None, lse=None, stream=None):
+            out=None, lse=None, stream=None, gate=None):
     """Causal prefill of packed sequences in the MHA form.  q_nope [T, H, d_nope],
     q_rope [T, H, d_rope], c_kv [T, d_c], k_rope [T, d_rope]; cu_seqlens [n_seq + 1]
-    int32 on the device.  Returns (out [T, H, d_v], lse [T, H], workspace)."""
+    int32 on the device; gate [T, H, d_v] optional output-gate logits.
+    Returns (out [T, H, d_v], lse [T, H], workspace)."""
     at = act_torch_dtype(d)
     T = q_nope.shape[0]
     n_seq = cu_seqlens.shape[0] - 1
@@ -220,6 +232,38 @@ def prefill(d: Dims, q_nope, q_rope, c_kv, k_rope, cu_seqlens, max_seqlen: int, 
     _check("mla_prefill", load_library().mla_prefill(
         ctypes.byref(d), n_seq, _ptr(cu_seqlens, "cu_seqlens", torch.int32), T, max_seqlen,
         _ptr(q_nope, "q_nope", at), _ptr(q_rope, "q_rope", at), _ptr(c_kv, "c_kv", at), _ptr(k_rope, "k_rope", at),
-        _ptr(w_uk, "w_uk", at), _ptr(w_uv, "w_uv", at), _ptr(workspace, "workspace"), ws_bytes,
+        _ptr(w_uk, "w_uk", at), _ptr(w_uv, "w_uv", at), _ptr(gate, "gate", at), _ptr(workspace, "workspace"),
+        ws_bytes, _ptr(out, "out", at), _ptr(lse, "lse", torch.float32), _stream(stream)))
+    return out, lse, workspace
+
+
+def prefill_paged_workspace_bytes(d: Dims, total_q: int, total_k: int) -> int:
+    return load_library().mla_prefill_paged_workspace_bytes(ctypes.byref(d), total_q, total_k)
+
+
+def prefill_paged(d: Dims, q_nope, q_rope, cu_q, max_q: int, cu_k, total_k: int, pool, block_table, w_uk, w_uv,
+                  workspace=None, out=None, lse=None, stream=None, gate=None):
+    """Chunked prefill over the paged cache: sequence b's cu_q[b+1]-cu_q[b] newest
+    tokens (already appended) attend causally to its cu_k[b+1]-cu_k[b] cached
+    tokens.  q_nope [Tq, H, d_nope], q_rope [Tq, H, d_rope] (unrotated); cu_q,
+    cu_k [n_seq + 1] int32 on the device; total_k = cu_k[-1] (host value).
+    Returns (out [Tq, H, d_v], lse [Tq, H], workspace)."""
+    at = act_torch_dtype(d)
+    Tq = q_nope.shape[0]
+    n_seq = cu_q.shape[0] - 1
+    dev = q_nope.device
+    if out is None:
+        out = torch.empty((Tq, d.n_heads, d.d_v), dtype=at, device=dev)
+    if lse is None:
+        lse = torch.empty((Tq, d.n_heads), dtype=torch.float32, device=dev)
+    if workspace is None:
+        workspace = torch.empty(max(prefill_paged_workspace_bytes(d, Tq, total_k), 1), dtype=torch.uint8,
+                                device=dev)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("mla_prefill_paged", load_library().mla_prefill_paged(
+        ctypes.byref(d), n_seq, _ptr(cu_q, "cu_q", torch.int32), Tq, max_q, _ptr(cu_k, "cu_k", torch.int32),
+        total_k, _ptr(q_nope, "q_nope", at), _ptr(q_rope, "q_rope", at), _ptr(pool, "pool", torch.uint8),
+        _ptr(block_table, "block_table", torch.int32), block_table.shape[1], _ptr(w_uk, "w_uk", at),
+        _ptr(w_uv, "w_uv", at), _ptr(gate, "gate", at), _ptr(workspace, "workspace"), ws_bytes,
         _ptr(out, "out", at), _ptr(lse, "lse", torch.float32), _stream(stream)))
     return out, lse, workspace

@@ -214,8 +214,9 @@ mla_status mla_combine(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, cons
                         static_cast<hipStream_t>(stream));
 }
 
-mla_status mla_up_proj(const mla_dims* d, int32_t n_tok, const void* o_latent, const void* w_uv, void* out,
-                       mla_stream_t stream) {
+namespace {
+mla_status up_proj_common(const mla_dims* d, int32_t n_tok, const void* o_latent, const void* w_uv,
+                          const void* gate, void* out, mla_stream_t stream) {
   const mla_status s = dims_supported(d);
   if (s != MLA_OK) return s;
   if (n_tok < 0) return MLA_ERR_INVALID_ARG;
@@ -223,9 +224,23 @@ mla_status mla_up_proj(const mla_dims* d, int32_t n_tok, const void* o_latent, c
   if (!o_latent || !w_uv || !out) return MLA_ERR_INVALID_ARG;
   if (n_tok > 2147483647 / d->n_heads) return MLA_ERR_UNSUPPORTED;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  if (up_proj_tuned_applies(*d) && aligned16(o_latent) && aligned16(w_uv) && aligned16(out))
-    return launch_up_proj_tuned(*d, n_tok, o_latent, w_uv, out, st);
-  return launch_up_proj_generic(*d, n_tok, o_latent, w_uv, out, st);
+  // the tuned kernel reads the gate in 8-byte pieces
+  if (up_proj_tuned_applies(*d) && aligned16(o_latent) && aligned16(w_uv) && aligned16(out) &&
+      (!gate || aligned16(gate)))
+    return launch_up_proj_tuned(*d, n_tok, o_latent, w_uv, gate, out, st);
+  return launch_up_proj_generic(*d, n_tok, o_latent, w_uv, gate, out, st);
+}
+}  // namespace
+
+mla_status mla_up_proj(const mla_dims* d, int32_t n_tok, const void* o_latent, const void* w_uv, void* out,
+                       mla_stream_t stream) {
+  return up_proj_common(d, n_tok, o_latent, w_uv, nullptr, out, stream);
+}
+
+mla_status mla_up_proj_gated(const mla_dims* d, int32_t n_tok, const void* o_latent, const void* w_uv,
+                             const void* gate, void* out, mla_stream_t stream) {
+  if (n_tok > 0 && !gate) return MLA_ERR_INVALID_ARG;
+  return up_proj_common(d, n_tok, o_latent, w_uv, gate, out, stream);
 }
 
 size_t mla_prefill_workspace_bytes(const mla_dims* d, int32_t total_tokens) {
@@ -235,7 +250,7 @@ size_t mla_prefill_workspace_bytes(const mla_dims* d, int32_t total_tokens) {
 
 mla_status mla_prefill(const mla_dims* d, int32_t n_seq, const int32_t* cu_seqlens, int32_t total_tokens,
                        int32_t max_seqlen, const void* q_nope, const void* q_rope, const void* c_kv,
-                       const void* k_rope, const void* w_uk, const void* w_uv, void* workspace,
+                       const void* k_rope, const void* w_uk, const void* w_uv, const void* gate, void* workspace,
                        size_t workspace_bytes, void* out, float* lse, mla_stream_t stream) {
   const mla_status s = dims_supported(d);
   if (s != MLA_OK) return s;
@@ -250,10 +265,42 @@ mla_status mla_prefill(const mla_dims* d, int32_t n_seq, const int32_t* cu_seqle
   if (static_cast<int64_t>(n_seq) * d->n_heads * ((max_seqlen + 127) / 128) > 2147483647LL) return MLA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < prefill_workspace_bytes(*d, total_tokens)) return MLA_ERR_WORKSPACE;
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(c_kv) || !aligned16(k_rope) || !aligned16(w_uk) ||
-      !aligned16(w_uv) || !aligned16(workspace) || !aligned16(out))
+      !aligned16(w_uv) || !aligned16(workspace) || !aligned16(out) || (gate && !aligned16(gate)))
     return MLA_ERR_INVALID_ARG;
   return launch_prefill(*d, n_seq, cu_seqlens, total_tokens, max_seqlen, q_nope, q_rope, c_kv, k_rope, w_uk, w_uv,
-                        workspace, out, lse, static_cast<hipStream_t>(stream));
+                        gate, workspace, out, lse, static_cast<hipStream_t>(stream));
+}
+
+size_t mla_prefill_paged_workspace_bytes(const mla_dims* d, int32_t total_q, int32_t total_k) {
+  if (dims_supported(d) != MLA_OK || !prefill_supported(*d) || d->cache_dtype != MLA_BF16 || total_q < 0 ||
+      total_k < 0)
+    return 0;
+  return prefill_paged_workspace_bytes(*d, total_q, total_k);
+}
+
+mla_status mla_prefill_paged(const mla_dims* d, int32_t n_seq, const int32_t* cu_q, int32_t total_q, int32_t max_q,
+                             const int32_t* cu_k, int32_t total_k, const void* q_nope, const void* q_rope,
+                             const void* cache_pool, const int32_t* block_table, int32_t max_blocks,
+                             const void* w_uk, const void* w_uv, const void* gate, void* workspace,
+                             size_t workspace_bytes, void* out, float* lse, mla_stream_t stream) {
+  const mla_status s = dims_supported(d);
+  if (s != MLA_OK) return s;
+  if (!prefill_supported(*d) || d->cache_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (n_seq <= 0 || total_q < 0 || max_q < 0 || total_k < 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (total_q == 0) return MLA_OK;
+  if (!cu_q || !cu_k || !q_nope || !q_rope || !cache_pool || !block_table || !w_uk || !w_uv || !out || !lse)
+    return MLA_ERR_INVALID_ARG;
+  if (max_q == 0 || max_q > total_q || total_k < total_q) return MLA_ERR_INVALID_ARG;
+  // 32-bit index math: key tokens x heads x 128, the grid, block-table rows and pool rows
+  if (static_cast<int64_t>(total_k) * d->n_heads * 128 > 2147483647LL) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(n_seq) * d->n_heads * ((max_q + 127) / 128) > 2147483647LL) return MLA_ERR_UNSUPPORTED;
+  if (static_cast<int64_t>(max_blocks) * d->block_size > 2147483647LL) return MLA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < prefill_paged_workspace_bytes(*d, total_q, total_k)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(cache_pool) || !aligned16(w_uk) || !aligned16(w_uv) ||
+      !aligned16(workspace) || !aligned16(out) || (gate && !aligned16(gate)))
+    return MLA_ERR_INVALID_ARG;
+  return launch_prefill_paged(*d, n_seq, cu_q, total_q, max_q, cu_k, total_k, q_nope, q_rope, cache_pool, block_table,
+                              max_blocks, w_uk, w_uv, gate, workspace, out, lse, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -17,7 +17,7 @@ bool absorb_tuned_applies(const mla_dims& d);
 mla_status launch_absorb_tuned(const mla_dims& d, int32_t n_tok, const void* q_nope, const void* q_rope,
                                const int32_t* pos, const void* w_uk, void* q_abs, hipStream_t st);
 bool up_proj_tuned_applies(const mla_dims& d);
-mla_status launch_up_proj_tuned(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv, void* out,
-                                hipStream_t st);
+mla_status launch_up_proj_tuned(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv,
+                                const void* gate, void* out, hipStream_t st);
 
 }  // namespace mla

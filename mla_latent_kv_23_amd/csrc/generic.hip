@@ -262,11 +262,13 @@ __global__ void __launch_bounds__(256) combine_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// up-projection: out[t,s,v] = sum_c w_uv[s,v,c] o_lat[t,s,c]; grid (n_tok, H), block 256
+// up-projection: out[t,s,v] = sum_c w_uv[s,v,c] o_lat[t,s,c], times
+// sigmoid(gate[t,s,v]) when a gate is given; grid (n_tok, H), block 256
 // ----------------------------------------------------------------------------
 template <typename T>
-__global__ void __launch_bounds__(256) up_proj_generic_kernel(
-    const T* __restrict__ o_lat, const T* __restrict__ w_uv, T* __restrict__ out, int H, int d_c, int d_v) {
+__global__ void __launch_bounds__(256) up_proj_generic_kernel(const T* __restrict__ o_lat, const T* __restrict__ w_uv,
+                                                              const T* __restrict__ gate, T* __restrict__ out, int H,
+                                                              int d_c, int d_v) {
   extern __shared__ float sh_o[];           // d_c
   const int t = blockIdx.x, s = blockIdx.y;
   const int64_t row = static_cast<int64_t>(t) * H + s;
@@ -279,7 +281,10 @@ __global__ void __launch_bounds__(256) up_proj_generic_kernel(
     float a = 0.f;
     for (int c = lane; c < d_c; c += 64) a = fmaf(sh_o[c], Act<T>::ld(w, static_cast<int64_t>(v) * d_c + c), a);
     for (int off = 32; off > 0; off >>= 1) a += __shfl_xor(a, off, 64);
-    if (lane == 0) Act<T>::st(out, row * d_v + v, a);
+    if (lane == 0) {
+      if (gate) a *= sigmoid_f32(Act<T>::ld(gate, row * d_v + v));
+      Act<T>::st(out, row * d_v + v, a);
+    }
   }
 }
 
@@ -368,15 +373,15 @@ mla_status launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t n_s
 }
 
 mla_status launch_up_proj_generic(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv,
-                                  void* out, hipStream_t st) {
+                                  const void* gate, void* out, hipStream_t st) {
   dim3 grid(n_tok, d.n_heads);
   const size_t shm = sizeof(float) * d.d_c;
   if (d.act_dtype == MLA_F32)
     hipLaunchKernelGGL(up_proj_generic_kernel<float>, grid, dim3(256), shm, st, (const float*)o_lat,
-                       (const float*)w_uv, (float*)out, d.n_heads, d.d_c, d.d_v);
+                       (const float*)w_uv, (const float*)gate, (float*)out, d.n_heads, d.d_c, d.d_v);
   else
     hipLaunchKernelGGL(up_proj_generic_kernel<uint16_t>, grid, dim3(256), shm, st, (const uint16_t*)o_lat,
-                       (const uint16_t*)w_uv, (uint16_t*)out, d.n_heads, d.d_c, d.d_v);
+                       (const uint16_t*)w_uv, (const uint16_t*)gate, (uint16_t*)out, d.n_heads, d.d_c, d.d_v);
   return launch_status();
 }
 

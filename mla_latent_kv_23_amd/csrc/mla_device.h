@@ -22,6 +22,10 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) {
   return __uint_as_float(static_cast<uint32_t>(b) << 16);
 }
 
+// Logistic output gate sigma(g) = 1 / (1 + e^-g) in float32: 0 for g -> -inf
+// (e^-g overflows to inf), 1 for g -> +inf.
+__device__ __forceinline__ float sigmoid_f32(float g) { return 1.0f / (1.0f + expf(-g)); }
+
 // float32 -> bf16, round to nearest even; NaN stays NaN (quiet bit set).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
   uint32_t u = __float_as_uint(f);

@@ -75,11 +75,17 @@ mla_status launch_combine_stream(const mla_dims& d, const DecodePlan& plan, int3
                                  const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st);
 bool prefill_supported(const mla_dims& d);
 size_t prefill_workspace_bytes(const mla_dims& d, int64_t total_tokens);
+size_t prefill_paged_workspace_bytes(const mla_dims& d, int64_t total_q, int64_t total_k);
 mla_status launch_prefill(const mla_dims& d, int32_t n_seq, const int32_t* cu_seqlens, int32_t total_tokens,
                           int32_t max_seqlen, const void* q_nope, const void* q_rope, const void* c_kv,
-                          const void* k_rope, const void* w_uk, const void* w_uv, void* ws, void* out, float* lse,
-                          hipStream_t st);
+                          const void* k_rope, const void* w_uk, const void* w_uv, const void* gate, void* ws,
+                          void* out, float* lse, hipStream_t st);
+mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t* cu_q, int32_t total_q, int32_t max_q,
+                                const int32_t* cu_k, int32_t total_k, const void* q_nope, const void* q_rope,
+                                const void* cache_pool, const int32_t* block_table, int32_t max_blocks,
+                                const void* w_uk, const void* w_uv, const void* gate, void* ws, void* out, float* lse,
+                                hipStream_t st);
 mla_status launch_up_proj_generic(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv,
-                                  void* out, hipStream_t st);
+                                  const void* gate, void* out, hipStream_t st);
 
 }  // namespace mla

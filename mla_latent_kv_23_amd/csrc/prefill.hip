@@ -2,13 +2,20 @@
 // 双重投影, training/prefill column): every head attends with its own key
 // [k_C | k_R], k_C = W_UK[s] c (d_nope = 128) and k_R the shared rotated key
 // (d_R = 64), and its own value v = W_UV[s] c (d_v = 128); the query is
-// [q_nope | RoPE(q_R)].  Sequences are packed (cu_seqlens); token i of a
-// sequence sits at position i and attends to tokens 0..i.
+// [q_nope | RoPE(q_R)].  Queries and keys are packed per sequence (cu_q,
+// cu_k): with Lq queries and Lk keys, query j sits at position Lk - Lq + j and
+// attends to keys 0..Lk - Lq + j.  A whole prompt has Lq = Lk (query i at
+// position i); a chunk of a longer prompt attends to the cached prefix too.
+// The keys come either from packed c_KV / raw k_R rows (mla_prefill) or from
+// the paged latent cache (mla_prefill_paged), whose k_R rows are already
+// rotated.
 //
-// Three launches:
-//  1. prefill_rope_kernel: q_R' [T, H, 64] and k_R' [T, 64] in bf16, by the
-//     RoPE rule of the absorb and append kernels (fp64 angle, fp32 cos/sin,
-//     fp64 rotation, one rounding); cos/sin once per (token, pair).
+// Launches:
+//  1. prefill_rope_kernel: q_R' [Tq, H, 64] (and, for packed keys, k_R'
+//     [Tk, 64]) in bf16, by the RoPE rule of the absorb and append kernels
+//     (fp64 angle, fp32 cos/sin, fp64 rotation, one rounding); cos/sin once
+//     per (token, pair).  For paged keys, prefill_gather_kernel copies the
+//     cached k_R' rows and records each key's physical cache row.
 //  2. prefill_decompress_kernel: k_C [T, H, 128] and v [T, H, 128] in bf16, a
 //     bf16 MFMA GEMM with fp32 accumulation: a 128-dim x 128-token tile of one
 //     head per work-group, the 512-long contraction in chunks of 64 through LDS.
@@ -23,7 +30,9 @@
 //       swapped), so the weights never leave the wave;
 //     * online softmax in the exp2 domain with a lazy reference: the output is
 //       rescaled only when a query's running max rises by more than 2^8;
-//     * O^T += V^T P^T on MFMA, V^T from the staged rows by transpose reads.
+//     * O^T += V^T P^T on MFMA, V^T from the staged rows by transpose reads;
+//     * with an output gate (gated MLA), out = sigmoid(gate) * o before the
+//       one rounding to bf16.
 #include "decode_tile.h"
 
 namespace mla {
@@ -33,23 +42,32 @@ constexpr int kPfDc = 512, kPfDn = 128, kPfDr = 64, kPfDv = 128;
 
 // ---------------------------------------------------------------- 1. RoPE
 
+// the sequence holding packed token t: the last b with cu[b] <= t
+__device__ __forceinline__ int pf_seq_of(const int32_t* __restrict__ cu, int n_seq, int t) {
+  int lo = 0, hi = n_seq;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= t) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
+// grid Tq (one work-group per query token).  k_rope non-null (packed keys,
+// cu_k == cu_q): the key of the same token is rotated too.
 __global__ void __launch_bounds__(256) prefill_rope_kernel(const uint16_t* __restrict__ q_rope,
                                                            const uint16_t* __restrict__ k_rope,
-                                                           const int32_t* __restrict__ cu, int n_seq, int H,
+                                                           const int32_t* __restrict__ cu_q,
+                                                           const int32_t* __restrict__ cu_k, int n_seq, int H,
                                                            uint16_t* __restrict__ qr_out, uint16_t* __restrict__ kr_out,
                                                            RopeFreqs f) {
   __shared__ float s_cs[kPfDr / 2], s_sn[kPfDr / 2];
   const int t = blockIdx.x, tid = threadIdx.x;
   if (tid < kPfDr / 2) {
-    // the sequence holding token t: the last b with cu[b] <= t
-    int lo = 0, hi = n_seq;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (cu[mid] <= t) lo = mid;
-      else hi = mid;
-    }
+    const int b = pf_seq_of(cu_q, n_seq, t);
+    const int pos = (t - cu_q[b]) + (cu_k[b + 1] - cu_k[b]) - (cu_q[b + 1] - cu_q[b]);
     float cs, sn;
-    rope_cos_sin(t - cu[lo], f.inv_freq[tid], &cs, &sn);
+    rope_cos_sin(pos, f.inv_freq[tid], &cs, &sn);
     s_cs[tid] = cs;
     s_sn[tid] = sn;
   }
@@ -63,7 +81,7 @@ __global__ void __launch_bounds__(256) prefill_rope_kernel(const uint16_t* __res
               &oy);
     *(uint32_t*)(qr_out + at) = (uint32_t)f32_to_bf16_bits(ox) | ((uint32_t)f32_to_bf16_bits(oy) << 16);
   }
-  if (tid < kPfDr / 2) {
+  if (k_rope && tid < kPfDr / 2) {
     const int64_t at = (int64_t)t * kPfDr + 2 * tid;
     const uint32_t x2 = *(const uint32_t*)(k_rope + at);
     float ox, oy;
@@ -71,6 +89,26 @@ __global__ void __launch_bounds__(256) prefill_rope_kernel(const uint16_t* __res
               s_sn[tid], &ox, &oy);
     *(uint32_t*)(kr_out + at) = (uint32_t)f32_to_bf16_bits(ox) | ((uint32_t)f32_to_bf16_bits(oy) << 16);
   }
+}
+
+// Paged keys: one thread per (key token, 16-byte piece of k_R'): the physical
+// cache row of key t (block_table[b][p / block_size] * block_size + p % block_size,
+// p its position) goes to rowmap[t], and its rotated k_R (bf16, the last d_R
+// entries of the row) is copied to kr_out[t].
+__global__ void __launch_bounds__(256) prefill_gather_kernel(const uint16_t* __restrict__ pool,
+                                                             const int32_t* __restrict__ block_table, int max_blocks,
+                                                             int block_size, const int32_t* __restrict__ cu_k,
+                                                             int n_seq, int total_k, int32_t* __restrict__ rowmap,
+                                                             uint16_t* __restrict__ kr_out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int t = i >> 3, piece = i & 7;
+  if (t >= total_k) return;
+  const int b = pf_seq_of(cu_k, n_seq, t);
+  const int p = t - cu_k[b];
+  const int row = block_table[(int64_t)b * max_blocks + p / block_size] * block_size + p % block_size;
+  if (piece == 0) rowmap[t] = row;
+  *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * piece) =
+      *(const u32x4*)(pool + (int64_t)row * (kPfDc + kPfDr) + kPfDc + 8 * piece);
 }
 
 // ---------------------------------------------------------------- 2. decompression
@@ -90,7 +128,10 @@ __device__ __forceinline__ u32x2 pf_pack4(float a, float b, float c, float d) {
 // grid (ceil(T / 128), H, 2): z = 0 writes k_C with W_UK, z = 1 writes v with W_UV.
 // out^T tile (128 dims x 128 tokens) = W[s] (dims x 512) c^T (512 x tokens);
 // wave w computes dims 64(w % 2) .. +63 x tokens 64(w / 2) .. +63 (2 x 2 MFMA tiles).
-__global__ void __launch_bounds__(256) prefill_decompress_kernel(const uint16_t* __restrict__ c_kv,
+// The latent of key t is row (rowmap ? rowmap[t] : t) of c_rows, c_stride
+// elements apart (packed c_KV, or the rows of the paged cache).
+__global__ void __launch_bounds__(256) prefill_decompress_kernel(const uint16_t* __restrict__ c_rows,
+                                                                 const int32_t* __restrict__ rowmap, int c_stride,
                                                                  const uint16_t* __restrict__ w_uk,
                                                                  const uint16_t* __restrict__ w_uv,
                                                                  uint16_t* __restrict__ kc, uint16_t* __restrict__ vv,
@@ -104,14 +145,20 @@ __global__ void __launch_bounds__(256) prefill_decompress_kernel(const uint16_t*
   const int wm = wave & 1, wn = wave >> 1;
 
   // staging: piece p = tid + 256 j (j < 4) is 16 bytes, row p / 8, part p % 8 of the chunk
+  const uint16_t* csrc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int p = tid + 256 * j, row = p >> 3, part = p & 7;
+    const int t = min(t0 + row, T - 1);
+    csrc[j] = c_rows + (int64_t)(rowmap ? rowmap[t] : t) * c_stride + 8 * part;
+  }
   u32x4 wreg[4], creg[4];
   auto load_chunk = [&](int kc0) {
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int p = tid + 256 * j, row = p >> 3, part = p & 7;
       wreg[j] = *(const u32x4*)(W + (int64_t)row * kPfDc + kc0 + 8 * part);
-      const int t = min(t0 + row, T - 1);
-      creg[j] = *(const u32x4*)(c_kv + (int64_t)t * kPfDc + kc0 + 8 * part);
+      creg[j] = *(const u32x4*)(csrc[j] + kc0);
     }
   };
   auto store_chunk = [&](int buf) {
@@ -187,10 +234,12 @@ struct PrefillArgs {
   const uint16_t* k_c;        // [T][H][128]
   const uint16_t* k_rot;      // [T][64] rotated
   const uint16_t* v;          // [T][H][128]
-  const int32_t* cu;          // [n_seq + 1]
-  uint16_t* out;              // [T][H][128]
-  float* lse;                 // [T][H]
-  int n_seq, H, n_qblk;       // n_qblk = ceil(max_seqlen / 128)
+  const int32_t* cu_q;        // [n_seq + 1] query offsets
+  const int32_t* cu_k;        // [n_seq + 1] key offsets
+  const uint16_t* gate;       // [Tq][H][128] output-gate logits, or null
+  uint16_t* out;              // [Tq][H][128]
+  float* lse;                 // [Tq][H]
+  int n_seq, H, n_qblk;       // n_qblk = ceil(max query length / 128)
   float scale_log2;
 };
 
@@ -223,11 +272,13 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
   const int k = xcd_unit(blockIdx.x, total);
   const int pair = k / a.n_qblk, qb = a.n_qblk - 1 - k % a.n_qblk;
   const int b = pair / H, s = pair % H;
-  const int cu0 = a.cu[b], L = a.cu[b + 1] - cu0;
+  const int cu0 = a.cu_q[b], Lq = a.cu_q[b + 1] - cu0;
+  const int ck0 = a.cu_k[b], L = a.cu_k[b + 1] - ck0;  // L keys; query j sits at position off + j
+  const int off = L - Lq;
   const int q0 = qb * kQBlk;
-  if (q0 >= L) return;
+  if (q0 >= Lq) return;
   const int qw = q0 + 32 * wave;                       // this wave's first query
-  const int q = min(qw + lr, L - 1);                   // this lane's query (past the end: a copy of the last)
+  const int q = min(qw + lr, Lq - 1);                  // this lane's query (past the end: a copy of the last)
 
   // queries: B operand, query q, dims 16k + 8 half .. +7 (k < 8: q_nope, else the rotated part)
   bf16x8 qf[kQk];
@@ -264,12 +315,12 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
 
   // stage loads: wave w brings rows 16w .. 16w+15 of the block, five 1 KB
   // blocks per 8 rows; lane l: row 16w + 8g + l/8, logical chunk 8cb + ((l % 8) ^ swz(l / 8))
-  const int last_key = min(L, q0 + kQBlk) - 1;
+  const int last_key = min(L, off + q0 + kQBlk) - 1;
   const int n_kblk = last_key / kKBlk + 1;
   auto load_stage = [&](int kbk) {
     const uint32_t dst = (uint32_t)(uintptr_t)(lds + (kbk & 1) * kStage);
     const int key0 = kbk * kKBlk;
-    const int64_t row0 = cu0 + key0;
+    const int64_t row0 = ck0 + key0;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
       const int r = 16 * wave + 8 * g + (lane >> 3);
@@ -321,13 +372,13 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int i = 0; i < 16; ++i) sv[t][i] = sacc[t][i];
-    if (kbk * kKBlk + kKBlk - 1 > qw) {      // a block reaching this wave's diagonal (wave-uniform)
+    if (kbk * kKBlk + kKBlk - 1 > off + qw) {   // a block reaching this wave's diagonal (wave-uniform)
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
           const int key = kbk * kKBlk + 32 * t + 16 * (i / 8) + 8 * half + (i % 8);
-          sv[t][i] = key <= q ? sv[t][i] : -INFINITY;
+          sv[t][i] = key <= off + q ? sv[t][i] : -INFINITY;
         }
     }
     float bmax = sv[0][0];
@@ -390,9 +441,23 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
     l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
   }
-  if (qw + lr < L) {
+  if (qw + lr < Lq) {
     const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    uint16_t* dst = a.out + ((int64_t)(cu0 + qw + lr) * H + s) * kPfDv + 4 * half;
+    const int64_t at = ((int64_t)(cu0 + qw + lr) * H + s) * kPfDv + 4 * half;
+    uint16_t* dst = a.out + at;
+    if (a.gate) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const u32x2 g4 = *(const u32x2*)(a.gate + at + 32 * db + 8 * g);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const uint32_t w2 = g4[e >> 1];
+            o[db][4 * g + e] *= sigmoid_f32(__uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16)));
+          }
+        }
+    }
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -410,49 +475,96 @@ bool prefill_supported(const mla_dims& d) {
   return d.act_dtype == MLA_BF16 && d.d_c == kPfDc && d.d_nope == kPfDn && d.d_rope == kPfDr && d.d_v == kPfDv;
 }
 
-size_t prefill_workspace_bytes(const mla_dims& d, int64_t total_tokens) {
-  // k_C, v [T][H][128], q_R' [T][H][64], k_R' [T][64], bf16 each, 256-byte aligned pieces
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t T = (size_t)total_tokens, H = (size_t)d.n_heads;
-  return up(T * H * kPfDn * 2) + up(T * H * kPfDv * 2) + up(T * H * kPfDr * 2) + up(T * kPfDr * 2);
+namespace {
+size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// workspace: k_C, v [Tk][H][128], q_R' [Tq][H][64], k_R' [Tk][64] (bf16), then,
+// for paged keys, the key row map [Tk] (int32); 256-byte aligned pieces
+struct PrefillWs {
+  uint16_t *kc, *vv, *qr, *kr;
+  int32_t* rowmap;
+};
+size_t prefill_ws_bytes(int64_t tq, int64_t tk, int64_t H, bool paged) {
+  return up256(tk * H * kPfDn * 2) + up256(tk * H * kPfDv * 2) + up256(tq * H * kPfDr * 2) + up256(tk * kPfDr * 2) +
+         (paged ? up256(tk * 4) : 0);
+}
+PrefillWs carve(void* ws, int64_t tq, int64_t tk, int64_t H) {
+  uint8_t* p = static_cast<uint8_t*>(ws);
+  PrefillWs w;
+  w.kc = reinterpret_cast<uint16_t*>(p);
+  p += up256(tk * H * kPfDn * 2);
+  w.vv = reinterpret_cast<uint16_t*>(p);
+  p += up256(tk * H * kPfDv * 2);
+  w.qr = reinterpret_cast<uint16_t*>(p);
+  p += up256(tq * H * kPfDr * 2);
+  w.kr = reinterpret_cast<uint16_t*>(p);
+  p += up256(tk * kPfDr * 2);
+  w.rowmap = reinterpret_cast<int32_t*>(p);
+  return w;
 }
 
-mla_status launch_prefill(const mla_dims& d, int32_t n_seq, const int32_t* cu_seqlens, int32_t total_tokens,
-                          int32_t max_seqlen, const void* q_nope, const void* q_rope, const void* c_kv,
-                          const void* k_rope, const void* w_uk, const void* w_uv, void* ws, void* out, float* lse,
-                          hipStream_t st) {
-  auto up = [](size_t x) { return (x + 255) & ~(size_t)255; };
-  const size_t T = (size_t)total_tokens, H = (size_t)d.n_heads;
-  uint8_t* p = static_cast<uint8_t*>(ws);
-  uint16_t* kc = reinterpret_cast<uint16_t*>(p);
-  p += up(T * H * kPfDn * 2);
-  uint16_t* vv = reinterpret_cast<uint16_t*>(p);
-  p += up(T * H * kPfDv * 2);
-  uint16_t* qr = reinterpret_cast<uint16_t*>(p);
-  p += up(T * H * kPfDr * 2);
-  uint16_t* kr = reinterpret_cast<uint16_t*>(p);
-
-  const RopeFreqs f = make_rope_freqs(d);
-  hipLaunchKernelGGL(prefill_rope_kernel, dim3(total_tokens), dim3(256), 0, st, static_cast<const uint16_t*>(q_rope),
-                     static_cast<const uint16_t*>(k_rope), cu_seqlens, n_seq, d.n_heads, qr, kr, f);
-  hipLaunchKernelGGL(prefill_decompress_kernel, dim3((total_tokens + kDcTok - 1) / kDcTok, d.n_heads, 2), dim3(256), 0,
-                     st, static_cast<const uint16_t*>(c_kv), static_cast<const uint16_t*>(w_uk),
-                     static_cast<const uint16_t*>(w_uv), kc, vv, total_tokens, d.n_heads);
+void launch_attention(const mla_dims& d, int32_t n_seq, const int32_t* cu_q, const int32_t* cu_k, int32_t max_q,
+                      const void* q_nope, const PrefillWs& w, const void* gate, void* out, float* lse,
+                      hipStream_t st) {
   PrefillArgs a;
   a.q_nope = static_cast<const uint16_t*>(q_nope);
-  a.q_rot = qr;
-  a.k_c = kc;
-  a.k_rot = kr;
-  a.v = vv;
-  a.cu = cu_seqlens;
+  a.q_rot = w.qr;
+  a.k_c = w.kc;
+  a.k_rot = w.kr;
+  a.v = w.vv;
+  a.cu_q = cu_q;
+  a.cu_k = cu_k;
+  a.gate = static_cast<const uint16_t*>(gate);
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
   a.n_seq = n_seq;
   a.H = d.n_heads;
-  a.n_qblk = (max_seqlen + kQBlk - 1) / kQBlk;
+  a.n_qblk = (max_q + kQBlk - 1) / kQBlk;
   a.scale_log2 = d.softmax_scale * 1.4426950408889634f;
   const int64_t grid = (int64_t)n_seq * d.n_heads * a.n_qblk;
   hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)grid), dim3(256), 0, st, a);
+}
+}  // namespace
+
+size_t prefill_workspace_bytes(const mla_dims& d, int64_t total_tokens) {
+  return prefill_ws_bytes(total_tokens, total_tokens, d.n_heads, false);
+}
+
+size_t prefill_paged_workspace_bytes(const mla_dims& d, int64_t total_q, int64_t total_k) {
+  return prefill_ws_bytes(total_q, total_k, d.n_heads, true);
+}
+
+mla_status launch_prefill(const mla_dims& d, int32_t n_seq, const int32_t* cu_seqlens, int32_t total_tokens,
+                          int32_t max_seqlen, const void* q_nope, const void* q_rope, const void* c_kv,
+                          const void* k_rope, const void* w_uk, const void* w_uv, const void* gate, void* ws,
+                          void* out, float* lse, hipStream_t st) {
+  const PrefillWs w = carve(ws, total_tokens, total_tokens, d.n_heads);
+  const RopeFreqs f = make_rope_freqs(d);
+  hipLaunchKernelGGL(prefill_rope_kernel, dim3(total_tokens), dim3(256), 0, st, static_cast<const uint16_t*>(q_rope),
+                     static_cast<const uint16_t*>(k_rope), cu_seqlens, cu_seqlens, n_seq, d.n_heads, w.qr, w.kr, f);
+  hipLaunchKernelGGL(prefill_decompress_kernel, dim3((total_tokens + kDcTok - 1) / kDcTok, d.n_heads, 2), dim3(256), 0,
+                     st, static_cast<const uint16_t*>(c_kv), nullptr, kPfDc, static_cast<const uint16_t*>(w_uk),
+                     static_cast<const uint16_t*>(w_uv), w.kc, w.vv, total_tokens, d.n_heads);
+  launch_attention(d, n_seq, cu_seqlens, cu_seqlens, max_seqlen, q_nope, w, gate, out, lse, st);
+  return launch_status();
+}
+
+mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t* cu_q, int32_t total_q, int32_t max_q,
+                                const int32_t* cu_k, int32_t total_k, const void* q_nope, const void* q_rope,
+                                const void* cache_pool, const int32_t* block_table, int32_t max_blocks,
+                                const void* w_uk, const void* w_uv, const void* gate, void* ws, void* out, float* lse,
+                                hipStream_t st) {
+  const PrefillWs w = carve(ws, total_q, total_k, d.n_heads);
+  const RopeFreqs f = make_rope_freqs(d);
+  const uint16_t* pool = static_cast<const uint16_t*>(cache_pool);
+  hipLaunchKernelGGL(prefill_rope_kernel, dim3(total_q), dim3(256), 0, st, static_cast<const uint16_t*>(q_rope),
+                     nullptr, cu_q, cu_k, n_seq, d.n_heads, w.qr, nullptr, f);
+  hipLaunchKernelGGL(prefill_gather_kernel, dim3((unsigned)(((int64_t)total_k * 8 + 255) / 256)), dim3(256), 0, st,
+                     pool, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k, w.rowmap, w.kr);
+  hipLaunchKernelGGL(prefill_decompress_kernel, dim3((total_k + kDcTok - 1) / kDcTok, d.n_heads, 2), dim3(256), 0, st,
+                     pool, w.rowmap, kPfDc + kPfDr, static_cast<const uint16_t*>(w_uk),
+                     static_cast<const uint16_t*>(w_uv), w.kc, w.vv, total_k, d.n_heads);
+  launch_attention(d, n_seq, cu_q, cu_k, max_q, q_nope, w, gate, out, lse, st);
   return launch_status();
 }
 

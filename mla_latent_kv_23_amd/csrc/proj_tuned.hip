@@ -179,9 +179,12 @@ __global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __res
 // 128w .. 128w+127 for all d_v/32 output-row blocks of the block's 32 tokens
 // (all its operands are loaded up front), writes its fp32 partial tiles to
 // LDS, and after the barrier finishes output-row block w by summing the four
-// partials in a fixed order.
+// partials in a fixed order.  kGate: the fp32 result is multiplied by
+// sigmoid(gate) of the same element before its one rounding to bf16.
+template <bool kGate>
 __global__ void __launch_bounds__(256) up_proj_tuned_kernel(const uint16_t* __restrict__ o_lat,
                                                             const uint16_t* __restrict__ w_uv,
+                                                            const uint16_t* __restrict__ gate,
                                                             uint16_t* __restrict__ out, int n_tok, int H) {
   constexpr int kVb = kUpDv / 32;                    // 4 output-row blocks
   constexpr int kSlice = kUpDc / 4;                  // latent dims per wave
@@ -198,6 +201,13 @@ __global__ void __launch_bounds__(256) up_proj_tuned_kernel(const uint16_t* __re
   bf16x8 bf[kSteps];
 #pragma unroll
   for (int ks = 0; ks < kSteps; ++ks) bf[ks] = bsrc[2 * ks];
+  // this lane's gate logits: output rows 32 w + 8 g + 4 half .. +3 of token t
+  u32x2 graw[4];
+  if constexpr (kGate) {
+    const uint16_t* gsrc = gate + ((int64_t)tc * H + s) * kUpDv + 32 * wave + 4 * half;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) graw[g] = *(const u32x2*)(gsrc + 8 * g);
+  }
   bf16x8 af[kVb][kSteps];
 #pragma unroll
   for (int vb = 0; vb < kVb; ++vb) {
@@ -227,6 +237,15 @@ __global__ void __launch_bounds__(256) up_proj_tuned_kernel(const uint16_t* __re
     for (int w2 = 1; w2 < 4; ++w2) x += red[((w2 * kVb + wave) * 16 + i) * 64 + lane];
     v[i] = x;
   }
+  if constexpr (kGate) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t w2 = graw[g][e >> 1];
+        v[4 * g + e] *= sigmoid_f32(__uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16)));
+      }
+  }
   if (t < n_tok) {
     uint16_t* dst = out + ((int64_t)t * H + s) * kUpDv + 32 * wave + 4 * half;
 #pragma unroll
@@ -254,11 +273,16 @@ bool up_proj_tuned_applies(const mla_dims& d) {
   return d.act_dtype == MLA_BF16 && d.d_c == kUpDc && d.d_v == kUpDv;
 }
 
-mla_status launch_up_proj_tuned(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv, void* out,
-                                hipStream_t st) {
+mla_status launch_up_proj_tuned(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv,
+                                const void* gate, void* out, hipStream_t st) {
   dim3 grid(d.n_heads, (n_tok + 31) / 32);
-  hipLaunchKernelGGL(up_proj_tuned_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(o_lat),
-                     static_cast<const uint16_t*>(w_uv), static_cast<uint16_t*>(out), n_tok, d.n_heads);
+  if (gate)
+    hipLaunchKernelGGL(up_proj_tuned_kernel<true>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(o_lat),
+                       static_cast<const uint16_t*>(w_uv), static_cast<const uint16_t*>(gate),
+                       static_cast<uint16_t*>(out), n_tok, d.n_heads);
+  else
+    hipLaunchKernelGGL(up_proj_tuned_kernel<false>, grid, dim3(256), 0, st, static_cast<const uint16_t*>(o_lat),
+                       static_cast<const uint16_t*>(w_uv), nullptr, static_cast<uint16_t*>(out), n_tok, d.n_heads);
   return launch_status();
 }
 

@@ -29,8 +29,9 @@ class DecodeStep:
         self.needs_combine = B.decode_needs_combine(dims, n_seq, q_per_seq, max_blocks, num_splits)
 
     def run(self, *, q_nope, q_rope, q_pos, new_c_kv, new_k_rope, new_seq_id, new_pos, block_table, seqlens,
-            pool, w_uk, w_uv, stream=None):
-        """q_nope/q_rope [n_seq*q_per_seq, H, *]; q_pos [n_seq*q_per_seq]; new_* the tokens to append."""
+            pool, w_uk, w_uv, gate=None, stream=None):
+        """q_nope/q_rope [n_seq*q_per_seq, H, *]; q_pos [n_seq*q_per_seq]; new_* the tokens to append;
+        gate [n_seq*q_per_seq, H, d_v] (optional): output-gate logits of gated MLA."""
         d = self.d
         n_tok = self.n_seq * self.q_per_seq
         B.absorb_q(d, q_nope, q_rope, q_pos, w_uk, q_abs=self.q_abs.view(n_tok, d.n_heads, -1), stream=stream)
@@ -41,5 +42,5 @@ class DecodeStep:
         if self.needs_combine:
             B.combine(d, seqlens, self.max_blocks, self.workspace, self.o_latent, self.lse, self.num_splits,
                       stream=stream)
-        B.up_proj(d, self.o_latent.view(n_tok, d.n_heads, d.d_c), w_uv, out=self.out, stream=stream)
+        B.up_proj(d, self.o_latent.view(n_tok, d.n_heads, d.d_c), w_uv, out=self.out, stream=stream, gate=gate)
         return self.out, self.o_latent, self.lse

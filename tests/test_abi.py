@@ -69,6 +69,8 @@ def test_invalid_arguments_are_rejected(lib):
     assert lib.mla_append_cache(r, 4, FAKE, FAKE, FAKE, FAKE, None, 1, 1, FAKE, 1, None) == 1
     assert lib.mla_decode(r, 1, 1, FAKE, FAKE, FAKE, 1, None, 0, None, 0, FAKE, FAKE, None) == 1
     assert lib.mla_up_proj(r, 4, FAKE, None, FAKE, None) == 1
+    assert lib.mla_up_proj_gated(r, 4, FAKE, FAKE, None, FAKE, None) == 1   # the gate is required
+    assert lib.mla_up_proj_gated(r, 4, FAKE, None, FAKE, FAKE, None) == 1
     assert lib.mla_combine(r, 1, 1, None, 1, 0, FAKE, 0, FAKE, FAKE, None) == 1
     # sizes
     assert lib.mla_absorb_q(r, -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
@@ -99,6 +101,7 @@ def test_empty_calls_do_nothing(lib):
     assert lib.mla_absorb_q(r, 0, None, None, None, None, None, None) == 0
     assert lib.mla_append_cache(r, 0, None, None, None, None, None, 1, 1, None, 1, None) == 0
     assert lib.mla_up_proj(r, 0, None, None, None, None) == 0
+    assert lib.mla_up_proj_gated(r, 0, None, None, None, None, None) == 0
 
 
 def test_workspace_size_is_checked_before_launch(lib):
@@ -113,3 +116,48 @@ def test_workspace_size_is_checked_before_launch(lib):
     # one split: no partials, no workspace, nothing for combine to do
     assert lib.mla_decode_workspace_bytes(r, 1, 1, 64, 1) == 0
     assert lib.mla_decode_needs_combine(r, 1, 1, 64, 1) == 0
+
+
+def test_prefill_arguments_are_checked_before_launch(lib):
+    d = M.make_dims(**V3)
+    r = ctypes.byref(d)
+    ws = lib.mla_prefill_workspace_bytes(r, 100)
+    assert ws > 0
+    # mla_prefill(dims, n_seq, cu, T, max_len, q_nope, q_rope, c_kv, k_rope, w_uk, w_uv, gate, ws, ws_bytes, out, lse, stream)
+    args = [r, 1, FAKE, 100, 100, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws, FAKE, FAKE, None]
+    bad = list(args); bad[6] = None                       # q_rope missing
+    assert lib.mla_prefill(*bad) == 1
+    bad = list(args); bad[4] = 101                        # max_len above the token count
+    assert lib.mla_prefill(*bad) == 1
+    bad = list(args); bad[13] = ws - 1                    # workspace too small
+    assert lib.mla_prefill(*bad) == 3
+    bad = list(args); bad[11] = ctypes.c_void_p(0x1002)   # misaligned gate
+    assert lib.mla_prefill(*bad) == 1
+    bad = list(args); bad[3] = 0                          # nothing to do
+    assert lib.mla_prefill(*bad) == 0
+    f32 = M.make_dims(n_heads=4, d_c=64, d_rope=16, d_nope=32, d_v=32, act_dtype="f32", cache_dtype="f32")
+    assert lib.mla_prefill_workspace_bytes(ctypes.byref(f32), 10) == 0
+    assert lib.mla_prefill(ctypes.byref(f32), *args[1:]) == 2
+
+
+def test_prefill_paged_arguments_are_checked_before_launch(lib):
+    d = M.make_dims(**V3)
+    r = ctypes.byref(d)
+    ws = lib.mla_prefill_paged_workspace_bytes(r, 50, 400)
+    assert ws > lib.mla_prefill_workspace_bytes(r, 50)
+    # (dims, n_seq, cu_q, Tq, max_q, cu_k, Tk, q_nope, q_rope, pool, table, max_blocks, w_uk, w_uv, gate,
+    #  ws, ws_bytes, out, lse, stream)
+    args = [r, 2, FAKE, 50, 40, FAKE, 400, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None, FAKE, ws, FAKE, FAKE, None]
+    bad = list(args); bad[10] = None                      # block table missing
+    assert lib.mla_prefill_paged(*bad) == 1
+    bad = list(args); bad[6] = 49                         # fewer cached tokens than queries
+    assert lib.mla_prefill_paged(*bad) == 1
+    bad = list(args); bad[11] = 0                         # no blocks
+    assert lib.mla_prefill_paged(*bad) == 1
+    bad = list(args); bad[16] = ws - 1
+    assert lib.mla_prefill_paged(*bad) == 3
+    bad = list(args); bad[3] = 0
+    assert lib.mla_prefill_paged(*bad) == 0
+    fp8 = M.make_dims(**V3, cache_dtype="fp8")
+    assert lib.mla_prefill_paged_workspace_bytes(ctypes.byref(fp8), 50, 400) == 0
+    assert lib.mla_prefill_paged(ctypes.byref(fp8), *args[1:]) == 2

@@ -107,6 +107,36 @@ def test_up_proj(name, cuda_device):
 
 
 @pytest.mark.parametrize("name", NAMES)
+@pytest.mark.parametrize("aligned", [True, False])
+def test_up_proj_gated(name, aligned, cuda_device):
+    """Gated MLA: the up-projection times sigmoid(gate), one rounding.  The
+    unaligned gate (2 bytes past a 16-byte boundary) takes the generic kernel."""
+    import mla_latent_kv_23_amd as M
+    w, inp = _inputs(name)
+    U.say(f"[up_proj_gated] {name} aligned={aligned}")
+    d = U.dims_of(w)
+    r = np.random.default_rng(6)
+    n_tok = 37
+    o_lat = U.to_act(r.standard_normal((n_tok, w.n_heads, w.d_c)) * 0.1, w.act_dtype, cuda_device)
+    g = r.standard_normal((n_tok, w.n_heads, w.d_v)) * 3
+    g[0, 0, :4] = [60.0, -60.0, 200.0, -200.0]   # saturated gates
+    g[-1, -1, -2:] = [0.0, -0.0]
+    gate = U.to_act(g, w.act_dtype, cuda_device)
+    if not aligned:
+        buf = torch.empty(gate.numel() + 8, dtype=gate.dtype, device=cuda_device)
+        buf[1:1 + gate.numel()] = gate.reshape(-1)
+        gate = buf[1:1 + gate.numel()].view(gate.shape)
+    got = M.up_proj(d, o_lat, inp["w_uv"].to(cuda_device), gate=gate)
+    want = O.output_gate(O.up_proj(o_lat.double().cpu().numpy(), inp["w_uv"].double().numpy()),
+                         gate.double().cpu().numpy())
+    U.assert_close(got, want, w.act_dtype, "gated out")
+    # gate 60 passes the element, -60 closes it
+    ungated = M.up_proj(d, o_lat, inp["w_uv"].to(cuda_device))
+    assert torch.equal(got[0, 0, 0], ungated[0, 0, 0])
+    assert got[0, 0, 1].item() == 0.0 or abs(got[0, 0, 1].item()) < 1e-20
+
+
+@pytest.mark.parametrize("name", NAMES)
 def test_chain_vs_non_absorbed_oracle(name, cuda_device):
     """absorb -> append (the new tokens) -> decode -> combine -> up_proj, against the
     oracle's MHA form, which decompresses K and V per head explicitly."""

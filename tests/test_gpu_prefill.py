@@ -45,3 +45,84 @@ def test_prefill_rejects_unsupported_dims(cuda_device):
     w = S.WORKLOADS["tiny_fp32"]
     d = U.dims_of(w)
     assert M.prefill_workspace_bytes(d, 10) == 0
+
+
+@pytest.mark.parametrize("heads,lens,qlens", [
+    (16, [1000, 129, 64, 300], [70, 1, 64, 300]),    # prefix + chunk, one query, one whole block, whole prompt
+    (128, [700, 200], [200, 33]),
+    (16, [5000, 77], [129, 0]),                       # a sequence with no queries
+])
+def test_prefill_paged_matches_oracle(heads, lens, qlens, cuda_device):
+    """Chunked prefill: each sequence's newest tokens (already in the paged cache,
+    written by the library's append) attend to the whole cached prompt."""
+    import mla_latent_kv_23_amd as M
+    w = V3.replace(n_heads=heads)
+    inp = S.make_chunk_prefill_inputs(w, 600 + heads + len(lens), torch.tensor(lens, dtype=torch.int32),
+                                      torch.tensor(qlens, dtype=torch.int32))
+    U.say(f"[prefill_paged] H={heads} lens={lens} qlens={qlens}")
+    d = U.dims_of(w)
+    dev = cuda_device
+    pool = U.gpu_pool(w, inp, dev)
+    out, lse, _ = M.prefill_paged(d, inp["q_nope"].to(dev), inp["q_rope"].to(dev), inp["cu_q"].to(dev), max(qlens),
+                                  inp["cu_k"].to(dev), sum(lens), pool, inp["block_table"].to(dev),
+                                  inp["w_uk"].to(dev), inp["w_uv"].to(dev))
+    torch.cuda.synchronize()
+    heads_chk = list(range(heads)) if heads <= 16 else [0, 5, 64, 127]
+    cu_q, cu_k = inp["cu_q"].tolist(), inp["cu_k"].tolist()
+    for b, (L, Lq) in enumerate(zip(lens, qlens)):
+        if Lq == 0:
+            continue
+        ks, qs = slice(cu_k[b], cu_k[b] + L), slice(cu_q[b], cu_q[b] + Lq)
+        c, kr = O.cached_token_values(inp["c_kv"][ks].double().numpy(), inp["k_rope"][ks].double().numpy(),
+                                      np.arange(L), w.cache_dtype, w.rope_base)
+        want_o, want_lse = O.prefill_chunk_mha_form(inp["q_nope"][qs].double().numpy(),
+                                                    inp["q_rope"][qs].double().numpy(), c, kr,
+                                                    inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
+                                                    w.softmax_scale, w.rope_base, heads=heads_chk,
+                                                    operand_dtype="bf16")
+        U.assert_close(out[qs][:, heads_chk], want_o, "bf16", f"out seq {b} L={L} Lq={Lq}")
+        U.assert_close(lse[qs][:, heads_chk], want_lse, "bf16", f"lse seq {b} L={L} Lq={Lq}")
+
+
+@pytest.mark.parametrize("paged", [False, True])
+def test_prefill_output_gate(paged, cuda_device):
+    """Gated MLA in prefill: out = sigmoid(gate) * o against the oracle's gated
+    prefill; lse is the ungated one."""
+    import mla_latent_kv_23_amd as M
+    w = V3.replace(n_heads=16)
+    lens, qlens, dev = [300, 45], [100, 45], cuda_device
+    d = U.dims_of(w)
+    U.say(f"[prefill_gate] paged={paged}")
+    if paged:
+        inp = S.make_chunk_prefill_inputs(w, 700, torch.tensor(lens, dtype=torch.int32),
+                                          torch.tensor(qlens, dtype=torch.int32))
+        pool = U.gpu_pool(w, inp, dev)
+        gate = S.make_gate_logits(w, 701, sum(qlens))
+        out, lse, _ = M.prefill_paged(d, inp["q_nope"].to(dev), inp["q_rope"].to(dev), inp["cu_q"].to(dev),
+                                      max(qlens), inp["cu_k"].to(dev), sum(lens), pool, inp["block_table"].to(dev),
+                                      inp["w_uk"].to(dev), inp["w_uv"].to(dev), gate=gate.to(dev))
+        cu_q, cu_k = inp["cu_q"].tolist(), inp["cu_k"].tolist()
+    else:
+        inp = S.make_prefill_inputs(w, 702, torch.tensor(lens, dtype=torch.int32))
+        gate = S.make_gate_logits(w, 703, sum(lens))
+        out, lse, _ = M.prefill(d, inp["q_nope"].to(dev), inp["q_rope"].to(dev), inp["c_kv"].to(dev),
+                                inp["k_rope"].to(dev), inp["cu_seqlens"].to(dev), max(lens), inp["w_uk"].to(dev),
+                                inp["w_uv"].to(dev), gate=gate.to(dev))
+        cu_q = cu_k = inp["cu_seqlens"].tolist()
+        qlens = lens
+    torch.cuda.synchronize()
+    wk, wv = inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy()
+    for b, (L, Lq) in enumerate(zip(lens, qlens)):
+        ks, qs = slice(cu_k[b], cu_k[b] + L), slice(cu_q[b], cu_q[b] + Lq)
+        qn, qr = inp["q_nope"][qs].double().numpy(), inp["q_rope"][qs].double().numpy()
+        if paged:
+            c, kr = O.cached_token_values(inp["c_kv"][ks].double().numpy(), inp["k_rope"][ks].double().numpy(),
+                                          np.arange(L), w.cache_dtype, w.rope_base)
+            o, l = O.prefill_chunk_mha_form(qn, qr, c, kr, wk, wv, w.softmax_scale, w.rope_base,
+                                            operand_dtype="bf16")
+        else:
+            o, l = O.prefill_mha_form(qn, qr, inp["c_kv"][ks].double().numpy(), inp["k_rope"][ks].double().numpy(),
+                                      wk, wv, w.softmax_scale, w.rope_base, operand_dtype="bf16")
+        want = O.output_gate(o, gate[qs].double().numpy())
+        U.assert_close(out[qs], want, "bf16", f"gated out seq {b}")
+        U.assert_close(lse[qs], l, "bf16", f"lse seq {b}")
