@@ -199,6 +199,26 @@ def make_chunk_prefill_inputs(w: Workload, seed: int, seqlens: torch.Tensor, qle
     return out
 
 
+# DeepSeek-V3's hidden width and query-latent width (the upstream projections)
+V3_D_MODEL, V3_D_CQ = 7168, 1536
+
+
+def make_upstream_inputs(w: Workload, seed: int, n_tok: int, d_model: int = V3_D_MODEL,
+                         d_cq: int = V3_D_CQ) -> dict:
+    """Hidden states and upstream projection weights, N(0, 1) activations and
+    N(0, 1/sqrt(fan_in)) weights in the act dtype:
+      h [n_tok, d_model]; w_down [d_cq + d_c + d_R, d_model] (rows W_DQ, W_DKV, W_KR);
+      w_uq [H, d_nope + d_R, d_cq] (per head: the W_UQ rows, then the W_QR rows)."""
+    gen = torch.Generator().manual_seed(seed)
+    dt = TORCH_DTYPE[w.act_dtype]
+    return {
+        "h": _normal(gen, (n_tok, d_model)).to(dt),
+        "w_down": _normal(gen, (d_cq + w.d_c + w.d_rope, d_model), 1.0 / math.sqrt(d_model)).to(dt),
+        "w_uq": _normal(gen, (w.n_heads, w.d_nope + w.d_rope, d_cq), 1.0 / math.sqrt(d_cq)).to(dt),
+        "d_model": d_model, "d_cq": d_cq,
+    }
+
+
 def make_gate_logits(w: Workload, seed: int, n_tok: int) -> torch.Tensor:
     """Output-gate logits of gated MLA, [n_tok, H, d_v] in the act dtype, N(0, 1)."""
     gen = torch.Generator().manual_seed(seed)

@@ -44,6 +44,9 @@ Readings where the pages are silent or garbled (each one is a choice):
   R6  weights are stored W_UK [H, d_nope, d_c], W_UV [H, d_v, d_c], so that
       k_C = W_UK[s] c and v = W_UV[s] c.
   R7  lse is the natural log of the sum of exp over the scaled scores.
+  R17 upstream projections: c_Q, c_KV and the raw k_R (from h) and q_C, q_R
+      (from c_Q) are activations, each rounded once to the act dtype before
+      the next step uses it.
   R16 gated MLA: out = sigmoid(g) * o elementwise per head, with the gate
       logits g [tokens, heads, d_v] given (the pages name the gate only).
 """
@@ -289,6 +292,38 @@ def absorb_q(q_nope, q_rope, q_pos, w_uk, base):
     q_lat = np.einsum("...hn,hnc->...hc", q_nope, np.asarray(w_uk, dtype=F64))
     qr = rope(q_rope, np.asarray(q_pos), base)        # q_pos broadcasts to q_rope.shape[:-1]
     return np.concatenate([q_lat, qr], axis=-1)
+
+
+# ----------------------------------------------------------------------------
+# Upstream projections ([P4] MLA：高层次的思路: the latent c^KV is a
+# down-projection of the hidden state h, and queries are compressed to a
+# latent c^Q and restored the same way; 为什么需要解耦 RoPE: the RoPE query
+# parts come from the query latent and the shared RoPE key from h)
+# ----------------------------------------------------------------------------
+
+
+def project_down(h, w_down, d_cq: int, d_c: int, d_rope: int, out_dtype: Optional[str] = "bf16"):
+    """[c_Q | c_KV | k_R] = W_down h for every token, W_down = [W_DQ; W_DKV; W_KR]
+    stored [d_cq + d_c + d_R, d_model] (R6's orientation: out = W in).  Reading
+    R17: each projection is an activation, stored in the act dtype (rounded
+    once from the exact product) before it is used, so the fused path equals
+    projecting and then appending.  h [n, d_model].  Returns (c_q, c_kv,
+    k_rope_raw) as float64 values."""
+    y = np.asarray(h, dtype=F64) @ np.asarray(w_down, dtype=F64).T
+    if out_dtype is not None:
+        y = store_value(y, out_dtype)
+    return y[:, :d_cq], y[:, d_cq:d_cq + d_c], y[:, d_cq + d_c:d_cq + d_c + d_rope]
+
+
+def query_from_latent(c_q, w_uq, q_pos, w_uk, d_nope: int, base: float, out_dtype: Optional[str] = "bf16"):
+    """Absorbed queries from the query latent: per head s, [q_C | q_R] = W_UQ[s] c_Q
+    (W_UQ [H, d_nope + d_R, d_cq]: the W^UQ rows, then the W^QR rows), stored
+    in the act dtype (R17), then absorb_q.  c_q [n, d_cq], q_pos [n].
+    Returns q_abs [n, H, d_c + d_R] (float64)."""
+    q = np.einsum("tk,hrk->thr", np.asarray(c_q, dtype=F64), np.asarray(w_uq, dtype=F64))
+    if out_dtype is not None:
+        q = store_value(q, out_dtype)
+    return absorb_q(q[..., :d_nope], q[..., d_nope:], np.asarray(q_pos)[:, None], w_uk, base)
 
 
 def decode_absorbed_form(q_abs, c_cached, kr_cached, q_pos, scale):

@@ -488,3 +488,55 @@ def test_output_gate_symmetry_and_library_logistic():
     # the gate only shrinks: |out| <= |o| elementwise, with the sign of o
     out = O.output_gate(o, g)
     assert np.all(np.abs(out) <= np.abs(o)) and np.all(out * o >= 0)
+
+
+# ---------------------------------------------------------------- upstream projections
+
+def test_project_down_selection_rows_copy_coordinates():
+    """Unit-vector rows of W_down pick coordinates of h: the projections are
+    those coordinates, exact whenever they are bf16 values already."""
+    r = _rng(31)
+    d_model, d_cq, d_c, d_r = 40, 6, 8, 4
+    h = O.to_bf16_value(r.standard_normal((5, d_model)))
+    pick = r.permutation(d_model)[:d_cq + d_c + d_r]
+    W = np.zeros((d_cq + d_c + d_r, d_model))
+    W[np.arange(len(pick)), pick] = 1.0
+    cq, ckv, kr = O.project_down(h, W, d_cq, d_c, d_r)
+    assert np.array_equal(np.concatenate([cq, ckv, kr], axis=1), h[:, pick])
+
+
+def test_project_down_brute_force_and_rounding():
+    r = _rng(32)
+    h, W = r.standard_normal((3, 10)), r.standard_normal((7, 10))
+    cq, ckv, kr = O.project_down(h, W, 2, 3, 2, out_dtype=None)
+    y = np.concatenate([cq, ckv, kr], axis=1)
+    for t in range(3):
+        for n in range(7):
+            assert abs(y[t, n] - sum(h[t, k] * W[n, k] for k in range(10))) < 1e-12
+    yb = np.concatenate(O.project_down(h, W, 2, 3, 2), axis=1)
+    # one rounding to bf16 (8 significant bits): within half an ulp, at most 2^-8 relative, and on the bf16 grid
+    assert np.all(np.abs(yb - y) <= np.abs(y) * 2.0 ** -8)
+    assert np.array_equal(O.to_bf16_value(yb), yb)
+
+
+def test_query_from_latent_equals_the_composed_absorbed_map():
+    """Without the intermediate rounding, W_UK^T (W_UQ c) is the composed map
+    (W_UK^T W_UQ) c: the absorption of W_UK into the query projection
+    ([P4] 为什么需要解耦 RoPE; [P1] 双重投影, q = x W_q W_k^T)."""
+    r = _rng(33)
+    H, d_nope, d_r, d_c, d_cq, n = 3, 8, 4, 16, 12, 5
+    c_q = r.standard_normal((n, d_cq))
+    w_uq = r.standard_normal((H, d_nope + d_r, d_cq))
+    w_uk = r.standard_normal((H, d_nope, d_c))
+    pos = np.array([0, 1, 5, 100, 7])
+    qa = O.query_from_latent(c_q, w_uq, pos, w_uk, d_nope, 10000.0, out_dtype=None)
+    for s in range(H):
+        composed = w_uk[s].T @ w_uq[s, :d_nope]                  # [d_c, d_cq]
+        assert np.allclose(qa[:, s, :d_c], c_q @ composed.T, rtol=1e-12, atol=1e-12)
+        # the RoPE part is the rotated W_QR c_Q
+        qr = c_q @ w_uq[s, d_nope:].T
+        assert np.allclose(qa[:, s, d_c:], O.rope(qr, pos, 10000.0), rtol=1e-12, atol=1e-12)
+    # with the bf16 reading, the intermediate is on the bf16 grid and the result moves by about its resolution
+    qb = O.query_from_latent(c_q, w_uq, pos, w_uk, d_nope, 10000.0)
+    rel = np.linalg.norm(qb - qa) / np.linalg.norm(qa)
+    assert 1e-5 < rel < 1e-2
