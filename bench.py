@@ -76,6 +76,9 @@ def parse():
                     help="sequences of the workload the CPU oracle is timed on (0 = skip)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode+combine calls (for profiling)")
+    ap.add_argument("--upstream", action="store_true",
+                    help="start the step from the hidden state: mla_project_down (W_DQ, W_DKV, W_KR and the append) "
+                         "and mla_absorb_from_latent (W_UQ and the absorb) replace the append and the absorb")
     ap.add_argument("--gated", action="store_true",
                     help="gated MLA: the up-projection applies a sigmoid output gate (mla_up_proj_gated)")
     ap.add_argument("--prefill", action="store_true",
@@ -185,6 +188,14 @@ def main():
         new_seq_id=inp["tok_seq"][new_rows].to(dev), new_pos=inp["tok_pos"][new_rows].to(dev),
         block_table=table, seqlens=seqlens, pool=pool, w_uk=inp["w_uk"].to(dev), w_uv=inp["w_uv"].to(dev))
     gate = S.make_gate_logits(w, S.SEEDS[w.name] + 7, n_tok).to(dev) if args.gated else None
+    if args.upstream:
+        up = S.make_upstream_inputs(w, S.SEEDS[w.name] + 8, n_tok)
+        d_cq = up["d_cq"]
+        h_new, w_down, w_uq = up["h"].to(dev), up["w_down"].to(dev), up["w_uq"].to(dev)
+        c_q = torch.empty((n_tok, d_cq), dtype=h_new.dtype, device=dev)
+        ws_down = torch.empty(M.project_down_workspace_bytes(d, n_tok, up["d_model"], d_cq), dtype=torch.uint8,
+                              device=dev)
+        ws_q = torch.empty(M.absorb_from_latent_workspace_bytes(d, n_tok, d_cq), dtype=torch.uint8, device=dev)
     step = M.DecodeStep(d, B, sq, table.shape[1], num_splits=args.num_splits, device=dev)
     torch.cuda.synchronize()
     setup_s = time.time() - t0
@@ -203,10 +214,16 @@ def main():
                           args.num_splits, stream=stream)
             return
         dd = step.d
-        M.absorb_q(dd, step_inputs["q_nope"], step_inputs["q_rope"], step_inputs["q_pos"], step_inputs["w_uk"],
-                   q_abs=step.q_abs.view(n_tok, H, -1), stream=stream)
-        M.append_cache(dd, step_inputs["new_c_kv"], step_inputs["new_k_rope"], step_inputs["new_seq_id"],
-                       step_inputs["new_pos"], table, pool, stream=stream)
+        if args.upstream:
+            M.project_down(dd, h_new, w_down, d_cq, step_inputs["new_seq_id"], step_inputs["new_pos"], table, pool,
+                           c_q=c_q, workspace=ws_down, stream=stream)
+            M.absorb_from_latent(dd, c_q, w_uq, step_inputs["q_pos"], step_inputs["w_uk"],
+                                 q_abs=step.q_abs.view(n_tok, H, -1), workspace=ws_q, stream=stream)
+        else:
+            M.absorb_q(dd, step_inputs["q_nope"], step_inputs["q_rope"], step_inputs["q_pos"], step_inputs["w_uk"],
+                       q_abs=step.q_abs.view(n_tok, H, -1), stream=stream)
+            M.append_cache(dd, step_inputs["new_c_kv"], step_inputs["new_k_rope"], step_inputs["new_seq_id"],
+                           step_inputs["new_pos"], table, pool, stream=stream)
         if ev_pair:
             ev_pair[0].record(stream)
         M.decode(dd, step.q_abs, pool, table, seqlens, args.num_splits, step.workspace, step.o_latent,
@@ -265,6 +282,7 @@ def main():
         "config": {"workload": w.name, "batch": B, "q_per_seq": sq, "n_heads": H, "d_c": w.d_c,
                    "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v, "seqlen": w.seqlen,
                    "block_size": w.block_size, "cache_dtype": w.cache_dtype, "output_gate": bool(args.gated),
+                   "from_hidden_state": bool(args.upstream),
                    "parallelism": "single GPU"},
         "decode_ms": round(dec_ms, 4),
         "decode_hbm_gbps": round(dec_gbps, 1),

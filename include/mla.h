@@ -150,6 +150,50 @@ size_t mla_decode_workspace_bytes(const mla_dims* dims, int32_t n_seq, int32_t q
                                   int32_t max_blocks, int32_t num_splits);
 
 /*
+ * mla_project_down -- the down-projections of the hidden state fused with the
+ * cache append ("DeepSeek-V3 解读", MLA：高层次的思路: the latent c^KV = W^DKV h,
+ * and the queries are compressed to a latent the same way; 为什么需要解耦
+ * RoPE: the shared RoPE key comes from h).  With W_down = [W_DQ; W_DKV; W_KR]
+ * stored [d_cq + d_c + d_rope, d_model] (row-major, contraction-contiguous):
+ *   [c_q[n] | c_kv[n] | k_rope[n]] = W_down h[n]   (fp32 accumulation, each rounded once to bf16)
+ * c_q [n_tok, d_cq] is written (the query latent, for mla_absorb_from_latent;
+ * d_cq = 0 means no query latent, c_q may be null); [c_kv | k_rope] is then
+ * appended exactly as mla_append_cache does (same arguments and skipping
+ * rules), so the call equals projecting and appending.  h [n_tok, d_model]
+ * bf16.  workspace: at least mla_project_down_workspace_bytes, 16-byte
+ * aligned (split-K partials and the projected rows).  Supported: bf16
+ * activations, d_model a multiple of 16, d_cq + d_c + d_rope a multiple of 8
+ * (else MLA_ERR_UNSUPPORTED).  n_tok may be 0 (no launch).
+ */
+size_t mla_project_down_workspace_bytes(const mla_dims* dims, int32_t n_tok, int32_t d_model,
+                                        int32_t d_cq);
+mla_status mla_project_down(const mla_dims* dims, int32_t n_tok, int32_t d_model, int32_t d_cq,
+                            const void* h, const void* w_down, const int32_t* seq_id,
+                            const int32_t* pos, const int32_t* block_table, int32_t n_seq,
+                            int32_t max_blocks, void* cache_pool, int64_t n_pool_blocks, void* c_q,
+                            void* workspace, size_t workspace_bytes, mla_stream_t stream);
+
+/*
+ * mla_absorb_from_latent -- the query up-projections fused with the
+ * absorption ("DeepSeek-V3 解读", 为什么需要解耦 RoPE: the per-head query and
+ * its RoPE part are restored from the query latent; W^UK can be absorbed into
+ * the query side).  w_uq [H, d_nope + d_rope, d_cq] holds per head the W_UQ
+ * rows, then the W_QR rows:
+ *   [q_nope[t,s] | q_rope[t,s]] = w_uq[s] c_q[t]     (fp32 accumulation, rounded once to bf16)
+ * then q_abs as mla_absorb_q with those q_nope, q_rope, pos and w_uk.  The two
+ * factors are chained, not composed into one d_c x d_cq matrix per head
+ * (which would triple the weight bytes at DeepSeek-V3 shape).  c_q [n_tok,
+ * d_cq] bf16; q_abs [n_tok, H, d_c + d_rope].  workspace: at least
+ * mla_absorb_from_latent_workspace_bytes, 16-byte aligned.  Supported: bf16,
+ * d_cq a multiple of 16, H (d_nope + d_rope) a multiple of 8.  n_tok may be 0.
+ */
+size_t mla_absorb_from_latent_workspace_bytes(const mla_dims* dims, int32_t n_tok, int32_t d_cq);
+mla_status mla_absorb_from_latent(const mla_dims* dims, int32_t n_tok, int32_t d_cq,
+                                  const void* c_q, const void* w_uq, const int32_t* pos,
+                                  const void* w_uk, void* q_abs, void* workspace,
+                                  size_t workspace_bytes, mla_stream_t stream);
+
+/*
  * mla_decode -- latent attention, the absorbed form ("Transformer升级之路：21、
  * MLA好在哪里？（下）", 双重投影, decoding column: every head attends with key
  * [c | k_R] and value c, shared by all heads).

@@ -66,6 +66,11 @@ SIGNATURES = {
     "mla_prefill_workspace_bytes": (_SZ, [_DP, _I32]),
     "mla_prefill": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
     "mla_prefill_paged_workspace_bytes": (_SZ, [_DP, _I32, _I32]),
+    "mla_project_down_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I32]),
+    "mla_project_down": (ctypes.c_int, [_DP, _I32, _I32, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, ctypes.c_int64,
+                                        _P, _P, _SZ, _P]),
+    "mla_absorb_from_latent_workspace_bytes": (_SZ, [_DP, _I32, _I32]),
+    "mla_absorb_from_latent": (ctypes.c_int, [_DP, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
     "mla_prefill_paged": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
                                          _SZ, _P, _P, _P]),
 }
@@ -267,3 +272,55 @@ def prefill_paged(d: Dims, q_nope, q_rope, cu_q, max_q: int, cu_k, total_k: int,
         _ptr(w_uv, "w_uv", at), _ptr(gate, "gate", at), _ptr(workspace, "workspace"), ws_bytes,
         _ptr(out, "out", at), _ptr(lse, "lse", torch.float32), _stream(stream)))
     return out, lse, workspace
+
+
+def project_down_workspace_bytes(d: Dims, n_tok: int, d_model: int, d_cq: int) -> int:
+    return load_library().mla_project_down_workspace_bytes(ctypes.byref(d), n_tok, d_model, d_cq)
+
+
+def project_down(d: Dims, h, w_down, d_cq: int, seq_id, pos, block_table, pool, c_q=None, workspace=None,
+                 stream=None):
+    """[c_Q | c_KV | k_R] = W_down h (W_down [d_cq + d_c + d_rope, d_model]); the
+    latent and the shared key are appended to the paged pool as append_cache
+    does.  Returns c_q [n_tok, d_cq]."""
+    at = act_torch_dtype(d)
+    n_tok, d_model = h.shape
+    bb = cache_block_bytes(d)
+    if pool.dtype != torch.uint8 or pool.numel() % bb:
+        raise ValueError("pool must be a uint8 tensor of whole blocks")
+    if c_q is None and d_cq > 0:
+        c_q = torch.empty((n_tok, d_cq), dtype=at, device=h.device)
+    if workspace is None:
+        workspace = torch.empty(max(project_down_workspace_bytes(d, n_tok, d_model, d_cq), 1), dtype=torch.uint8,
+                                device=h.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    n_seq, max_blocks = block_table.shape
+    _check("mla_project_down", load_library().mla_project_down(
+        ctypes.byref(d), n_tok, d_model, d_cq, _ptr(h, "h", at), _ptr(w_down, "w_down", at),
+        _ptr(seq_id, "seq_id", torch.int32), _ptr(pos, "pos", torch.int32),
+        _ptr(block_table, "block_table", torch.int32), n_seq, max_blocks, _ptr(pool, "pool", torch.uint8),
+        pool.numel() // bb, _ptr(c_q, "c_q", at), _ptr(workspace, "workspace"), ws_bytes, _stream(stream)))
+    return c_q
+
+
+def absorb_from_latent_workspace_bytes(d: Dims, n_tok: int, d_cq: int) -> int:
+    return load_library().mla_absorb_from_latent_workspace_bytes(ctypes.byref(d), n_tok, d_cq)
+
+
+def absorb_from_latent(d: Dims, c_q, w_uq, pos, w_uk, q_abs=None, workspace=None, stream=None):
+    """q_abs [n_tok, H, d_c + d_rope] from the query latent c_q [n_tok, d_cq]:
+    [q_nope | q_rope] = w_uq[s] c_q per head (w_uq [H, d_nope + d_rope, d_cq]),
+    then the absorption of W_UK and the rotation of q_rope at pos."""
+    at = act_torch_dtype(d)
+    n_tok, d_cq = c_q.shape
+    if q_abs is None:
+        q_abs = torch.empty((n_tok, d.n_heads, d.d_c + d.d_rope), dtype=at, device=c_q.device)
+    if workspace is None:
+        workspace = torch.empty(max(absorb_from_latent_workspace_bytes(d, n_tok, d_cq), 1), dtype=torch.uint8,
+                                device=c_q.device)
+    ws_bytes = workspace.numel() * workspace.element_size()
+    _check("mla_absorb_from_latent", load_library().mla_absorb_from_latent(
+        ctypes.byref(d), n_tok, d_cq, _ptr(c_q, "c_q", at), _ptr(w_uq, "w_uq", at), _ptr(pos, "pos", torch.int32),
+        _ptr(w_uk, "w_uk", at), _ptr(q_abs, "q_abs", at), _ptr(workspace, "workspace"), ws_bytes,
+        _stream(stream)))
+    return q_abs

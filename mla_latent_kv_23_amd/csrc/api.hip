@@ -303,4 +303,68 @@ mla_status mla_prefill_paged(const mla_dims* d, int32_t n_seq, const int32_t* cu
                               max_blocks, w_uk, w_uv, gate, workspace, out, lse, static_cast<hipStream_t>(stream));
 }
 
+namespace {
+// the upstream GEMMs: bf16, 16-byte rows, whole float4 pieces of the partials
+// that never straddle an output segment (the segment widths are multiples of 4)
+bool upstream_shape_ok(const mla_dims* d, int64_t K, int64_t N) {
+  return d->act_dtype == MLA_BF16 && K >= 16 && K % 16 == 0 && N % 8 == 0 && d->d_c % 4 == 0 && d->d_rope % 4 == 0 &&
+         d->d_nope % 4 == 0;
+}
+}  // namespace
+
+size_t mla_project_down_workspace_bytes(const mla_dims* d, int32_t n_tok, int32_t d_model, int32_t d_cq) {
+  if (dims_supported(d) != MLA_OK || n_tok < 0 || d_model <= 0 || d_cq < 0) return 0;
+  if (!upstream_shape_ok(d, d_model, (int64_t)d_cq + d->d_c + d->d_rope) || d_cq % 4 != 0) return 0;
+  return project_down_workspace_bytes(*d, n_tok, d_model, d_cq);
+}
+
+mla_status mla_project_down(const mla_dims* d, int32_t n_tok, int32_t d_model, int32_t d_cq, const void* h,
+                            const void* w_down, const int32_t* seq_id, const int32_t* pos,
+                            const int32_t* block_table, int32_t n_seq, int32_t max_blocks, void* cache_pool,
+                            int64_t n_pool_blocks, void* c_q, void* workspace, size_t workspace_bytes,
+                            mla_stream_t stream) {
+  const mla_status s = dims_supported(d);
+  if (s != MLA_OK) return s;
+  if (n_tok < 0 || d_model <= 0 || d_cq < 0 || n_seq <= 0 || max_blocks <= 0 || n_pool_blocks <= 0)
+    return MLA_ERR_INVALID_ARG;
+  const int64_t N = (int64_t)d_cq + d->d_c + d->d_rope;
+  if (!upstream_shape_ok(d, d_model, N) || d_cq % 4 != 0) return MLA_ERR_UNSUPPORTED;
+  if (n_tok == 0) return MLA_OK;
+  if (!h || !w_down || !seq_id || !pos || !block_table || !cache_pool || (d_cq > 0 && !c_q))
+    return MLA_ERR_INVALID_ARG;
+  // 32-bit index math: rows of h and W and the partials' token x feature
+  if ((int64_t)n_tok * d_model > 2147483647LL || N * d_model > 2147483647LL || (int64_t)n_tok * N > 2147483647LL)
+    return MLA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < project_down_workspace_bytes(*d, n_tok, d_model, d_cq))
+    return MLA_ERR_WORKSPACE;
+  if (!aligned16(h) || !aligned16(w_down) || !aligned16(workspace) || (d_cq > 0 && !aligned16(c_q)))
+    return MLA_ERR_INVALID_ARG;
+  return launch_project_down(*d, n_tok, d_model, d_cq, h, w_down, seq_id, pos, block_table, n_seq, max_blocks,
+                             cache_pool, n_pool_blocks, c_q, workspace, static_cast<hipStream_t>(stream));
+}
+
+size_t mla_absorb_from_latent_workspace_bytes(const mla_dims* d, int32_t n_tok, int32_t d_cq) {
+  if (dims_supported(d) != MLA_OK || n_tok < 0 || d_cq <= 0) return 0;
+  if (!upstream_shape_ok(d, d_cq, (int64_t)d->n_heads * (d->d_nope + d->d_rope))) return 0;
+  return absorb_from_latent_workspace_bytes(*d, n_tok, d_cq);
+}
+
+mla_status mla_absorb_from_latent(const mla_dims* d, int32_t n_tok, int32_t d_cq, const void* c_q,
+                                  const void* w_uq, const int32_t* pos, const void* w_uk, void* q_abs,
+                                  void* workspace, size_t workspace_bytes, mla_stream_t stream) {
+  const mla_status s = dims_supported(d);
+  if (s != MLA_OK) return s;
+  if (n_tok < 0 || d_cq <= 0) return MLA_ERR_INVALID_ARG;
+  const int64_t N = (int64_t)d->n_heads * (d->d_nope + d->d_rope);
+  if (!upstream_shape_ok(d, d_cq, N)) return MLA_ERR_UNSUPPORTED;
+  if (n_tok == 0) return MLA_OK;
+  if (!c_q || !w_uq || !pos || !w_uk || !q_abs) return MLA_ERR_INVALID_ARG;
+  if ((int64_t)n_tok * d_cq > 2147483647LL || N * d_cq > 2147483647LL || (int64_t)n_tok * N > 2147483647LL)
+    return MLA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < absorb_from_latent_workspace_bytes(*d, n_tok, d_cq)) return MLA_ERR_WORKSPACE;
+  if (!aligned16(c_q) || !aligned16(w_uq) || !aligned16(workspace)) return MLA_ERR_INVALID_ARG;
+  return launch_absorb_from_latent(*d, n_tok, d_cq, c_q, w_uq, pos, w_uk, q_abs, workspace,
+                                   static_cast<hipStream_t>(stream));
+}
+
 }  // extern "C"

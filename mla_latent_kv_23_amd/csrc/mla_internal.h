@@ -85,6 +85,15 @@ mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t*
                                 const void* cache_pool, const int32_t* block_table, int32_t max_blocks,
                                 const void* w_uk, const void* w_uv, const void* gate, void* ws, void* out, float* lse,
                                 hipStream_t st);
+size_t project_down_workspace_bytes(const mla_dims& d, int64_t n_tok, int64_t d_model, int64_t d_cq);
+mla_status launch_project_down(const mla_dims& d, int32_t n_tok, int32_t d_model, int32_t d_cq, const void* h,
+                               const void* w_down, const int32_t* seq_id, const int32_t* pos,
+                               const int32_t* block_table, int32_t n_seq, int32_t max_blocks, void* pool,
+                               int64_t n_pool_blocks, void* c_q, void* ws, hipStream_t st);
+size_t absorb_from_latent_workspace_bytes(const mla_dims& d, int64_t n_tok, int64_t d_cq);
+mla_status launch_absorb_from_latent(const mla_dims& d, int32_t n_tok, int32_t d_cq, const void* c_q,
+                                     const void* w_uq, const int32_t* pos, const void* w_uk, void* q_abs, void* ws,
+                                     hipStream_t st);
 mla_status launch_up_proj_generic(const mla_dims& d, int32_t n_tok, const void* o_lat, const void* w_uv,
                                   const void* gate, void* out, hipStream_t st);
 

@@ -1,0 +1,126 @@
+"""GPU parity of the upstream projections (mla_project_down, mla_absorb_from_latent)
+against the CPU oracle, at DeepSeek-V3 widths (d_model 7168, d_cq 1536).
+
+The library accumulates in float32 and the oracle in float64; each projection is
+then rounded once to bf16.  Where the two sums straddle a bf16 rounding boundary
+the stored values differ by one unit in the last place, so the checks are: every
+element within a small number of ulps of the exact value, and the cached bytes
+equal to the oracle's on all but a small fraction (a projection that rounds
+differently changes its cached bytes, nothing else).  All calls go through the
+C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import mla_synth as S
+from oracle import mla_oracle as O
+from tests import _util as U
+
+pytestmark = pytest.mark.gpu
+
+V3 = S.WORKLOADS["v3_bs64_ctx8k"]
+
+
+def _assert_rotated_close(g, e, what):
+    """Rotated pairs whose raw value (a bf16 projection) may have rounded the other
+    way on one side: the raw elements differ by at most one ulp of the pair's norm
+    n (u = 2^(floor(log2 n) - 7)), the rotation keeps that difference (at most
+    sqrt(2) u) and each side's final rounding adds at most u / 2: 2.5 u in all."""
+    n = np.sqrt(e[..., 0::2] ** 2 + e[..., 1::2] ** 2)
+    u = np.repeat(np.exp2(np.floor(np.log2(np.maximum(n, 1e-30))) - 7), 2, axis=-1)
+    ratio = np.abs(g - e) / u
+    assert np.all(ratio <= 2.5), f"{what}: {int((ratio > 2.5).sum())} elements beyond 2.5 u (worst {ratio.max():.2f})"
+
+
+def _bf16_pool_values(pool_u8: np.ndarray, n_blocks: int, block_size: int, width: int) -> np.ndarray:
+    bits = pool_u8.view(np.uint16).reshape(n_blocks, block_size, width)
+    return O.bf16_bits_to_f64(bits)
+
+
+@pytest.mark.parametrize("cache_dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("lens,d_cq", [([100, 37], 1536), ([64] * 4, 1536), ([1], 1536), ([70, 5], 0)])
+def test_project_down_matches_oracle(cache_dtype, lens, d_cq, cuda_device):
+    import mla_latent_kv_23_amd as M
+    w = V3.replace(cache_dtype=cache_dtype)
+    inp = S.make_inputs(w, 810 + len(lens), seqlens=torch.tensor(lens, dtype=torch.int32))
+    T = int(sum(lens))
+    up = S.make_upstream_inputs(w, 811, T, d_cq=max(d_cq, 16))
+    w_down = up["w_down"] if d_cq > 0 else up["w_down"][up["d_cq"]:].contiguous()
+    U.say(f"[project_down] cache={cache_dtype} lens={lens} d_cq={d_cq}")
+    d = U.dims_of(w)
+    dev = cuda_device
+    bb = M.cache_block_bytes(d)
+    pool = torch.full((inp["n_blocks"] * bb,), 0xA5, dtype=torch.uint8, device=dev)
+    c_q = M.project_down(d, up["h"].to(dev), w_down.to(dev), d_cq, inp["tok_seq"].to(dev), inp["tok_pos"].to(dev),
+                         inp["block_table"].to(dev), pool)
+    torch.cuda.synchronize()
+    h64, wd64 = up["h"].double().numpy(), w_down.double().numpy()
+    cq_x, ckv_x, kr_x = O.project_down(h64, wd64, d_cq, w.d_c, w.d_rope, out_dtype=None)
+    if d_cq > 0:
+        U.assert_close_ulp(c_q, cq_x, "bf16", "c_q", ulps=1.0)
+    # expected pool from the oracle's projections (R17: rounded once to bf16), then the append
+    _, ckv_b, kr_b = O.project_down(h64, wd64, d_cq, w.d_c, w.d_rope)
+    want = O.append_expected_pool(np.full(inp["n_blocks"] * bb, 0xA5, dtype=np.uint8), ckv_b, kr_b,
+                                  inp["tok_seq"].numpy(), inp["tok_pos"].numpy(), inp["block_table"].numpy(),
+                                  block_size=w.block_size, d_c=w.d_c, d_rope=w.d_rope, cache_dtype=cache_dtype,
+                                  base=w.rope_base)
+    got = pool.cpu().numpy()
+    diff = got != want
+    # every differing byte belongs to a written token row (untouched bytes stay poisoned)
+    assert diff.mean() < 2e-3, f"{diff.mean():.2e} of the pool bytes differ"
+    nb = inp["n_blocks"]
+    if cache_dtype == "bf16":
+        g = _bf16_pool_values(got, nb, w.block_size, w.d_c + w.d_rope)
+        e = _bf16_pool_values(want, nb, w.block_size, w.d_c + w.d_rope)
+        written = np.zeros((nb, w.block_size), dtype=bool)
+        tbl = inp["block_table"].numpy()
+        for sq, p in zip(inp["tok_seq"].numpy(), inp["tok_pos"].numpy()):
+            written[tbl[sq, p // w.block_size], p % w.block_size] = True
+        # one ulp of the latent; the rotated key as bounded above
+        gl, el = g[written][:, :w.d_c], e[written][:, :w.d_c]
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(el), 1e-30))) - 7)
+        assert np.all(np.abs(gl - el) <= ulp), "latent beyond one ulp"
+        _assert_rotated_close(g[written][:, w.d_c:], e[written][:, w.d_c:], "cached k_R")
+    else:
+        # the decoded latent: where a code differs it is one E4M3 step away (at most 1/8 relative)
+        blk = 64 * w.d_c
+        for b in range(nb):
+            base = b * bb
+            gc = O.e4m3fn_decode(got[base:base + blk])
+            ec = O.e4m3fn_decode(want[base:base + blk])
+            gs = got[base + blk:base + blk + 4 * 64].view(np.float32).astype(np.float64)
+            es = want[base + blk:base + blk + 4 * 64].view(np.float32).astype(np.float64)
+            gv = gc.reshape(64, w.d_c) * gs[:, None]
+            ev = ec.reshape(64, w.d_c) * es[:, None]
+            ok = np.isfinite(ev)
+            assert np.all(np.abs(gv - ev)[ok] <= 0.126 * np.abs(ev)[ok] + 2.0 ** -9 * np.abs(es).max() + 1e-30)
+
+
+@pytest.mark.parametrize("n_tok", [64, 37, 1, 200])
+def test_absorb_from_latent_matches_oracle(n_tok, cuda_device):
+    import mla_latent_kv_23_amd as M
+    w = V3
+    inp = S.make_inputs(w.replace(batch=1), 820, seqlens=torch.tensor([8], dtype=torch.int32))
+    up = S.make_upstream_inputs(w, 821, n_tok)
+    gen = torch.Generator().manual_seed(822)
+    c_q = torch.randn(n_tok, up["d_cq"], generator=gen).to(torch.bfloat16)
+    pos = torch.randint(0, 100000, (n_tok,), generator=gen, dtype=torch.int32)
+    U.say(f"[absorb_from_latent] n_tok={n_tok}")
+    d = U.dims_of(w)
+    dev = cuda_device
+    q_abs = M.absorb_from_latent(d, c_q.to(dev), up["w_uq"].to(dev), pos.to(dev), inp["w_uk"].to(dev))
+    torch.cuda.synchronize()
+    args = (c_q.double().numpy(), up["w_uq"].double().numpy(), pos.numpy(), inp["w_uk"].double().numpy(), w.d_nope,
+            w.rope_base)
+    want = O.query_from_latent(*args)                       # R17: q_C, q_R rounded to bf16 first
+    exact = O.query_from_latent(*args, out_dtype=None)      # no intermediate rounding
+    # the latent part: the bf16 bar against the exact chain, and one rounding of the R17 chain's value on
+    # all but a few elements (where the float32 sum of a q_C element rounds the other way than the
+    # float64 one, the 128-term absorb moves by about that element's ulp times a weight)
+    U.assert_close(q_abs[..., :w.d_c], exact[..., :w.d_c], "bf16", "q_lat vs exact chain")
+    g = q_abs[..., :w.d_c].double().cpu().numpy()
+    e = want[..., :w.d_c]
+    ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(e), 1e-30))) - 7)
+    frac = float(np.mean(np.abs(g - e) <= 1.5 * ulp))
+    assert frac >= 0.999, f"q_lat: only {frac:.5f} of the elements within 1.5 ulp of the bf16 chain"
+    _assert_rotated_close(q_abs[..., w.d_c:].double().cpu().numpy(), want[..., w.d_c:], "rotated q_R")
