@@ -17,12 +17,13 @@
 // contraction-contiguous) is computed transposed on MFMA 32x32x16: each
 // work-group owns 64 output features x 64 tokens and a range of the
 // contraction (split-K, so that a few tokens still spread the weight stream
-// over the whole chip); its four waves take a quarter of that range each,
-// with both operands read straight from global memory, 16 bytes per lane, 8
-// k-steps of loads issued before their MFMAs.  The four partial tiles are
-// summed through LDS and each split writes an fp32 partial [split][n_tok][N];
-// the small epilogue kernels sum the splits in a fixed order.  (32 features
-// per work-group, or 16 k-steps per batch, measured slower at 64 tokens.)
+// over the whole chip).  Both operands are staged through LDS in stages of
+// 128 contraction elements, loaded as whole 256-byte row segments (16 lanes
+// per row), two stages in flight in registers; each wave multiplies one
+// 32 x 32 output tile out of LDS.  Each split writes an fp32 partial
+// [split][n_tok][N]; the small epilogue kernels sum the splits in a fixed
+// order.  (Reading the MFMA fragments straight from global memory touches 32
+// bytes of 32 rows per load instruction and measured 1.5-2x slower.)
 #include <algorithm>
 
 #include "decode_latent576.h"
@@ -35,95 +36,99 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
-#ifndef GEMM_FT
-#define GEMM_FT 2
-#endif
-#ifndef GEMM_STEPS
-#define GEMM_STEPS 8
-#endif
 constexpr int kGemmTok = 64;            // tokens per work-group (two MFMA column tiles)
-constexpr int kFT = GEMM_FT;            // 32-feature tiles per work-group
-constexpr int kGemmFeat = 32 * kFT;     // features per work-group
-constexpr int kGemmSteps = GEMM_STEPS;  // k-steps (16 each) loaded per wave before its MFMAs
-constexpr int kRedPitch = kGemmFeat + 4;   // LDS floats per token row of a wave's partial tile (padded)
+constexpr int kGemmFeat = 64;           // features per work-group (two MFMA row tiles)
+constexpr int kChunkK = 128;            // contraction elements per LDS stage (8 k-steps)
+constexpr int kRowB = kChunkK * 2 + 16; // LDS bytes per staged row (256 + 16 pad: conflict-free fragment reads)
+constexpr int kStageB = (kGemmFeat + kGemmTok) * kRowB;   // 34816
+constexpr int kPieces = (kGemmFeat + kGemmTok) * (kChunkK * 2 / 16) / 256;   // 16-byte loads per thread per stage: 8
 
-// grid (ceil(N / kGemmFeat), ceil(n_tok / 64), S), block 256.
+// grid (ceil(N / 64), ceil(n_tok / 64), S), block 256.  Each stage holds 128
+// contraction elements of the 64 weight rows and the 64 token rows; thread t
+// loads pieces p = t + 256 j: row p / 16, 16-byte part p % 16 (16 consecutive
+// lanes read one 256-byte row segment).  Two stages are in flight in
+// registers while the previous one is multiplied out of LDS.  Wave w computes
+// the 32 x 32 output tile (features 32 (w % 2), tokens 32 (w / 2)).
 __global__ void __launch_bounds__(256) xwt_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                        int n_tok, int N, int K, int steps_per_split,
                                                        float* __restrict__ part) {
-  __shared__ __attribute__((aligned(16))) float red_raw[4 * kGemmTok * kRedPitch];
+  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[2 * kStageB];
+  lds_u8* lds = (lds_u8*)lds_raw;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ft = wave & 1, tt = wave >> 1;
   const int f0 = blockIdx.x * kGemmFeat, t0 = blockIdx.y * kGemmTok, z = blockIdx.z;
   const int ksteps = K / 16;
-  const int z0 = z * steps_per_split, z1 = min(z0 + steps_per_split, ksteps);
-  const int per = (z1 - z0 + 3) / 4;
-  const int w0 = min(z0 + wave * per, z1), w1 = min(w0 + per, z1);
+  const int ks0 = z * steps_per_split, ks1 = min(ks0 + steps_per_split, ksteps);
+  const int n_chunks = (ks1 - ks0 + 7) / 8;
 
-  // A: feature rows f0 + 32 ft + lane % 32; B: token rows t0 + 32 tt + lane % 32 (clamped; out-of-range rows are
-  // not stored)
-  const bf16x8* arow[kFT];
+  // this thread's source rows (clamped: rows past N or n_tok are loaded but never stored)
+  const uint16_t* src[kPieces];
 #pragma unroll
-  for (int ft = 0; ft < kFT; ++ft) arow[ft] = (const bf16x8*)(W + (int64_t)min(f0 + 32 * ft + (lane & 31), N - 1) * K) + half;
-  const bf16x8* brow[2];
+  for (int j = 0; j < kPieces; ++j) {
+    const int p = tid + 256 * j, row = p >> 4, part16 = p & 15;
+    const uint16_t* base = row < kGemmFeat ? W + (int64_t)min(f0 + row, N - 1) * K
+                                           : X + (int64_t)min(t0 + row - kGemmFeat, n_tok - 1) * K;
+    src[j] = base + 16 * ks0 + 8 * part16;
+  }
+  // k-steps past the split's end read the split's last k-step (in bounds) and are skipped by the MFMAs
+  auto load = [&](u32x4 (&r)[kPieces], int c) {
+    const int off = min(8 * c + ((tid & 15) >> 1), ks1 - ks0 - 1) * 16 - ((tid & 15) >> 1) * 16;
 #pragma unroll
-  for (int tt = 0; tt < 2; ++tt) brow[tt] = (const bf16x8*)(X + (int64_t)min(t0 + 32 * tt + (lane & 31), n_tok - 1) * K) + half;
-
-  f32x16 acc[kFT][2];
+    for (int j = 0; j < kPieces; ++j) r[j] = *(const u32x4*)(src[j] + off);
+  };
+  auto store = [&](const u32x4 (&r)[kPieces], int buf) {
 #pragma unroll
-  for (int ft = 0; ft < kFT; ++ft) acc[ft][0] = acc[ft][1] = f32x16{};
-  for (int ks = w0; ks < w1; ks += kGemmSteps) {
-    bf16x8 a[kGemmSteps][kFT], b[kGemmSteps][2];
-#pragma unroll
-    for (int j = 0; j < kGemmSteps; ++j) {
-      const int k = min(ks + j, w1 - 1);
-#pragma unroll
-      for (int ft = 0; ft < kFT; ++ft) a[j][ft] = arow[ft][2 * k];
-#pragma unroll
-      for (int tt = 0; tt < 2; ++tt) b[j][tt] = brow[tt][2 * k];
+    for (int j = 0; j < kPieces; ++j) {
+      const int p = tid + 256 * j, row = p >> 4, part16 = p & 15;
+      *(lds_u32x4*)(lds + buf * kStageB + row * kRowB + 16 * part16) = r[j];
     }
+  };
+  f32x16 acc = f32x16{};
+  auto compute = [&](int buf, int c) {
+    const lds_u8* base = lds + buf * kStageB;
 #pragma unroll
-    for (int j = 0; j < kGemmSteps; ++j)
-      if (ks + j < w1) {
-#pragma unroll
-        for (int ft = 0; ft < kFT; ++ft)
-#pragma unroll
-          for (int tt = 0; tt < 2; ++tt)
-            acc[ft][tt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[j][ft], b[j][tt], acc[ft][tt], 0, 0, 0);
+    for (int j = 0; j < 8; ++j) {
+      if (8 * c + j < ks1 - ks0) {
+        const bf16x8 a = *(const lds_bf16x8*)(base + (32 * ft + (lane & 31)) * kRowB + 32 * j + 16 * half);
+        const bf16x8 b = *(const lds_bf16x8*)(base + (kGemmFeat + 32 * tt + (lane & 31)) * kRowB + 32 * j + 16 * half);
+        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
       }
+    }
+  };
+
+  u32x4 ra[kPieces], rb[kPieces];
+  if (n_chunks > 0) load(ra, 0);
+  if (n_chunks > 1) load(rb, 1);
+  if (n_chunks > 0) store(ra, 0);
+  __syncthreads();
+  for (int c = 0; c < n_chunks; c += 2) {
+    // chunk c in buffer 0 (ra free), chunk c + 1 in flight in rb
+    if (c + 2 < n_chunks) load(ra, c + 2);
+    compute(0, c);
+    if (c + 1 < n_chunks) store(rb, 1);
+    __syncthreads();
+    if (c + 1 >= n_chunks) break;
+    // chunk c + 1 in buffer 1 (rb free), chunk c + 2 in flight in ra
+    if (c + 3 < n_chunks) load(rb, c + 3);
+    compute(1, c + 1);
+    if (c + 2 < n_chunks) store(ra, 0);
+    __syncthreads();
   }
 
-  // lane holds token 32 tt + lane % 32, features 32 ft + 8 g + 4 half + 0..3 (g = i / 4)
-  lds_f32x4* red = (lds_f32x4*)(__attribute__((address_space(3))) float*)red_raw;
+  // lane holds token t0 + 32 tt + lane % 32, features f0 + 32 ft + 8 g + 4 half + 0..3
+  const int t = t0 + 32 * tt + (lane & 31);
+  if (t < n_tok) {
+    float* dst = part + ((int64_t)z * n_tok + t) * N + f0 + 32 * ft + 4 * half;
 #pragma unroll
-  for (int ft = 0; ft < kFT; ++ft)
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int row = wave * kGemmTok + 32 * tt + (lane & 31);
-        red[(row * kRedPitch + 32 * ft + 8 * g + 4 * half) / 4] =
-            f32x4{acc[ft][tt][4 * g], acc[ft][tt][4 * g + 1], acc[ft][tt][4 * g + 2], acc[ft][tt][4 * g + 3]};
-      }
-  __syncthreads();
-  // thread: token r = tid / 4, features 8 (tid % 4) + 32 ft .. +7, summed over the waves in order
-  const int r = tid >> 2, t = t0 + r;
-#pragma unroll
-  for (int ft = 0; ft < kFT; ++ft) {
-    const int c8 = 32 * ft + 8 * (tid & 3);
-    f32x4 s0 = red[(r * kRedPitch + c8) / 4], s1 = red[(r * kRedPitch + c8 + 4) / 4];
-#pragma unroll
-    for (int w = 1; w < 4; ++w) {
-      s0 += red[((w * kGemmTok + r) * kRedPitch + c8) / 4];
-      s1 += red[((w * kGemmTok + r) * kRedPitch + c8 + 4) / 4];
-    }
-    if (t < n_tok) {
-      float* dst = part + ((int64_t)z * n_tok + t) * N + f0 + c8;
-      if (f0 + c8 + 4 <= N) *(f32x4*)dst = s0;
-      if (f0 + c8 + 8 <= N) *(f32x4*)(dst + 4) = s1;
-    }
+    for (int g = 0; g < 4; ++g)
+      if (f0 + 32 * ft + 8 * g + 4 * half + 4 <= N)
+        *(f32x4*)(dst + 8 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
   }
 }
 
@@ -133,8 +138,20 @@ __global__ void __launch_bounds__(256) xwt_gemm_kernel(const uint16_t* __restric
 __device__ __forceinline__ bool sum_partials4(const float* __restrict__ part, int S, int n_tok, int N, int t, int n,
                                               u32x2* out) {
   if (n >= N) return false;
-  f32x4 v = *(const f32x4*)(part + (int64_t)t * N + n);
-  for (int z = 1; z < S; ++z) v += *(const f32x4*)(part + ((int64_t)z * n_tok + t) * N + n);
+  // four splits' loads in flight at a time, summed in split order
+  const float* p0 = part + (int64_t)t * N + n;
+  const int64_t zs = (int64_t)n_tok * N;
+  f32x4 v = *(const f32x4*)p0;
+  int z = 1;
+  for (; z + 3 < S; z += 4) {
+    const f32x4 a = *(const f32x4*)(p0 + z * zs), b = *(const f32x4*)(p0 + (z + 1) * zs);
+    const f32x4 c = *(const f32x4*)(p0 + (z + 2) * zs), d = *(const f32x4*)(p0 + (z + 3) * zs);
+    v += a;
+    v += b;
+    v += c;
+    v += d;
+  }
+  for (; z < S; ++z) v += *(const f32x4*)(p0 + z * zs);
   (*out)[0] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
   (*out)[1] = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
   return true;
@@ -173,14 +190,15 @@ __global__ void __launch_bounds__(256) q_split_kernel(const float* __restrict__ 
 
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// Split count: about 512 work-groups (two per CU) whatever the token count,
-// at least 4 k-steps per wave.  A function of the shape only, so that the
-// workspace size does not depend on the device.
+// Split count: about 256 work-groups (one per CU; 512 and 1024 measured
+// slower at 64 tokens: more, shorter work-groups and more partials) whatever
+// the token count, at least two LDS stages per split.  A function of the
+// shape only, so that the workspace size does not depend on the device.
 int gemm_splits(int64_t n_tok, int64_t N, int64_t K) {
   const int64_t tiles = ((N + kGemmFeat - 1) / kGemmFeat) * ((n_tok + kGemmTok - 1) / kGemmTok);
   const int64_t ksteps = K / 16;
-  int64_t s = (512 + tiles - 1) / tiles;
-  s = std::min<int64_t>(s, std::max<int64_t>(1, ksteps / 16));
+  int64_t s = (256 + tiles - 1) / tiles;
+  s = std::min<int64_t>(s, std::max<int64_t>(1, ksteps / 16));   // at least two LDS stages per split
   return (int)std::max<int64_t>(s, 1);
 }
 

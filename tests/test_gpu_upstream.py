@@ -19,16 +19,20 @@ from tests import _util as U
 pytestmark = pytest.mark.gpu
 
 V3 = S.WORKLOADS["v3_bs64_ctx8k"]
+# float32 accumulation of a 7168-long dot product of O(1) terms moves the value
+# before its bf16 rounding by up to about 1e-5 (a few times sqrt(448 k-steps) x
+# 2^-24); near zero that is more than a bf16 ulp of the result
+ACC_ABS = 2e-5
 
 
-def _assert_rotated_close(g, e, what):
+def _assert_rotated_close(g, e, what, abs_tol=ACC_ABS):
     """Rotated pairs whose raw value (a bf16 projection) may have rounded the other
     way on one side: the raw elements differ by at most one ulp of the pair's norm
     n (u = 2^(floor(log2 n) - 7)), the rotation keeps that difference (at most
     sqrt(2) u) and each side's final rounding adds at most u / 2: 2.5 u in all."""
     n = np.sqrt(e[..., 0::2] ** 2 + e[..., 1::2] ** 2)
     u = np.repeat(np.exp2(np.floor(np.log2(np.maximum(n, 1e-30))) - 7), 2, axis=-1)
-    ratio = np.abs(g - e) / u
+    ratio = np.maximum(np.abs(g - e) - abs_tol, 0.0) / u
     assert np.all(ratio <= 2.5), f"{what}: {int((ratio > 2.5).sum())} elements beyond 2.5 u (worst {ratio.max():.2f})"
 
 
@@ -57,7 +61,9 @@ def test_project_down_matches_oracle(cache_dtype, lens, d_cq, cuda_device):
     h64, wd64 = up["h"].double().numpy(), w_down.double().numpy()
     cq_x, ckv_x, kr_x = O.project_down(h64, wd64, d_cq, w.d_c, w.d_rope, out_dtype=None)
     if d_cq > 0:
-        U.assert_close_ulp(c_q, cq_x, "bf16", "c_q", ulps=1.0)
+        g = c_q.double().cpu().numpy()
+        ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(cq_x), 1e-30))) - 7)
+        assert np.all(np.abs(g - cq_x) <= ulp + ACC_ABS), "c_q beyond one ulp"
     # expected pool from the oracle's projections (R17: rounded once to bf16), then the append
     _, ckv_b, kr_b = O.project_down(h64, wd64, d_cq, w.d_c, w.d_rope)
     want = O.append_expected_pool(np.full(inp["n_blocks"] * bb, 0xA5, dtype=np.uint8), ckv_b, kr_b,
@@ -79,7 +85,8 @@ def test_project_down_matches_oracle(cache_dtype, lens, d_cq, cuda_device):
         # one ulp of the latent; the rotated key as bounded above
         gl, el = g[written][:, :w.d_c], e[written][:, :w.d_c]
         ulp = np.exp2(np.floor(np.log2(np.maximum(np.abs(el), 1e-30))) - 7)
-        assert np.all(np.abs(gl - el) <= ulp), "latent beyond one ulp"
+        bad = np.abs(gl - el) > ulp + ACC_ABS
+        assert not bad.any(), f"latent: {int(bad.sum())} elements beyond one ulp (+{ACC_ABS})"
         _assert_rotated_close(g[written][:, w.d_c:], e[written][:, w.d_c:], "cached k_R")
     else:
         # the decoded latent: where a code differs it is one E4M3 step away (at most 1/8 relative)
