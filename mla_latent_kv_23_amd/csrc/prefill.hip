@@ -365,6 +365,19 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
         sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[kk], sacc[t], 0, 0, 0);
       }
     }
+    // issue order per half: kKf K reads, then (MFMA, read) pairs, then the last kKf MFMAs, so that kKf
+    // reads stay in flight ahead of the MFMA chain (left to itself the compiler sinks each read to its
+    // MFMA and waits on it)
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      __builtin_amdgcn_sched_group_barrier(0x100, kKf, 0);
+#pragma unroll
+      for (int kk = 0; kk < kQk - kKf; ++kk) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, kKf, 0);
+    }
 
     // ---- softmax: lane holds query q, keys 64 kbk + 32 t + 16 (i / 8) + 8 half + i % 8
     float sv[2][16];
