@@ -14,11 +14,12 @@
 //  1. prefill_rope_kernel: q_R' [Tq, H, 64] (and, for packed keys, k_R'
 //     [Tk, 64]) in bf16, by the RoPE rule of the absorb and append kernels
 //     (fp64 angle, fp32 cos/sin, fp64 rotation, one rounding); cos/sin once
-//     per (token, pair).  For paged keys, prefill_gather_kernel copies the
-//     cached k_R' rows and records each key's physical cache row.
+//     per (token, pair).  For paged keys, prefill_gather_kernel packs each
+//     key's cache row (latent and rotated k_R) into the workspace.
 //  2. prefill_decompress_kernel: k_C [T, H, 128] and v [T, H, 128] in bf16, a
-//     bf16 MFMA GEMM with fp32 accumulation: a 128-dim x 128-token tile of one
-//     head per work-group, the 512-long contraction in chunks of 64 through LDS.
+//     bf16 MFMA GEMM with fp32 accumulation: each wave holds its 32 weight rows
+//     in registers, and the latent streams through LDS, 32 tokens at a time,
+//     shared by the K and V waves of a head.
 //  3. prefill_attn_kernel: causal flash attention per (sequence, head, block of
 //     128 queries), one wave per 32 queries:
 //     * key blocks of 64 rows [k_C | k_R | v] (640 B) are staged in LDS with
@@ -33,6 +34,8 @@
 //     * O^T += V^T P^T on MFMA, V^T from the staged rows by transpose reads;
 //     * with an output gate (gated MLA), out = sigmoid(gate) * o before the
 //       one rounding to bf16.
+#include <algorithm>
+
 #include "decode_tile.h"
 
 namespace mla {
@@ -91,32 +94,50 @@ __global__ void __launch_bounds__(256) prefill_rope_kernel(const uint16_t* __res
   }
 }
 
-// Paged keys: one thread per (key token, 16-byte piece of k_R'): the physical
-// cache row of key t (block_table[b][p / block_size] * block_size + p % block_size,
-// p its position) goes to rowmap[t], and its rotated k_R (bf16, the last d_R
-// entries of the row) is copied to kr_out[t].
+// Paged keys: one thread per (key token, 16-byte piece of its cache row):
+// the row of key t (block_table[b][p / block_size] * block_size + p %
+// block_size, p its position) is copied into the packed latent [t][d_c] and
+// the packed rotated key [t][d_R] (the cache holds k_R already rotated).
 __global__ void __launch_bounds__(256) prefill_gather_kernel(const uint16_t* __restrict__ pool,
                                                              const int32_t* __restrict__ block_table, int max_blocks,
                                                              int block_size, const int32_t* __restrict__ cu_k,
-                                                             int n_seq, int total_k, int32_t* __restrict__ rowmap,
+                                                             int n_seq, int total_k, uint16_t* __restrict__ c_out,
                                                              uint16_t* __restrict__ kr_out) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  const int t = i >> 3, piece = i & 7;
+  constexpr int kPieces = (kPfDc + kPfDr) / 8;   // 72 pieces of 16 bytes per row
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int t = (int)(i / kPieces), piece = (int)(i % kPieces);
   if (t >= total_k) return;
   const int b = pf_seq_of(cu_k, n_seq, t);
   const int p = t - cu_k[b];
   const int row = block_table[(int64_t)b * max_blocks + p / block_size] * block_size + p % block_size;
-  if (piece == 0) rowmap[t] = row;
-  *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * piece) =
-      *(const u32x4*)(pool + (int64_t)row * (kPfDc + kPfDr) + kPfDc + 8 * piece);
+  const u32x4 v = *(const u32x4*)(pool + (int64_t)row * (kPfDc + kPfDr) + 8 * piece);
+  if (piece < kPfDc / 8) *(u32x4*)(c_out + (int64_t)t * kPfDc + 8 * piece) = v;
+  else *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * (piece - kPfDc / 8)) = v;
 }
+
+// one direct-to-LDS load of 16 bytes per lane: LDS m0 + 16 lane <- src + voff
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void* src, uint32_t voff, uint32_t m0) {
+  const uint64_t a = (uint64_t)(uintptr_t)src;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  const uint64_t sv = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane(m0);
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v], %[s]"
+               :
+               : [v] "v"(voff), [s] "s"(sv), [m] "s"(m)
+               : "memory", "m0");
+}
+#pragma clang diagnostic pop
 
 // ---------------------------------------------------------------- 2. decompression
 
-constexpr int kDcTok = 128;                  // tokens per tile
-constexpr int kDcChunk = 64;                 // contraction chunk
-constexpr int kDcRow = kDcChunk * 2 + 16;    // LDS row bytes, padded: 16 rows at one 16-byte slot hit distinct banks
-constexpr int kDcBuf = 2 * 128 * kDcRow;     // one buffer: 128 weight rows, then 128 token rows
+constexpr int kDcTok = 32;                   // tokens per LDS stage
+constexpr int kDcStages = 4;                 // stage ring depth (three stages in flight)
+constexpr int kDcStageB = kDcTok * kPfDc * 2;   // 32 KB: 32 latent rows of 1 KB
+constexpr int kDcKs = kPfDc / 16;            // 32 k-steps
+constexpr int kDcAhead = 8;                  // latent fragments read ahead of the MFMA chain
 
 __device__ __forceinline__ u32x2 pf_pack4(float a, float b, float c, float d) {
   u32x2 r;
@@ -125,92 +146,103 @@ __device__ __forceinline__ u32x2 pf_pack4(float a, float b, float c, float d) {
   return r;
 }
 
-// grid (ceil(T / 128), H, 2): z = 0 writes k_C with W_UK, z = 1 writes v with W_UV.
-// out^T tile (128 dims x 128 tokens) = W[s] (dims x 512) c^T (512 x tokens);
-// wave w computes dims 64(w % 2) .. +63 x tokens 64(w / 2) .. +63 (2 x 2 MFMA tiles).
-// The latent of key t is row (rowmap ? rowmap[t] : t) of c_rows, c_stride
-// elements apart (packed c_KV, or the rows of the paged cache).
-__global__ void __launch_bounds__(256) prefill_decompress_kernel(const uint16_t* __restrict__ c_rows,
-                                                                 const int32_t* __restrict__ rowmap, int c_stride,
-                                                                 const uint16_t* __restrict__ w_uk,
-                                                                 const uint16_t* __restrict__ w_uv,
-                                                                 uint16_t* __restrict__ kc, uint16_t* __restrict__ vv,
-                                                                 int T, int H) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds_raw[2 * kDcBuf];
-  lds_u8* lds = (lds_u8*)lds_raw;
-  const int s = blockIdx.y, t0 = blockIdx.x * kDcTok;
-  const uint16_t* W = (blockIdx.z == 0 ? w_uk : w_uv) + (int64_t)s * kPfDv * kPfDc;
-  uint16_t* out = blockIdx.z == 0 ? kc : vv;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, half = lane >> 5;
-  const int wm = wave & 1, wn = wave >> 1;
+// grid H * G, block 512 (8 waves).  Work-group (head s, token group g) writes
+// k_C = W_UK[s] c (waves 0-3, dims 32 w ..) and v = W_UV[s] c (waves 4-7) for
+// the 32-token tiles of group g.  Each wave keeps its 32 weight rows (the whole
+// 512-long contraction, 128 VGPRs) in registers for the life of the
+// work-group, so only the latent streams: 32 tokens x 1 KB per stage through a
+// four-stage LDS ring filled by direct-to-LDS loads (one 1 KB row per
+// instruction, 16-byte chunk p of row r holding logical chunk p ^ (r % 8), so
+// that eight rows read at one chunk hit distinct banks), three stages in
+// flight.  The K and V halves share every latent tile; the work-groups of
+// one token group run on one XCD and share the tiles in its L2.
+__global__ void __launch_bounds__(512, 1) prefill_decompress_kernel(const uint16_t* __restrict__ c_kv,
+                                                                    const uint16_t* __restrict__ w_uk,
+                                                                    const uint16_t* __restrict__ w_uv,
+                                                                    uint16_t* __restrict__ kc, uint16_t* __restrict__ vv,
+                                                                    int T, int H, int G) {
+  __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kDcStages * kDcStageB];
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_u8*)lds_raw;
+  const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5, lr = lane & 31;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int u = xcd_unit(blockIdx.x, H * G);
+  const int g = u / H, s = u % H;
+  const int n_tiles = (T + kDcTok - 1) / kDcTok;
+  const int j0 = (int)((int64_t)g * n_tiles / G), nt = (int)((int64_t)(g + 1) * n_tiles / G) - j0;
+  if (nt <= 0) return;
+  const bool is_v = wave >= 4;
+  const int d0 = 32 * (wave & 3);
 
-  // staging: piece p = tid + 256 j (j < 4) is 16 bytes, row p / 8, part p % 8 of the chunk
-  const uint16_t* csrc[4];
+  // this wave's weight rows as MFMA A fragments: row d0 + lane % 32, k-step ks: elements 16 ks + 8 half .. +7
+  bf16x8 af[kDcKs];
+  {
+    const bf16x8* wr = (const bf16x8*)((is_v ? w_uv : w_uk) + ((int64_t)s * kPfDv + d0 + lr) * kPfDc) + half;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int p = tid + 256 * j, row = p >> 3, part = p & 7;
-    const int t = min(t0 + row, T - 1);
-    csrc[j] = c_rows + (int64_t)(rowmap ? rowmap[t] : t) * c_stride + 8 * part;
+    for (int ks = 0; ks < kDcKs; ++ks) af[ks] = wr[2 * ks];
   }
-  u32x4 wreg[4], creg[4];
-  auto load_chunk = [&](int kc0) {
+  __builtin_amdgcn_s_waitcnt(0);             // weights resident before the first stage load is queued
+
+  // stage loads: wave w brings rows 4w .. 4w+3 of a tile, one row per instruction
+  auto issue = [&](int j) {
+    const uint32_t stage = lds0 + (uint32_t)((j % kDcStages) * kDcStageB);
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = tid + 256 * j, row = p >> 3, part = p & 7;
-      wreg[j] = *(const u32x4*)(W + (int64_t)row * kPfDc + kc0 + 8 * part);
-      creg[j] = *(const u32x4*)(csrc[j] + kc0);
+    for (int rr = 0; rr < 4; ++rr) {
+      const int r = 4 * wave + rr;
+      const int t = min((j0 + j) * kDcTok + r, T - 1);   // past the end: the last token (finite, not stored)
+      dma16(c_kv + (int64_t)t * kPfDc, (uint32_t)(16 * (lane ^ (r & 7))), stage + (uint32_t)(r * 1024));
     }
   };
-  auto store_chunk = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int p = tid + 256 * j, row = p >> 3, part = p & 7;
-      *(lds_u32x4*)(lds + buf * kDcBuf + row * kDcRow + 16 * part) = wreg[j];
-      *(lds_u32x4*)(lds + buf * kDcBuf + (128 + row) * kDcRow + 16 * part) = creg[j];
+  // operations this wave queued after tile j's loads, when it waits for them: the
+  // loads of tiles j+1, j+2 and the stores of tiles j-3 .. j-1 (four each)
+  auto wait_tile = [&](int j) {
+    const int n = min(2, nt - 1 - j) + min(3, j);
+    switch (n) {
+      case 0: wait_vmcnt<0>(); break;
+      case 1: wait_vmcnt<4>(); break;
+      case 2: wait_vmcnt<8>(); break;
+      case 3: wait_vmcnt<12>(); break;
+      case 4: wait_vmcnt<16>(); break;
+      default: wait_vmcnt<20>(); break;
     }
   };
 
-  f32x16 acc[2][2];
+  for (int j = 0; j < min(kDcStages - 1, nt); ++j) issue(j);
+  uint16_t* out = (is_v ? vv : kc) + (int64_t)s * kPfDv + d0 + 4 * half;
+  for (int j = 0; j < nt; ++j) {
+    wait_tile(j);
+    lds_barrier();                           // every wave's rows of tile j have landed; stage j-1 is free
+    if (j + kDcStages - 1 < nt) issue(j + kDcStages - 1);
+    const uint32_t stage = lds0 + (uint32_t)((j % kDcStages) * kDcStageB);
+    const uint32_t brow = stage + (uint32_t)(lr * 1024);
+    f32x16 acc = f32x16{};
+    bf16x8 bf[kDcAhead];
 #pragma unroll
-  for (int a = 0; a < 2; ++a)
+    for (int ks = 0; ks < kDcAhead; ++ks)
+      bf[ks] = *(const lds_bf16x8*)(uintptr_t)(brow + 16 * ((2 * ks + half) ^ (lr & 7)));
 #pragma unroll
-    for (int b = 0; b < 2; ++b) acc[a][b] = f32x16{};
-
-  load_chunk(0);
-  store_chunk(0);
-  __syncthreads();
-  constexpr int kChunks = kPfDc / kDcChunk;
-  for (int ch = 0; ch < kChunks; ++ch) {
-    if (ch + 1 < kChunks) load_chunk((ch + 1) * kDcChunk);
-    const lds_u8* base = lds + (ch & 1) * kDcBuf;
-#pragma unroll
-    for (int ks = 0; ks < kDcChunk / 16; ++ks) {
-      bf16x8 af[2], bf[2];
-#pragma unroll
-      for (int x = 0; x < 2; ++x) {
-        af[x] = *(const lds_bf16x8*)(base + (64 * wm + 32 * x + (lane & 31)) * kDcRow + (16 * ks + 8 * half) * 2);
-        bf[x] = *(const lds_bf16x8*)(base + (128 + 64 * wn + 32 * x + (lane & 31)) * kDcRow + (16 * ks + 8 * half) * 2);
-      }
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int b = 0; b < 2; ++b) acc[a][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[a], bf[b], acc[a][b], 0, 0, 0);
+    for (int ks = 0; ks < kDcKs; ++ks) {
+      const bf16x8 cur = bf[ks % kDcAhead];
+      if (ks + kDcAhead < kDcKs)
+        bf[ks % kDcAhead] = *(const lds_bf16x8*)(uintptr_t)(brow + 16 * ((2 * (ks + kDcAhead) + half) ^ (lr & 7)));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], cur, acc, 0, 0, 0);
     }
-    if (ch + 1 < kChunks) store_chunk((ch + 1) & 1);
-    __syncthreads();
-  }
-  // tile (a, b): lane holds token 64 wn + 32 b + lane % 32, dims 64 wm + 32 a + 8 (i / 4) + 4 half + i % 4
+    __builtin_amdgcn_sched_group_barrier(0x100, kDcAhead, 0);
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int t = t0 + 64 * wn + 32 * b + (lane & 31);
-    if (t >= T) continue;
-    uint16_t* dst = out + ((int64_t)t * H + s) * kPfDv + 64 * wm + 4 * half;
+    for (int ks = 0; ks < kDcKs - kDcAhead; ++ks) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, kDcAhead, 0);
+    // lane holds token (j0 + j) 32 + lane % 32, dims d0 + 8 g + 4 half + 0..3 (g = i / 4); four
+    // stores per tile (the clamped tokens of a partial last tile store to their own row: rows past
+    // T are skipped by the lane's predicate, the instructions still issue)
+    const int t = (j0 + j) * kDcTok + lr;
+    if (t < T) {
+      uint16_t* dst = out + (int64_t)t * H * kPfDv;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(u32x2*)(dst + 32 * a + 8 * g) =
-            pf_pack4(acc[a][b][4 * g], acc[a][b][4 * g + 1], acc[a][b][4 * g + 2], acc[a][b][4 * g + 3]);
+      for (int gg = 0; gg < 4; ++gg)
+        *(u32x2*)(dst + 8 * gg) = pf_pack4(acc[4 * gg], acc[4 * gg + 1], acc[4 * gg + 2], acc[4 * gg + 3]);
+    }
   }
 }
 
@@ -243,21 +275,7 @@ struct PrefillArgs {
   float scale_log2;
 };
 
-// one direct-to-LDS load of 16 bytes per lane: LDS m0 + 16 lane <- src + voff
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void dma16(const void* src, uint32_t voff, uint32_t m0) {
-  const uint64_t a = (uint64_t)(uintptr_t)src;
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
-  const uint64_t sv = ((uint64_t)hi << 32) | (uint64_t)lo;
-  const uint32_t m = (uint32_t)__builtin_amdgcn_readfirstlane(m0);
-  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v], %[s]"
-               :
-               : [v] "v"(voff), [s] "s"(sv), [m] "s"(m)
-               : "memory", "m0");
-}
-#pragma clang diagnostic pop
+
 
 __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[2 * kStage];
@@ -495,11 +513,11 @@ size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 // for paged keys, the key row map [Tk] (int32); 256-byte aligned pieces
 struct PrefillWs {
   uint16_t *kc, *vv, *qr, *kr;
-  int32_t* rowmap;
+  uint16_t* ckv;   // paged keys: the packed latent rows
 };
 size_t prefill_ws_bytes(int64_t tq, int64_t tk, int64_t H, bool paged) {
   return up256(tk * H * kPfDn * 2) + up256(tk * H * kPfDv * 2) + up256(tq * H * kPfDr * 2) + up256(tk * kPfDr * 2) +
-         (paged ? up256(tk * 4) : 0);
+         (paged ? up256(tk * kPfDc * 2) : 0);
 }
 PrefillWs carve(void* ws, int64_t tq, int64_t tk, int64_t H) {
   uint8_t* p = static_cast<uint8_t*>(ws);
@@ -512,8 +530,17 @@ PrefillWs carve(void* ws, int64_t tq, int64_t tk, int64_t H) {
   p += up256(tq * H * kPfDr * 2);
   w.kr = reinterpret_cast<uint16_t*>(p);
   p += up256(tk * kPfDr * 2);
-  w.rowmap = reinterpret_cast<int32_t*>(p);
+  w.ckv = reinterpret_cast<uint16_t*>(p);
   return w;
+}
+
+void launch_decompress(const mla_dims& d, const uint16_t* c_kv, const void* w_uk, const void* w_uv, const PrefillWs& w,
+                       int32_t total_k, hipStream_t st) {
+  // token groups: about one work-group per CU (256) over the heads
+  const int G = std::max(1, std::min(256 / std::max(d.n_heads, 1), (total_k + kDcTok - 1) / kDcTok));
+  hipLaunchKernelGGL(prefill_decompress_kernel, dim3(d.n_heads * G), dim3(512), 0, st, c_kv,
+                     static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv), w.kc, w.vv, total_k,
+                     d.n_heads, G);
 }
 
 void launch_attention(const mla_dims& d, int32_t n_seq, const int32_t* cu_q, const int32_t* cu_k, int32_t max_q,
@@ -555,9 +582,7 @@ mla_status launch_prefill(const mla_dims& d, int32_t n_seq, const int32_t* cu_se
   const RopeFreqs f = make_rope_freqs(d);
   hipLaunchKernelGGL(prefill_rope_kernel, dim3(total_tokens), dim3(256), 0, st, static_cast<const uint16_t*>(q_rope),
                      static_cast<const uint16_t*>(k_rope), cu_seqlens, cu_seqlens, n_seq, d.n_heads, w.qr, w.kr, f);
-  hipLaunchKernelGGL(prefill_decompress_kernel, dim3((total_tokens + kDcTok - 1) / kDcTok, d.n_heads, 2), dim3(256), 0,
-                     st, static_cast<const uint16_t*>(c_kv), nullptr, kPfDc, static_cast<const uint16_t*>(w_uk),
-                     static_cast<const uint16_t*>(w_uv), w.kc, w.vv, total_tokens, d.n_heads);
+  launch_decompress(d, static_cast<const uint16_t*>(c_kv), w_uk, w_uv, w, total_tokens, st);
   launch_attention(d, n_seq, cu_seqlens, cu_seqlens, max_seqlen, q_nope, w, gate, out, lse, st);
   return launch_status();
 }
@@ -572,11 +597,9 @@ mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t*
   const uint16_t* pool = static_cast<const uint16_t*>(cache_pool);
   hipLaunchKernelGGL(prefill_rope_kernel, dim3(total_q), dim3(256), 0, st, static_cast<const uint16_t*>(q_rope),
                      nullptr, cu_q, cu_k, n_seq, d.n_heads, w.qr, nullptr, f);
-  hipLaunchKernelGGL(prefill_gather_kernel, dim3((unsigned)(((int64_t)total_k * 8 + 255) / 256)), dim3(256), 0, st,
-                     pool, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k, w.rowmap, w.kr);
-  hipLaunchKernelGGL(prefill_decompress_kernel, dim3((total_k + kDcTok - 1) / kDcTok, d.n_heads, 2), dim3(256), 0, st,
-                     pool, w.rowmap, kPfDc + kPfDr, static_cast<const uint16_t*>(w_uk),
-                     static_cast<const uint16_t*>(w_uv), w.kc, w.vv, total_k, d.n_heads);
+  hipLaunchKernelGGL(prefill_gather_kernel, dim3((unsigned)(((int64_t)total_k * 72 + 255) / 256)), dim3(256), 0, st,
+                     pool, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k, w.ckv, w.kr);
+  launch_decompress(d, w.ckv, w_uk, w_uv, w, total_k, st);
   launch_attention(d, n_seq, cu_q, cu_k, max_q, q_nope, w, gate, out, lse, st);
   return launch_status();
 }
