@@ -510,7 +510,7 @@ namespace {
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 // workspace: k_C, v [Tk][H][128], q_R' [Tq][H][64], k_R' [Tk][64] (bf16), then,
-// for paged keys, the key row map [Tk] (int32); 256-byte aligned pieces
+// for paged keys, the packed latent rows [Tk][d_c] (bf16); 256-byte aligned pieces
 struct PrefillWs {
   uint16_t *kc, *vv, *qr, *kr;
   uint16_t* ckv;   // paged keys: the packed latent rows
