@@ -68,8 +68,10 @@ def measured_traffic():
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the chip needs tens of ms of work to reach its steady clocks: with 5 warm-up steps the
+    # first timed steps run ~10% slower than the steady state a serving loop sees
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--workload", default="v3_bs64_ctx8k")
     ap.add_argument("--num-splits", type=int, default=0)
     ap.add_argument("--cpu-sample-seqs", type=int, default=16,
@@ -111,6 +113,7 @@ class TimingEvent:
             rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
             TimingEvent._rt = rt
         self._ct = ctypes
+        self._rt = TimingEvent._rt   # kept for __del__ at interpreter exit, when module globals may be gone
         self.h = ctypes.c_void_p()
         self._ok(TimingEvent._rt.hipEventCreateWithFlags(ctypes.byref(self.h), self.DISABLE_SYSTEM_FENCE))
 
@@ -128,8 +131,8 @@ class TimingEvent:
         return ms.value
 
     def __del__(self):
-        if TimingEvent._rt is not None and self.h:
-            TimingEvent._rt.hipEventDestroy(self.h)
+        if getattr(self, "_rt", None) is not None and self.h:
+            self._rt.hipEventDestroy(self.h)
 
 
 def calib_copy(mib):
