@@ -218,9 +218,11 @@ def decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scal
     explicitly, key = [k_C | k_R], query = [q_nope | RoPE(q_R)], and standard
     causal softmax attention runs over tokens t <= position of the query.
     Returns o [s_q, h, d_v], o_lat [s_q, h, d_c], lse [s_q, h] over the chosen heads.
-    operand_dtype (e.g. "bf16"): round the rotated query part and the
-    decompressed k_C and v to that storage type before the attention, the
-    points where a kernel that runs this form on bf16 matrix units rounds them.
+    operand_dtype (e.g. "bf16"): round the latent, the rotated query part and
+    the decompressed k_C and v to that storage type before they are used, the
+    points where a kernel that runs this form on bf16 matrix units rounds them
+    (the latent of a bf16 cache is already on that grid; an fp8 one,
+    code * scale, is rounded once).
     """
     q_nope = np.asarray(q_nope, dtype=F64)
     q_pos = np.asarray(q_pos, dtype=np.int64)
@@ -228,8 +230,10 @@ def decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scal
     L = c_cached.shape[0]
     heads = list(range(H)) if heads is None else list(heads)
     qr = rope(q_rope, q_pos[:, None], base)                              # [s_q, H, d_R]
+    c_cached = np.asarray(c_cached, dtype=F64)
     if operand_dtype is not None:
         qr = store_value(qr, operand_dtype)
+        c_cached = store_value(c_cached, operand_dtype)
     visible = np.arange(L)[None, :] <= q_pos[:, None]                   # [s_q, L]
     o = np.zeros((s_q, len(heads), w_uv.shape[1]))
     o_lat = np.zeros((s_q, len(heads), c_cached.shape[1]))
