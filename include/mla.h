@@ -310,8 +310,9 @@ mla_status mla_prefill(const mla_dims* dims, int32_t n_seq, const int32_t* cu_se
  * [total_q, H, d_nope], q_rope [total_q, H, d_rope] (unrotated), w_uk, w_uv,
  * gate (null or [total_q, H, d_v]), out [total_q, H, d_v] and lse [total_q, H]
  * as mla_prefill.  workspace: at least mla_prefill_paged_workspace_bytes,
- * 16-byte aligned.  Supported: the dims of mla_prefill with a bf16 cache (else
- * MLA_ERR_UNSUPPORTED).  total_q = 0 launches nothing.
+ * 16-byte aligned.  Supported: the dims of mla_prefill with a bf16 or fp8
+ * cache (else MLA_ERR_UNSUPPORTED); an fp8 latent enters the decompression as
+ * bf16(code * scale), rounded once.  total_q = 0 launches nothing.
  */
 size_t mla_prefill_paged_workspace_bytes(const mla_dims* dims, int32_t total_q, int32_t total_k);
 mla_status mla_prefill_paged(const mla_dims* dims, int32_t n_seq, const int32_t* cu_q,

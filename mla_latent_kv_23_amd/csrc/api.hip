@@ -272,7 +272,7 @@ mla_status mla_prefill(const mla_dims* d, int32_t n_seq, const int32_t* cu_seqle
 }
 
 size_t mla_prefill_paged_workspace_bytes(const mla_dims* d, int32_t total_q, int32_t total_k) {
-  if (dims_supported(d) != MLA_OK || !prefill_supported(*d) || d->cache_dtype != MLA_BF16 || total_q < 0 ||
+  if (dims_supported(d) != MLA_OK || !prefill_supported(*d) || d->cache_dtype == MLA_F32 || total_q < 0 ||
       total_k < 0)
     return 0;
   return prefill_paged_workspace_bytes(*d, total_q, total_k);
@@ -285,7 +285,7 @@ mla_status mla_prefill_paged(const mla_dims* d, int32_t n_seq, const int32_t* cu
                              size_t workspace_bytes, void* out, float* lse, mla_stream_t stream) {
   const mla_status s = dims_supported(d);
   if (s != MLA_OK) return s;
-  if (!prefill_supported(*d) || d->cache_dtype != MLA_BF16) return MLA_ERR_UNSUPPORTED;
+  if (!prefill_supported(*d) || d->cache_dtype == MLA_F32) return MLA_ERR_UNSUPPORTED;
   if (n_seq <= 0 || total_q < 0 || max_q < 0 || total_k < 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
   if (total_q == 0) return MLA_OK;
   if (!cu_q || !cu_k || !q_nope || !q_rope || !cache_pool || !block_table || !w_uk || !w_uv || !out || !lse)

@@ -94,25 +94,65 @@ __global__ void __launch_bounds__(256) prefill_rope_kernel(const uint16_t* __res
   }
 }
 
+// bf16(code * scale) rounded once (to nearest even) from the exact product: the
+// product of a 4-bit and a 24-bit significand is exact in fp64; it is
+// narrowed to fp32 rounding to odd (toward zero, then the last bit set when
+// inexact), which keeps the final rounding to bf16 a single correct one.
+__device__ __forceinline__ uint16_t pf_scaled_bf16(float code, float scale) {
+  const double x = (double)code * (double)scale;
+  float f = __double2float_rz(x);
+  if ((double)f != x) f = __uint_as_float(__float_as_uint(f) | 1u);
+  return f32_to_bf16_bits(f);
+}
+
 // Paged keys: one thread per (key token, 16-byte piece of its cache row):
 // the row of key t (block_table[b][p / block_size] * block_size + p %
 // block_size, p its position) is copied into the packed latent [t][d_c] and
 // the packed rotated key [t][d_R] (the cache holds k_R already rotated).
-__global__ void __launch_bounds__(256) prefill_gather_kernel(const uint16_t* __restrict__ pool,
+// fp8 cache: the latent is dequantised, code * scale rounded once to bf16
+// (the E4M3FN code converts to bf16 exactly); 16 codes per thread.
+template <bool kFp8>
+__global__ void __launch_bounds__(256) prefill_gather_kernel(const uint8_t* __restrict__ pool, int64_t block_bytes,
                                                              const int32_t* __restrict__ block_table, int max_blocks,
                                                              int block_size, const int32_t* __restrict__ cu_k,
                                                              int n_seq, int total_k, uint16_t* __restrict__ c_out,
                                                              uint16_t* __restrict__ kr_out) {
-  constexpr int kPieces = (kPfDc + kPfDr) / 8;   // 72 pieces of 16 bytes per row
+  constexpr int kCPieces = kFp8 ? kPfDc / 16 : kPfDc / 8;   // latent pieces (16 codes or 8 bf16 each)
+  constexpr int kPieces = kCPieces + kPfDr / 8;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
   const int t = (int)(i / kPieces), piece = (int)(i % kPieces);
   if (t >= total_k) return;
   const int b = pf_seq_of(cu_k, n_seq, t);
   const int p = t - cu_k[b];
-  const int row = block_table[(int64_t)b * max_blocks + p / block_size] * block_size + p % block_size;
-  const u32x4 v = *(const u32x4*)(pool + (int64_t)row * (kPfDc + kPfDr) + 8 * piece);
-  if (piece < kPfDc / 8) *(u32x4*)(c_out + (int64_t)t * kPfDc + 8 * piece) = v;
-  else *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * (piece - kPfDc / 8)) = v;
+  const int64_t blk = block_table[(int64_t)b * max_blocks + p / block_size];
+  const int slot = p % block_size;
+  const uint8_t* base = pool + blk * block_bytes;
+  if constexpr (!kFp8) {
+    const u32x4 v = *(const u32x4*)(base + ((int64_t)slot * (kPfDc + kPfDr) + 8 * piece) * 2);
+    if (piece < kCPieces) *(u32x4*)(c_out + (int64_t)t * kPfDc + 8 * piece) = v;
+    else *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * (piece - kCPieces)) = v;
+  } else {
+    if (piece < kCPieces) {
+      const u32x4 codes = *(const u32x4*)(base + (int64_t)slot * kPfDc + 16 * piece);
+      const float scale = *(const float*)(base + (int64_t)block_size * kPfDc + 4 * slot);
+      uint32_t outw[8];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], 1.0f, false);   // codes 4w, 4w+1
+        const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], 1.0f, true);    // codes 4w+2, 4w+3
+        outw[2 * w] = (uint32_t)pf_scaled_bf16((float)lo[0], scale) | ((uint32_t)pf_scaled_bf16((float)lo[1], scale) << 16);
+        outw[2 * w + 1] =
+            (uint32_t)pf_scaled_bf16((float)hi[0], scale) | ((uint32_t)pf_scaled_bf16((float)hi[1], scale) << 16);
+      }
+      u32x4* dst = (u32x4*)(c_out + (int64_t)t * kPfDc + 16 * piece);
+      dst[0] = u32x4{outw[0], outw[1], outw[2], outw[3]};
+      dst[1] = u32x4{outw[4], outw[5], outw[6], outw[7]};
+    } else {
+      const int q = piece - kCPieces;
+      *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * q) =
+          *(const u32x4*)(base + (int64_t)block_size * (kPfDc + 4) + ((int64_t)slot * kPfDr + 8 * q) * 2);
+    }
+  }
 }
 
 // one direct-to-LDS load of 16 bytes per lane: LDS m0 + 16 lane <- src + voff
@@ -594,11 +634,16 @@ mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t*
                                 hipStream_t st) {
   const PrefillWs w = carve(ws, total_q, total_k, d.n_heads);
   const RopeFreqs f = make_rope_freqs(d);
-  const uint16_t* pool = static_cast<const uint16_t*>(cache_pool);
   hipLaunchKernelGGL(prefill_rope_kernel, dim3(total_q), dim3(256), 0, st, static_cast<const uint16_t*>(q_rope),
                      nullptr, cu_q, cu_k, n_seq, d.n_heads, w.qr, nullptr, f);
-  hipLaunchKernelGGL(prefill_gather_kernel, dim3((unsigned)(((int64_t)total_k * 72 + 255) / 256)), dim3(256), 0, st,
-                     pool, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k, w.ckv, w.kr);
+  const int64_t bb = (int64_t)mla_cache_block_bytes(&d);
+  const uint8_t* pool8 = static_cast<const uint8_t*>(cache_pool);
+  if (d.cache_dtype == MLA_FP8_E4M3)
+    hipLaunchKernelGGL(prefill_gather_kernel<true>, dim3((unsigned)(((int64_t)total_k * 40 + 255) / 256)), dim3(256), 0,
+                       st, pool8, bb, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k, w.ckv, w.kr);
+  else
+    hipLaunchKernelGGL(prefill_gather_kernel<false>, dim3((unsigned)(((int64_t)total_k * 72 + 255) / 256)), dim3(256), 0,
+                       st, pool8, bb, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k, w.ckv, w.kr);
   launch_decompress(d, w.ckv, w_uk, w_uv, w, total_k, st);
   launch_attention(d, n_seq, cu_q, cu_k, max_q, q_nope, w, gate, out, lse, st);
   return launch_status();

@@ -159,5 +159,7 @@ def test_prefill_paged_arguments_are_checked_before_launch(lib):
     bad = list(args); bad[3] = 0
     assert lib.mla_prefill_paged(*bad) == 0
     fp8 = M.make_dims(**V3, cache_dtype="fp8")
-    assert lib.mla_prefill_paged_workspace_bytes(ctypes.byref(fp8), 50, 400) == 0
-    assert lib.mla_prefill_paged(ctypes.byref(fp8), *args[1:]) == 2
+    assert lib.mla_prefill_paged_workspace_bytes(ctypes.byref(fp8), 50, 400) == ws
+    f32 = M.make_dims(n_heads=4, d_c=64, d_rope=16, d_nope=32, d_v=32, act_dtype="f32", cache_dtype="f32")
+    assert lib.mla_prefill_paged_workspace_bytes(ctypes.byref(f32), 50, 400) == 0
+    assert lib.mla_prefill_paged(ctypes.byref(f32), *args[1:]) == 2

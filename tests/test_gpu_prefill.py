@@ -47,19 +47,22 @@ def test_prefill_rejects_unsupported_dims(cuda_device):
     assert M.prefill_workspace_bytes(d, 10) == 0
 
 
-@pytest.mark.parametrize("heads,lens,qlens", [
-    (16, [1000, 129, 64, 300], [70, 1, 64, 300]),    # prefix + chunk, one query, one whole block, whole prompt
-    (128, [700, 200], [200, 33]),
-    (16, [5000, 77], [129, 0]),                       # a sequence with no queries
+@pytest.mark.parametrize("heads,lens,qlens,cache", [
+    (16, [1000, 129, 64, 300], [70, 1, 64, 300], "bf16"),    # prefix + chunk, one query, one block, whole prompt
+    (128, [700, 200], [200, 33], "bf16"),
+    (16, [5000, 77], [129, 0], "bf16"),                       # a sequence with no queries
+    (16, [1000, 129, 64], [70, 1, 64], "fp8"),
+    (128, [700, 200], [200, 33], "fp8"),
 ])
-def test_prefill_paged_matches_oracle(heads, lens, qlens, cuda_device):
+def test_prefill_paged_matches_oracle(heads, lens, qlens, cache, cuda_device):
     """Chunked prefill: each sequence's newest tokens (already in the paged cache,
-    written by the library's append) attend to the whole cached prompt."""
+    written by the library's append) attend to the whole cached prompt.  With an
+    fp8 cache the latent enters as bf16(code * scale) on both sides."""
     import mla_latent_kv_23_amd as M
-    w = V3.replace(n_heads=heads)
+    w = V3.replace(n_heads=heads, cache_dtype=cache)
     inp = S.make_chunk_prefill_inputs(w, 600 + heads + len(lens), torch.tensor(lens, dtype=torch.int32),
                                       torch.tensor(qlens, dtype=torch.int32))
-    U.say(f"[prefill_paged] H={heads} lens={lens} qlens={qlens}")
+    U.say(f"[prefill_paged] H={heads} lens={lens} qlens={qlens} cache={cache}")
     d = U.dims_of(w)
     dev = cuda_device
     pool = U.gpu_pool(w, inp, dev)
