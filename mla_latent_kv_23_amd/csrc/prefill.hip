@@ -375,8 +375,8 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
   // blocks per 8 rows; lane l: row 16w + 8g + l/8, logical chunk 8cb + ((l % 8) ^ swz(l / 8))
   const int last_key = min(L, off + q0 + kQBlk) - 1;
   const int n_kblk = last_key / kKBlk + 1;
-  auto load_stage = [&](int kbk) {
-    const uint32_t dst = (uint32_t)(uintptr_t)(lds + (kbk & 1) * kStage);
+  auto load_stage = [&](int kbk, int par) {   // par = kbk % 2 (a constant where the caller knows it)
+    const uint32_t dst = (uint32_t)(uintptr_t)(lds + par * kStage);
     const int key0 = kbk * kKBlk;
     const int64_t row0 = ck0 + key0;
 #pragma unroll
@@ -401,12 +401,13 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) o[i] = f32x16{};
 
-  load_stage(0);
-  for (int kbk = 0; kbk < n_kblk; ++kbk) {
+  // one key block; par = kbk % 2 is a constant in each of the two calls below, so the stage
+  // base folds into the LDS instructions' immediate offsets
+  auto block = [&](int kbk, int par) {
     wait_vmcnt<0>();                         // this wave's share of stage kbk has landed
     lds_barrier();                           // ... and everyone's; stage kbk-1 is free
-    if (kbk + 1 < n_kblk) load_stage(kbk + 1);
-    const uint32_t tb = (uint32_t)(uintptr_t)(lds + (kbk & 1) * kStage);
+    if (kbk + 1 < n_kblk) load_stage(kbk + 1, par ^ 1);
+    const uint32_t tb = (uint32_t)(uintptr_t)(lds + par * kStage);
 
     // ---- S^T for the two 32-key halves
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
@@ -504,6 +505,11 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
         const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
         o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], o[db], 0, 0, 0);
       }
+  };
+  load_stage(0, 0);
+  for (int kbk = 0; kbk < n_kblk; kbk += 2) {
+    block(kbk, 0);
+    if (kbk + 1 < n_kblk) block(kbk + 1, 1);
   }
 
   // ---- normalise and store: O^T tile db, lane holds query qw + lr, dims 32 db + 8 (i / 4) + 4 half + i % 4
