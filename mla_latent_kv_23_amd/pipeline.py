@@ -1,6 +1,9 @@
 """One MLA decode step for one layer, as the five library calls in order:
 absorb the query, append the new tokens to the paged cache, attend over the
 latent cache, merge the key splits, project back to per-head outputs.
+`run_from_hidden` starts one step earlier, from the hidden states: the
+down-projections with the append, and the query up-projection with the
+absorb, replace the first two calls.
 
 Buffers are allocated once per shape; `run()` only enqueues library calls on
 the current stream.
@@ -37,6 +40,34 @@ class DecodeStep:
         B.absorb_q(d, q_nope, q_rope, q_pos, w_uk, q_abs=self.q_abs.view(n_tok, d.n_heads, -1), stream=stream)
         if new_c_kv is not None and new_c_kv.shape[0] > 0:
             B.append_cache(d, new_c_kv, new_k_rope, new_seq_id, new_pos, block_table, pool, stream=stream)
+        B.decode(d, self.q_abs, pool, block_table, seqlens, self.num_splits, self.workspace, self.o_latent,
+                 self.lse, stream=stream)
+        if self.needs_combine:
+            B.combine(d, seqlens, self.max_blocks, self.workspace, self.o_latent, self.lse, self.num_splits,
+                      stream=stream)
+        B.up_proj(d, self.o_latent.view(n_tok, d.n_heads, d.d_c), w_uv, out=self.out, stream=stream, gate=gate)
+        return self.out, self.o_latent, self.lse
+
+    def run_from_hidden(self, *, h, w_down, d_cq, w_uq, q_pos, new_seq_id, new_pos, block_table, seqlens, pool,
+                        w_uk, w_uv, gate=None, stream=None):
+        """h [n_seq*q_per_seq, d_model] are the hidden states of the new tokens (one per query row);
+        w_down [d_cq + d_c + d_rope, d_model] = [W_DQ; W_DKV; W_KR]; w_uq [H, d_nope + d_rope, d_cq]."""
+        d = self.d
+        n_tok = self.n_seq * self.q_per_seq
+        d_model = h.shape[1]
+        key = (d_model, d_cq)
+        if getattr(self, "_up_key", None) != key:
+            dev = h.device
+            self._c_q = torch.empty((n_tok, d_cq), dtype=B.act_torch_dtype(d), device=dev)
+            self._ws_down = torch.empty(max(B.project_down_workspace_bytes(d, n_tok, d_model, d_cq), 1),
+                                        dtype=torch.uint8, device=dev)
+            self._ws_q = torch.empty(max(B.absorb_from_latent_workspace_bytes(d, n_tok, d_cq), 1), dtype=torch.uint8,
+                                     device=dev)
+            self._up_key = key
+        B.project_down(d, h, w_down, d_cq, new_seq_id, new_pos, block_table, pool, c_q=self._c_q,
+                       workspace=self._ws_down, stream=stream)
+        B.absorb_from_latent(d, self._c_q, w_uq, q_pos, w_uk, q_abs=self.q_abs.view(n_tok, d.n_heads, -1),
+                             workspace=self._ws_q, stream=stream)
         B.decode(d, self.q_abs, pool, block_table, seqlens, self.num_splits, self.workspace, self.o_latent,
                  self.lse, stream=stream)
         if self.needs_combine:

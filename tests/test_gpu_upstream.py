@@ -131,3 +131,46 @@ def test_absorb_from_latent_matches_oracle(n_tok, cuda_device):
     frac = float(np.mean(np.abs(g - e) <= 1.5 * ulp))
     assert frac >= 0.999, f"q_lat: only {frac:.5f} of the elements within 1.5 ulp of the bf16 chain"
     _assert_rotated_close(q_abs[..., w.d_c:].double().cpu().numpy(), want[..., w.d_c:], "rotated q_R")
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_decode_step_from_hidden_states(gated, cuda_device):
+    """DecodeStep.run_from_hidden: down-projection + append, query path + absorb, decode,
+    combine and the (gated) up-projection, against the oracle's chain: the new tokens'
+    latents and keys from project_down, the queries from query_from_latent."""
+    import mla_latent_kv_23_amd as M
+    w = V3.replace(batch=2)
+    lens = [300, 70]
+    inp = S.make_inputs(w, 830, seqlens=torch.tensor(lens, dtype=torch.int32))
+    new_rows = S.new_token_rows(inp, 1).numpy()
+    hist = np.setdiff1d(np.arange(int(sum(lens))), new_rows)
+    up = S.make_upstream_inputs(w, 831, 2)
+    U.say(f"[step_from_hidden] gated={gated}")
+    d = U.dims_of(w)
+    dev = cuda_device
+    pool = U.gpu_pool(w, inp, dev, rows=hist)
+    table = inp["block_table"].to(dev)
+    q_pos = S.query_positions(inp["seqlens"], 1).reshape(-1)
+    gate = S.make_gate_logits(w, 832, 2) if gated else None
+    step = M.DecodeStep(d, 2, 1, table.shape[1], device=dev)
+    out, _, _ = step.run_from_hidden(
+        h=up["h"].to(dev), w_down=up["w_down"].to(dev), d_cq=up["d_cq"], w_uq=up["w_uq"].to(dev),
+        q_pos=q_pos.to(dev), new_seq_id=inp["tok_seq"][new_rows].to(dev), new_pos=inp["tok_pos"][new_rows].to(dev),
+        block_table=table, seqlens=inp["seqlens"].to(dev), pool=pool, w_uk=inp["w_uk"].to(dev),
+        w_uv=inp["w_uv"].to(dev), gate=None if gate is None else gate.to(dev))
+    torch.cuda.synchronize()
+    cq, ckv, kr = O.project_down(up["h"].double().numpy(), up["w_down"].double().numpy(), up["d_cq"], w.d_c, w.d_rope)
+    q_abs = O.query_from_latent(cq, up["w_uq"].double().numpy(), q_pos.numpy(), inp["w_uk"].double().numpy(), w.d_nope,
+                                w.rope_base)
+    cu = inp["cu_seqlens"].tolist()
+    for b, L in enumerate(lens):
+        rows = np.arange(cu[b], cu[b] + L - 1)
+        c_h, kr_h = O.cached_token_values(inp["c_kv"][rows].double().numpy(), inp["k_rope"][rows].double().numpy(),
+                                          np.arange(L - 1), w.cache_dtype, w.rope_base)
+        c_n, kr_n = O.cached_token_values(ckv[b:b + 1], kr[b:b + 1], np.array([L - 1]), w.cache_dtype, w.rope_base)
+        o_lat, _ = O.decode_absorbed_form(q_abs[b:b + 1], np.concatenate([c_h, c_n]), np.concatenate([kr_h, kr_n]),
+                                          np.array([L - 1]), w.softmax_scale)
+        want = O.up_proj(o_lat, inp["w_uv"].double().numpy())
+        if gated:
+            want = O.output_gate(want, gate[b:b + 1].double().numpy())
+        U.assert_close(out[b:b + 1], want, "bf16", f"out seq {b}")
