@@ -48,6 +48,15 @@ constexpr int kRowB = kChunkK * 2 + 16; // LDS bytes per staged row (256 + 16 pa
 constexpr int kStageB = (kGemmFeat + kGemmTok) * kRowB;   // 34816
 constexpr int kPieces = (kGemmFeat + kGemmTok) * (kChunkK * 2 / 16) / 256;   // 16-byte loads per thread per stage: 8
 
+// Where a split's result goes: fp32 partials part[split][n_tok][N], or (a
+// single split) bf16 straight into the query parts: feature n = s (d_nope +
+// d_rope) + r is q_nope[t, s, r] (r < d_nope) or q_rope[t, s, r - d_nope].
+struct GemmOut {
+  float* part;
+  uint16_t *q_nope, *q_rope;
+  int d_nope, d_rope;
+};
+
 // grid (ceil(N / 64), ceil(n_tok / 64), S), block 256.  Each stage holds 128
 // contraction elements of the 64 weight rows and the 64 token rows; thread t
 // loads pieces p = t + 256 j: row p / 16, 16-byte part p % 16 (16 consecutive
@@ -55,8 +64,7 @@ constexpr int kPieces = (kGemmFeat + kGemmTok) * (kChunkK * 2 / 16) / 256;   // 
 // registers while the previous one is multiplied out of LDS.  Wave w computes
 // the 32 x 32 output tile (features 32 (w % 2), tokens 32 (w / 2)).
 __global__ void __launch_bounds__(256) xwt_gemm_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
-                                                       int n_tok, int N, int K, int steps_per_split,
-                                                       float* __restrict__ part) {
+                                                       int n_tok, int N, int K, int steps_per_split, GemmOut go) {
   __shared__ __attribute__((aligned(16))) uint8_t lds_raw[2 * kStageB];
   lds_u8* lds = (lds_u8*)lds_raw;
   const int tid = threadIdx.x, lane = tid & 63, half = lane >> 5;
@@ -124,11 +132,27 @@ __global__ void __launch_bounds__(256) xwt_gemm_kernel(const uint16_t* __restric
   // lane holds token t0 + 32 tt + lane % 32, features f0 + 32 ft + 8 g + 4 half + 0..3
   const int t = t0 + 32 * tt + (lane & 31);
   if (t < n_tok) {
-    float* dst = part + ((int64_t)z * n_tok + t) * N + f0 + 32 * ft + 4 * half;
+    if (go.part) {
+      float* dst = go.part + ((int64_t)z * n_tok + t) * N + f0 + 32 * ft + 4 * half;
 #pragma unroll
-    for (int g = 0; g < 4; ++g)
-      if (f0 + 32 * ft + 8 * g + 4 * half + 4 <= N)
-        *(f32x4*)(dst + 8 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+      for (int g = 0; g < 4; ++g)
+        if (f0 + 32 * ft + 8 * g + 4 * half + 4 <= N)
+          *(f32x4*)(dst + 8 * g) = f32x4{acc[4 * g], acc[4 * g + 1], acc[4 * g + 2], acc[4 * g + 3]};
+    } else {
+      const int dq = go.d_nope + go.d_rope, H = N / dq;
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int n = f0 + 32 * ft + 8 * g + 4 * half;
+        if (n + 4 > N) continue;
+        const int s = n / dq, r = n % dq;
+        u32x2 o;
+        o[0] = (uint32_t)f32_to_bf16_bits(acc[4 * g]) | ((uint32_t)f32_to_bf16_bits(acc[4 * g + 1]) << 16);
+        o[1] = (uint32_t)f32_to_bf16_bits(acc[4 * g + 2]) | ((uint32_t)f32_to_bf16_bits(acc[4 * g + 3]) << 16);
+        uint16_t* dst = r < go.d_nope ? go.q_nope + ((int64_t)t * H + s) * go.d_nope + r
+                                      : go.q_rope + ((int64_t)t * H + s) * go.d_rope + (r - go.d_nope);
+        *(u32x2*)dst = o;
+      }
+    }
   }
 }
 
@@ -202,11 +226,11 @@ int gemm_splits(int64_t n_tok, int64_t N, int64_t K) {
   return (int)std::max<int64_t>(s, 1);
 }
 
-void launch_gemm(const uint16_t* X, const uint16_t* W, int n_tok, int N, int K, int S, float* part, hipStream_t st) {
+void launch_gemm(const uint16_t* X, const uint16_t* W, int n_tok, int N, int K, int S, GemmOut go, hipStream_t st) {
   const int ksteps = K / 16;
   const int steps_per_split = (ksteps + S - 1) / S;
   dim3 grid((N + kGemmFeat - 1) / kGemmFeat, (n_tok + kGemmTok - 1) / kGemmTok, S);
-  hipLaunchKernelGGL(xwt_gemm_kernel, grid, dim3(256), 0, st, X, W, n_tok, N, K, steps_per_split, part);
+  hipLaunchKernelGGL(xwt_gemm_kernel, grid, dim3(256), 0, st, X, W, n_tok, N, K, steps_per_split, go);
 }
 
 }  // namespace
@@ -229,7 +253,9 @@ mla_status launch_project_down(const mla_dims& d, int32_t n_tok, int32_t d_model
   uint16_t* ckv = reinterpret_cast<uint16_t*>(p);
   p += up256((size_t)n_tok * d.d_c * 2);
   uint16_t* kr = reinterpret_cast<uint16_t*>(p);
-  launch_gemm(static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), n_tok, N, d_model, S, part, st);
+  GemmOut go{};
+  go.part = part;
+  launch_gemm(static_cast<const uint16_t*>(h), static_cast<const uint16_t*>(w_down), n_tok, N, d_model, S, go, st);
   hipLaunchKernelGGL(down_reduce_kernel, dim3((N + 1023) / 1024, n_tok), dim3(256), 0, st, part, S, n_tok, N, d_cq, d.d_c,
                      static_cast<uint16_t*>(c_q), ckv, kr);
   const mla_status s = launch_status();
@@ -241,7 +267,8 @@ mla_status launch_project_down(const mla_dims& d, int32_t n_tok, int32_t d_model
 size_t absorb_from_latent_workspace_bytes(const mla_dims& d, int64_t n_tok, int64_t d_cq) {
   const int64_t N = (int64_t)d.n_heads * (d.d_nope + d.d_rope);
   const int S = gemm_splits(n_tok, N, d_cq);
-  return up256((size_t)S * n_tok * N * 4) + up256((size_t)n_tok * d.n_heads * d.d_nope * 2) +
+  // (a single split writes the query parts directly: no partials)
+  return (S > 1 ? up256((size_t)S * n_tok * N * 4) : 0) + up256((size_t)n_tok * d.n_heads * d.d_nope * 2) +
          up256((size_t)n_tok * d.n_heads * d.d_rope * 2);
 }
 
@@ -252,14 +279,23 @@ mla_status launch_absorb_from_latent(const mla_dims& d, int32_t n_tok, int32_t d
   const int S = gemm_splits(n_tok, N, d_cq);
   uint8_t* p = static_cast<uint8_t*>(ws);
   float* part = reinterpret_cast<float*>(p);
-  p += up256((size_t)S * n_tok * N * 4);
+  if (S > 1) p += up256((size_t)S * n_tok * N * 4);
   uint16_t* qn = reinterpret_cast<uint16_t*>(p);
   p += up256((size_t)n_tok * d.n_heads * d.d_nope * 2);
   uint16_t* qr = reinterpret_cast<uint16_t*>(p);
-  launch_gemm(static_cast<const uint16_t*>(c_q), static_cast<const uint16_t*>(w_uq), n_tok, N, d_cq, S, part, st);
-  hipLaunchKernelGGL(q_split_kernel, dim3((N + 1023) / 1024, n_tok), dim3(256), 0, st, part, S, n_tok, d.n_heads,
-                     d.d_nope, d.d_rope,
-                     qn, qr);
+  GemmOut go{};
+  if (S > 1) {
+    go.part = part;
+    launch_gemm(static_cast<const uint16_t*>(c_q), static_cast<const uint16_t*>(w_uq), n_tok, N, d_cq, S, go, st);
+    hipLaunchKernelGGL(q_split_kernel, dim3((N + 1023) / 1024, n_tok), dim3(256), 0, st, part, S, n_tok, d.n_heads,
+                       d.d_nope, d.d_rope, qn, qr);
+  } else {   // one split: the GEMM writes the bf16 query parts itself
+    go.q_nope = qn;
+    go.q_rope = qr;
+    go.d_nope = d.d_nope;
+    go.d_rope = d.d_rope;
+    launch_gemm(static_cast<const uint16_t*>(c_q), static_cast<const uint16_t*>(w_uq), n_tok, N, d_cq, S, go, st);
+  }
   const mla_status s = launch_status();
   if (s != MLA_OK) return s;
   if (absorb_tuned_applies(d) && ((uintptr_t)w_uk & 15) == 0 && ((uintptr_t)q_abs & 15) == 0)
