@@ -43,10 +43,12 @@ typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
 
 constexpr int kGemmTok = 64;            // tokens per work-group (two MFMA column tiles)
 constexpr int kGemmFeat = 64;           // features per work-group (two MFMA row tiles)
-constexpr int kChunkK = 128;            // contraction elements per LDS stage (8 k-steps)
-constexpr int kRowB = kChunkK * 2 + 16; // LDS bytes per staged row (256 + 16 pad: conflict-free fragment reads)
-constexpr int kStageB = (kGemmFeat + kGemmTok) * kRowB;   // 34816
-constexpr int kPieces = (kGemmFeat + kGemmTok) * (kChunkK * 2 / 16) / 256;   // 16-byte loads per thread per stage: 8
+constexpr int kChunkSteps = 8;          // k-steps (16 contraction elements each) per LDS stage (4 and 16 measured slower)
+constexpr int kChunkK = 16 * kChunkSteps;
+constexpr int kParts = 2 * kChunkSteps; // 16-byte parts per staged row
+constexpr int kRowB = kChunkK * 2 + 16; // LDS bytes per staged row (padded: conflict-free fragment reads)
+constexpr int kStageB = (kGemmFeat + kGemmTok) * kRowB;
+constexpr int kPieces = (kGemmFeat + kGemmTok) * kParts / 256;   // 16-byte loads per thread per stage
 
 // Where a split's result goes: fp32 partials part[split][n_tok][N], or (a
 // single split) bf16 straight into the query parts: feature n = s (d_nope +
@@ -73,36 +75,37 @@ __global__ void __launch_bounds__(256) xwt_gemm_kernel(const uint16_t* __restric
   const int f0 = blockIdx.x * kGemmFeat, t0 = blockIdx.y * kGemmTok, z = blockIdx.z;
   const int ksteps = K / 16;
   const int ks0 = z * steps_per_split, ks1 = min(ks0 + steps_per_split, ksteps);
-  const int n_chunks = (ks1 - ks0 + 7) / 8;
+  const int n_chunks = (ks1 - ks0 + kChunkSteps - 1) / kChunkSteps;
 
   // this thread's source rows (clamped: rows past N or n_tok are loaded but never stored)
   const uint16_t* src[kPieces];
 #pragma unroll
   for (int j = 0; j < kPieces; ++j) {
-    const int p = tid + 256 * j, row = p >> 4, part16 = p & 15;
+    const int p = tid + 256 * j, row = p / kParts, part = p % kParts;
     const uint16_t* base = row < kGemmFeat ? W + (int64_t)min(f0 + row, N - 1) * K
                                            : X + (int64_t)min(t0 + row - kGemmFeat, n_tok - 1) * K;
-    src[j] = base + 16 * ks0 + 8 * part16;
+    src[j] = base + 16 * ks0 + 8 * part;
   }
   // k-steps past the split's end read the split's last k-step (in bounds) and are skipped by the MFMAs
   auto load = [&](u32x4 (&r)[kPieces], int c) {
-    const int off = min(8 * c + ((tid & 15) >> 1), ks1 - ks0 - 1) * 16 - ((tid & 15) >> 1) * 16;
+    const int kk = (tid % kParts) >> 1;   // this thread's k-step in the stage (the same for every piece)
+    const int off = (min(kChunkSteps * c + kk, ks1 - ks0 - 1) - kk) * 16;
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) r[j] = *(const u32x4*)(src[j] + off);
   };
   auto store = [&](const u32x4 (&r)[kPieces], int buf) {
 #pragma unroll
     for (int j = 0; j < kPieces; ++j) {
-      const int p = tid + 256 * j, row = p >> 4, part16 = p & 15;
-      *(lds_u32x4*)(lds + buf * kStageB + row * kRowB + 16 * part16) = r[j];
+      const int p = tid + 256 * j, row = p / kParts, part = p % kParts;
+      *(lds_u32x4*)(lds + buf * kStageB + row * kRowB + 16 * part) = r[j];
     }
   };
   f32x16 acc = f32x16{};
   auto compute = [&](int buf, int c) {
     const lds_u8* base = lds + buf * kStageB;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (8 * c + j < ks1 - ks0) {
+    for (int j = 0; j < kChunkSteps; ++j) {
+      if (kChunkSteps * c + j < ks1 - ks0) {
         const bf16x8 a = *(const lds_bf16x8*)(base + (32 * ft + (lane & 31)) * kRowB + 32 * j + 16 * half);
         const bf16x8 b = *(const lds_bf16x8*)(base + (kGemmFeat + 32 * tt + (lane & 31)) * kRowB + 32 * j + 16 * half);
         acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc, 0, 0, 0);
