@@ -34,7 +34,8 @@ BF16_PEAK_TFLOPS = 2500.0         # MI355X dense bf16 MFMA
 # summary records a hash of the kernel sources it was measured on, and the
 # figure is reported only while the sources still match.
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode576_v3_bs64_ctx8k_traffic.md")
-KERNEL_SOURCES = ["decode_latent576.hip", "decode_tile.h", "decode_latent576.h", "mla_internal.h", "mla_device.h"]
+# the device code of the decode kernel (its file, its tile helpers, the shared device helpers)
+KERNEL_SOURCES = ["decode_latent576.hip", "decode_tile.h", "mla_device.h"]
 
 
 def kernel_source_hash():
@@ -222,11 +223,11 @@ def main():
                            c_q=c_q, workspace=ws_down, stream=stream)
             M.absorb_from_latent(dd, c_q, w_uq, step_inputs["q_pos"], step_inputs["w_uk"],
                                  q_abs=step.q_abs.view(n_tok, H, -1), workspace=ws_q, stream=stream)
-        else:
-            M.absorb_q(dd, step_inputs["q_nope"], step_inputs["q_rope"], step_inputs["q_pos"], step_inputs["w_uk"],
-                       q_abs=step.q_abs.view(n_tok, H, -1), stream=stream)
-            M.append_cache(dd, step_inputs["new_c_kv"], step_inputs["new_k_rope"], step_inputs["new_seq_id"],
-                           step_inputs["new_pos"], table, pool, stream=stream)
+        else:   # the absorb and the append of the new tokens in one launch
+            M.absorb_append(dd, step_inputs["q_nope"], step_inputs["q_rope"], step_inputs["q_pos"],
+                            step_inputs["w_uk"], step_inputs["new_c_kv"], step_inputs["new_k_rope"],
+                            step_inputs["new_seq_id"], step_inputs["new_pos"], table, pool,
+                            q_abs=step.q_abs.view(n_tok, H, -1), stream=stream)
         if ev_pair:
             ev_pair[0].record(stream)
         M.decode(dd, step.q_abs, pool, table, seqlens, args.num_splits, step.workspace, step.o_latent,

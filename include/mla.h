@@ -194,6 +194,21 @@ mla_status mla_absorb_from_latent(const mla_dims* dims, int32_t n_tok, int32_t d
                                   size_t workspace_bytes, mla_stream_t stream);
 
 /*
+ * mla_absorb_append -- mla_absorb_q and mla_append_cache in one launch (they
+ * are independent; the short appends fill the CUs the absorb leaves idle).
+ * Arguments as the two calls (n_q query tokens at q_pos, n_kv new tokens at
+ * seq_id / pos); the results are identical to calling them in turn, which is
+ * what happens where the tuned absorb does not apply.  Every argument is
+ * checked before any launch.
+ */
+mla_status mla_absorb_append(const mla_dims* dims, int32_t n_q, const void* q_nope,
+                             const void* q_rope, const int32_t* q_pos, const void* w_uk,
+                             void* q_abs, int32_t n_kv, const void* c_kv, const void* k_rope,
+                             const int32_t* seq_id, const int32_t* pos,
+                             const int32_t* block_table, int32_t n_seq, int32_t max_blocks,
+                             void* cache_pool, int64_t n_pool_blocks, mla_stream_t stream);
+
+/*
  * mla_decode -- latent attention, the absorbed form ("Transformer升级之路：21、
  * MLA好在哪里？（下）", 双重投影, decoding column: every head attends with key
  * [c | k_R] and value c, shared by all heads).
@@ -306,7 +321,8 @@ mla_status mla_prefill(const mla_dims* dims, int32_t n_seq, const int32_t* cu_se
  * cu_q, cu_k [n_seq + 1]: device int32, trusted (0 = cu[0] <= ... <=
  * cu[n_seq] = total_q / total_k, Lq_b <= Lk_b, every Lq_b <= max_q, a host
  * value).  cache_pool and block_table [n_seq, max_blocks] as mla_decode; the
- * blocks covering tokens 0..Lk_b - 1 must be valid (trusted).  q_nope
+ * blocks covering tokens 0..Lk_b - 1 must be valid (trusted; a negative entry
+ * there is read as a zero latent and key, one beyond the pool is not caught).  q_nope
  * [total_q, H, d_nope], q_rope [total_q, H, d_rope] (unrotated), w_uk, w_uv,
  * gate (null or [total_q, H, d_v]), out [total_q, H, d_v] and lse [total_q, H]
  * as mla_prefill.  workspace: at least mla_prefill_paged_workspace_bytes,

@@ -63,6 +63,8 @@ SIGNATURES = {
     "mla_combine": (ctypes.c_int, [_DP, _I32, _I32, _P, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "mla_up_proj": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P]),
     "mla_up_proj_gated": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P, _P]),
+    "mla_absorb_append": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P,
+                                         ctypes.c_int64, _P]),
     "mla_prefill_workspace_bytes": (_SZ, [_DP, _I32]),
     "mla_prefill": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
     "mla_prefill_paged_workspace_bytes": (_SZ, [_DP, _I32, _I32]),
@@ -192,6 +194,26 @@ def combine(d: Dims, seqlens, max_blocks: int, workspace, o_latent, lse, num_spl
         _ptr(workspace, "workspace"), ws_bytes, _ptr(o_latent, "o_latent", at), _ptr(lse, "lse", torch.float32),
         _stream(stream)))
     return o_latent, lse
+
+
+def absorb_append(d: Dims, q_nope, q_rope, q_pos, w_uk, c_kv, k_rope, seq_id, pos, block_table, pool, q_abs=None,
+                  stream=None):
+    """absorb_q and append_cache in one launch; returns q_abs [n_q, H, d_c + d_rope]."""
+    at = act_torch_dtype(d)
+    n_q, n_kv = q_nope.shape[0], c_kv.shape[0]
+    if q_abs is None:
+        q_abs = torch.empty((n_q, d.n_heads, d.d_c + d.d_rope), dtype=at, device=q_nope.device)
+    bb = cache_block_bytes(d)
+    if pool.dtype != torch.uint8 or pool.numel() % bb:
+        raise ValueError("pool must be a uint8 tensor of whole blocks")
+    n_seq, max_blocks = block_table.shape
+    _check("mla_absorb_append", load_library().mla_absorb_append(
+        ctypes.byref(d), n_q, _ptr(q_nope, "q_nope", at), _ptr(q_rope, "q_rope", at), _ptr(q_pos, "q_pos", torch.int32),
+        _ptr(w_uk, "w_uk", at), _ptr(q_abs, "q_abs", at), n_kv, _ptr(c_kv, "c_kv", at), _ptr(k_rope, "k_rope", at),
+        _ptr(seq_id, "seq_id", torch.int32), _ptr(pos, "pos", torch.int32),
+        _ptr(block_table, "block_table", torch.int32), n_seq, max_blocks, _ptr(pool, "pool", torch.uint8),
+        pool.numel() // bb, _stream(stream)))
+    return q_abs
 
 
 def up_proj(d: Dims, o_latent, w_uv, out=None, stream=None, gate=None):

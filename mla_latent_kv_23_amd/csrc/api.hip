@@ -169,6 +169,38 @@ mla_status mla_append_cache(const mla_dims* d, int32_t n_tok, const void* c_kv, 
                                n_pool_blocks, static_cast<hipStream_t>(stream));
 }
 
+mla_status mla_absorb_append(const mla_dims* d, int32_t n_q, const void* q_nope, const void* q_rope,
+                             const int32_t* q_pos, const void* w_uk, void* q_abs, int32_t n_kv, const void* c_kv,
+                             const void* k_rope, const int32_t* seq_id, const int32_t* pos,
+                             const int32_t* block_table, int32_t n_seq, int32_t max_blocks, void* cache_pool,
+                             int64_t n_pool_blocks, mla_stream_t stream) {
+  const mla_status s = dims_supported(d);
+  if (s != MLA_OK) return s;
+  // the checks of mla_absorb_q and mla_append_cache, all before any launch
+  if (n_q < 0 || n_kv < 0 || n_seq <= 0 || max_blocks <= 0 || n_pool_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (n_q > 0 && (!q_nope || !w_uk || !q_abs || (d->d_rope > 0 && (!q_rope || !q_pos)))) return MLA_ERR_INVALID_ARG;
+  if (n_kv > 0 && (!c_kv || !seq_id || !pos || !block_table || !cache_pool || (d->d_rope > 0 && !k_rope)))
+    return MLA_ERR_INVALID_ARG;
+  if (n_q > 2147483647 / d->n_heads) return MLA_ERR_UNSUPPORTED;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (n_q > 0 && n_kv > 0 && absorb_tuned_applies(*d) && d->cache_dtype != MLA_F32 && aligned16(q_nope) &&
+      aligned16(w_uk) && aligned16(q_abs) && (int64_t)d->n_heads * (d->d_c / 128) + n_kv <= 2147483647LL)
+    return launch_absorb_append(*d, n_q, q_nope, q_rope, q_pos, w_uk, q_abs, n_kv, c_kv, k_rope, seq_id, pos,
+                                block_table, n_seq, max_blocks, cache_pool, n_pool_blocks, st);
+  // otherwise the two calls in turn
+  mla_status r = MLA_OK;
+  if (n_q > 0) {
+    r = (absorb_tuned_applies(*d) && aligned16(q_nope) && aligned16(w_uk) && aligned16(q_abs))
+            ? launch_absorb_tuned(*d, n_q, q_nope, q_rope, q_pos, w_uk, q_abs, st)
+            : launch_absorb_generic(*d, n_q, q_nope, q_rope, q_pos, w_uk, q_abs, st);
+    if (r != MLA_OK) return r;
+  }
+  if (n_kv > 0)
+    r = launch_append_generic(*d, n_kv, c_kv, k_rope, seq_id, pos, block_table, n_seq, max_blocks, cache_pool,
+                              n_pool_blocks, st);
+  return r;
+}
+
 size_t mla_decode_workspace_bytes(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, int32_t max_blocks,
                                   int32_t num_splits) {
   if (check_decode_args(d, n_seq, q_per_seq, max_blocks, num_splits) != MLA_OK) return 0;

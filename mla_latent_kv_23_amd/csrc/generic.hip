@@ -2,6 +2,7 @@
 // straightforward scalar kernels: they serve small or unusual shapes (such as
 // a 64-wide latent in float32) and every shape the tuned gfx950 kernels do not
 // cover.  The tuned kernels live in their own files.
+#include "append_body.h"
 #include "mla_internal.h"
 
 namespace mla {
@@ -38,7 +39,7 @@ __global__ void __launch_bounds__(256) absorb_generic_kernel(
 }
 
 // ----------------------------------------------------------------------------
-// append: one block per token.
+// append: one block per token (the body is in append_body.h).
 // ----------------------------------------------------------------------------
 template <typename T, bool kFp8>
 __global__ void __launch_bounds__(256) append_generic_kernel(
@@ -47,49 +48,8 @@ __global__ void __launch_bounds__(256) append_generic_kernel(
     uint8_t* __restrict__ pool, int64_t n_pool_blocks, int64_t block_bytes, int block_size, int d_c,
     int d_rope, RopeFreqs freqs) {
   __shared__ float red[256];
-  const int n = blockIdx.x;
-  const int sq = seq_id[n], p = pos[n];
-  if (sq < 0 || sq >= n_seq || p < 0 || p / block_size >= max_blocks) return;
-  const int32_t blk = block_table[static_cast<int64_t>(sq) * max_blocks + p / block_size];
-  if (blk < 0 || blk >= n_pool_blocks) return;
-  const int slot = p % block_size;
-  uint8_t* base = pool + static_cast<int64_t>(blk) * block_bytes;
-  const int64_t crow = static_cast<int64_t>(n) * d_c, krow = static_cast<int64_t>(n) * d_rope;
-  if constexpr (!kFp8) {
-    T* row = reinterpret_cast<T*>(base) + static_cast<int64_t>(slot) * (d_c + d_rope);
-    for (int c = threadIdx.x; c < d_c; c += blockDim.x) row[c] = c_kv[crow + c];
-    for (int i = threadIdx.x; i < d_rope / 2; i += blockDim.x) {
-      float cs, sn, ox, oy;
-      rope_cos_sin(p, freqs.inv_freq[i], &cs, &sn);
-      rope_pair(Act<T>::ld(k_rope, krow + 2 * i), Act<T>::ld(k_rope, krow + 2 * i + 1), cs, sn, &ox, &oy);
-      Act<T>::st(row, d_c + 2 * i, ox);
-      Act<T>::st(row, d_c + 2 * i + 1, oy);
-    }
-  } else {
-    // per-token amax -> scale = amax / 448 -> codes
-    float amax = 0.f;
-    for (int c = threadIdx.x; c < d_c; c += blockDim.x) amax = fmaxf(amax, fabsf(Act<T>::ld(c_kv, crow + c)));
-    red[threadIdx.x] = amax;
-    __syncthreads();
-    for (int w = blockDim.x / 2; w > 0; w >>= 1) {
-      if (threadIdx.x < w) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + w]);
-      __syncthreads();
-    }
-    amax = red[0];
-    const float scale = amax == 0.f ? 1.0f : amax / 448.0f;
-    uint8_t* codes = base + static_cast<int64_t>(slot) * d_c;
-    for (int c = threadIdx.x; c < d_c; c += blockDim.x) codes[c] = f32_to_e4m3fn(Act<T>::ld(c_kv, crow + c) / scale);
-    if (threadIdx.x == 0) reinterpret_cast<float*>(base + static_cast<int64_t>(block_size) * d_c)[slot] = scale;
-    uint16_t* kr = reinterpret_cast<uint16_t*>(base + static_cast<int64_t>(block_size) * d_c + 4 * block_size) +
-                   static_cast<int64_t>(slot) * d_rope;
-    for (int i = threadIdx.x; i < d_rope / 2; i += blockDim.x) {
-      float cs, sn, ox, oy;
-      rope_cos_sin(p, freqs.inv_freq[i], &cs, &sn);
-      rope_pair(Act<T>::ld(k_rope, krow + 2 * i), Act<T>::ld(k_rope, krow + 2 * i + 1), cs, sn, &ox, &oy);
-      kr[2 * i] = f32_to_bf16_bits(ox);
-      kr[2 * i + 1] = f32_to_bf16_bits(oy);
-    }
-  }
+  append_token<T, kFp8>(blockIdx.x, c_kv, k_rope, seq_id, pos, block_table, n_seq, max_blocks, pool, n_pool_blocks,
+                        block_bytes, block_size, d_c, d_rope, freqs, red);
 }
 
 // ----------------------------------------------------------------------------

@@ -126,6 +126,16 @@ __global__ void __launch_bounds__(256) prefill_gather_kernel(const uint8_t* __re
   const int p = t - cu_k[b];
   const int64_t blk = block_table[(int64_t)b * max_blocks + p / block_size];
   const int slot = p % block_size;
+  if (blk < 0) {   // a padding entry inside the length (a caller error): zeros, nothing is read
+    if (piece < kCPieces) {
+      u32x4* dst = (u32x4*)(c_out + (int64_t)t * kPfDc + (kFp8 ? 16 : 8) * piece);
+      dst[0] = u32x4{0, 0, 0, 0};
+      if (kFp8) dst[1] = u32x4{0, 0, 0, 0};
+    } else {
+      *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * (piece - kCPieces)) = u32x4{0, 0, 0, 0};
+    }
+    return;
+  }
   const uint8_t* base = pool + blk * block_bytes;
   if constexpr (!kFp8) {
     const u32x4 v = *(const u32x4*)(base + ((int64_t)slot * (kPfDc + kPfDr) + 8 * piece) * 2);

@@ -17,6 +17,7 @@
 //    four fp32 partial tiles are summed through LDS.
 #include <math.h>
 
+#include "append_body.h"
 #include "decode_latent576.h"
 
 namespace mla {
@@ -53,17 +54,27 @@ __device__ __forceinline__ u32x2 pack4(float a, float b, float c, float d) {
 // x 32 bytes per 16 lanes) are free of bank conflicts.  Wave w computes latent
 // columns 32w .. 32w+31 of the block for every 32-token block in turn; the
 // next block's query fragments are loaded while the current one is multiplied.
-__global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __restrict__ q_nope,
-                                                           const uint16_t* __restrict__ q_rope,
-                                                           const int32_t* __restrict__ pos,
-                                                           const uint16_t* __restrict__ w_uk,
-                                                           uint16_t* __restrict__ q_abs, int n_tok, int H, int d_c,
-                                                           int d_rope, RopeFreqs freqs) {
+struct AbsorbArgs {
+  const uint16_t* q_nope;
+  const uint16_t* q_rope;
+  const int32_t* pos;
+  const uint16_t* w_uk;
+  uint16_t* q_abs;
+  int n_tok, H, d_c, d_rope;
+};
+
+// The absorb of head s, latent columns cblk*128 .. +127 (ny = d_c / 128 blocks per head).
+__device__ __forceinline__ void absorb_body(const AbsorbArgs& aa, int s, int cblk, int ny, const RopeFreqs& freqs) {
+  const uint16_t* __restrict__ q_nope = aa.q_nope;
+  const uint16_t* __restrict__ q_rope = aa.q_rope;
+  const int32_t* __restrict__ pos = aa.pos;
+  const uint16_t* __restrict__ w_uk = aa.w_uk;
+  uint16_t* __restrict__ q_abs = aa.q_abs;
+  const int n_tok = aa.n_tok, H = aa.H, d_c = aa.d_c, d_rope = aa.d_rope;
   constexpr int kSteps = kNope / 16;                 // 8 k-steps of 16
   constexpr int kChunks = kNope * 16 / 256;          // slab chunks per thread
   __shared__ __attribute__((aligned(16))) uint8_t slab_raw[kNope * kAbsorbCols * 2];
   lds_u8* slab = (lds_u8*)slab_raw;
-  const int s = blockIdx.x, cblk = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int d_k = d_c + d_rope;
   const int gi = lane >> 4, sp = lane & 15, half = lane >> 5;
@@ -72,7 +83,7 @@ __global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __res
   // (work-group cblk takes tokens t = cblk mod gridDim.y).  The inputs of this
   // thread's first two rotations are loaded before the slab, so that the fp64
   // cos/sin run while the slab loads are in flight (loads complete in order).
-  const int pairs = d_rope / 2, ny = gridDim.y;
+  const int pairs = d_rope / 2;
   const int n_rope = ((n_tok - cblk + ny - 1) / ny) * pairs;
   auto rope_item = [&](int i, int* t, int* p) {
     *t = cblk + ny * (i / pairs);
@@ -175,6 +186,38 @@ __global__ void __launch_bounds__(256) absorb_tuned_kernel(const uint16_t* __res
   }
 }
 
+__global__ void __launch_bounds__(256) absorb_tuned_kernel(AbsorbArgs aa, RopeFreqs freqs) {
+  absorb_body(aa, blockIdx.x, blockIdx.y, gridDim.y, freqs);
+}
+
+struct AppendArgs {
+  const uint16_t* c_kv;
+  const uint16_t* k_rope;
+  const int32_t* seq_id;
+  const int32_t* pos;
+  const int32_t* block_table;
+  uint8_t* pool;
+  int64_t n_pool_blocks, block_bytes;
+  int n_seq, max_blocks, block_size, d_c, d_rope;
+};
+
+// One launch for the two independent head-of-step calls: work-groups 0 ..
+// H ny - 1 absorb (head b / ny, latent block b % ny), the rest append one new
+// token each.  The appends are short and fill the CUs the absorb leaves idle.
+template <bool kFp8>
+__global__ void __launch_bounds__(256) absorb_append_kernel(AbsorbArgs aa, AppendArgs pa, int ny, RopeFreqs freqs) {
+  __shared__ float red[256];
+  const int n_abs = aa.H * ny;
+  const int b = blockIdx.x;
+  if (b < n_abs) {
+    absorb_body(aa, b / ny, b % ny, ny, freqs);
+  } else {
+    append_token<uint16_t, kFp8>(b - n_abs, pa.c_kv, pa.k_rope, pa.seq_id, pa.pos, pa.block_table, pa.n_seq,
+                                 pa.max_blocks, pa.pool, pa.n_pool_blocks, pa.block_bytes, pa.block_size, pa.d_c,
+                                 pa.d_rope, freqs, red);
+  }
+}
+
 // grid (H, ceil(n_tok / 32)), block 256.  Wave w contracts latent dims
 // 128w .. 128w+127 for all d_v/32 output-row blocks of the block's 32 tokens
 // (all its operands are loaded up front), writes its fp32 partial tiles to
@@ -263,9 +306,32 @@ mla_status launch_absorb_tuned(const mla_dims& d, int32_t n_tok, const void* q_n
                                const int32_t* pos, const void* w_uk, void* q_abs, hipStream_t st) {
   const RopeFreqs f = make_rope_freqs(d);
   dim3 grid(d.n_heads, d.d_c / kAbsorbCols);
-  hipLaunchKernelGGL(absorb_tuned_kernel, grid, dim3(256), 0, st, static_cast<const uint16_t*>(q_nope),
-                     static_cast<const uint16_t*>(q_rope), pos, static_cast<const uint16_t*>(w_uk),
-                     static_cast<uint16_t*>(q_abs), n_tok, d.n_heads, d.d_c, d.d_rope, f);
+  const AbsorbArgs aa{static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope), pos,
+                      static_cast<const uint16_t*>(w_uk), static_cast<uint16_t*>(q_abs), n_tok, d.n_heads, d.d_c,
+                      d.d_rope};
+  hipLaunchKernelGGL(absorb_tuned_kernel, grid, dim3(256), 0, st, aa, f);
+  return launch_status();
+}
+
+mla_status launch_absorb_append(const mla_dims& d, int32_t n_q, const void* q_nope, const void* q_rope,
+                                const int32_t* q_pos, const void* w_uk, void* q_abs, int32_t n_kv, const void* c_kv,
+                                const void* k_rope, const int32_t* seq_id, const int32_t* pos,
+                                const int32_t* block_table, int32_t n_seq, int32_t max_blocks, void* pool,
+                                int64_t n_pool_blocks, hipStream_t st) {
+  const RopeFreqs f = make_rope_freqs(d);
+  const int ny = d.d_c / kAbsorbCols;
+  const AbsorbArgs aa{static_cast<const uint16_t*>(q_nope), static_cast<const uint16_t*>(q_rope), q_pos,
+                      static_cast<const uint16_t*>(w_uk), static_cast<uint16_t*>(q_abs), n_q, d.n_heads, d.d_c,
+                      d.d_rope};
+  const AppendArgs pa{static_cast<const uint16_t*>(c_kv), static_cast<const uint16_t*>(k_rope), seq_id, pos,
+                      block_table, static_cast<uint8_t*>(pool), n_pool_blocks,
+                      static_cast<int64_t>(mla_cache_block_bytes(&d)), n_seq, max_blocks, d.block_size, d.d_c,
+                      d.d_rope};
+  const dim3 grid((unsigned)(d.n_heads * ny + n_kv));
+  if (d.cache_dtype == MLA_FP8_E4M3)
+    hipLaunchKernelGGL(absorb_append_kernel<true>, grid, dim3(256), 0, st, aa, pa, ny, f);
+  else
+    hipLaunchKernelGGL(absorb_append_kernel<false>, grid, dim3(256), 0, st, aa, pa, ny, f);
   return launch_status();
 }
 

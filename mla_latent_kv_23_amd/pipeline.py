@@ -37,9 +37,11 @@ class DecodeStep:
         gate [n_seq*q_per_seq, H, d_v] (optional): output-gate logits of gated MLA."""
         d = self.d
         n_tok = self.n_seq * self.q_per_seq
-        B.absorb_q(d, q_nope, q_rope, q_pos, w_uk, q_abs=self.q_abs.view(n_tok, d.n_heads, -1), stream=stream)
-        if new_c_kv is not None and new_c_kv.shape[0] > 0:
-            B.append_cache(d, new_c_kv, new_k_rope, new_seq_id, new_pos, block_table, pool, stream=stream)
+        if new_c_kv is not None and new_c_kv.shape[0] > 0:   # the absorb and the append in one launch
+            B.absorb_append(d, q_nope, q_rope, q_pos, w_uk, new_c_kv, new_k_rope, new_seq_id, new_pos, block_table,
+                            pool, q_abs=self.q_abs.view(n_tok, d.n_heads, -1), stream=stream)
+        else:
+            B.absorb_q(d, q_nope, q_rope, q_pos, w_uk, q_abs=self.q_abs.view(n_tok, d.n_heads, -1), stream=stream)
         B.decode(d, self.q_abs, pool, block_table, seqlens, self.num_splits, self.workspace, self.o_latent,
                  self.lse, stream=stream)
         if self.needs_combine:

@@ -137,6 +137,35 @@ def test_up_proj_gated(name, aligned, cuda_device):
 
 
 @pytest.mark.parametrize("name", NAMES)
+def test_absorb_append_equals_the_two_calls(name, cuda_device):
+    """The one-launch absorb + append writes exactly what mla_absorb_q and
+    mla_append_cache write (q_abs and every pool byte)."""
+    import mla_latent_kv_23_amd as M
+    w, inp = _inputs(name)
+    U.say(f"[absorb_append] {name}")
+    d = U.dims_of(w)
+    dev = cuda_device
+    sq = w.q_per_seq
+    n_tok = inp["q_nope"].shape[0] * sq
+    H = w.n_heads
+    qn = inp["q_nope"].reshape(n_tok, H, -1).to(dev)
+    qr = inp["q_rope"].reshape(n_tok, H, -1).to(dev)
+    qpos = U.q_positions_flat(inp, sq).to(dev)
+    table = inp["block_table"].to(dev)
+    args = (inp["c_kv"].to(dev), inp["k_rope"].to(dev), inp["tok_seq"].to(dev), inp["tok_pos"].to(dev), table)
+    bb = M.cache_block_bytes(d)
+    pool1 = torch.full((inp["n_blocks"] * bb,), 0x5A, dtype=torch.uint8, device=dev)
+    pool2 = pool1.clone()
+    q1 = M.absorb_q(d, qn, qr, qpos, inp["w_uk"].to(dev))
+    M.append_cache(d, *args, pool1)
+    q2 = M.absorb_append(d, qn, qr, qpos, inp["w_uk"].to(dev), *args, pool2)
+    torch.cuda.synchronize()
+    assert torch.equal(q1.view(torch.int16) if q1.dtype == torch.bfloat16 else q1,
+                       q2.view(torch.int16) if q2.dtype == torch.bfloat16 else q2)
+    assert torch.equal(pool1, pool2)
+
+
+@pytest.mark.parametrize("name", NAMES)
 def test_chain_vs_non_absorbed_oracle(name, cuda_device):
     """absorb -> append (the new tokens) -> decode -> combine -> up_proj, against the
     oracle's MHA form, which decompresses K and V per head explicitly."""
