@@ -11,11 +11,13 @@
 // rotated.
 //
 // Launches:
-//  1. prefill_rope_kernel: q_R' [Tq, H, 64] (and, for packed keys, k_R'
-//     [Tk, 64]) in bf16, by the RoPE rule of the absorb and append kernels
-//     (fp64 angle, fp32 cos/sin, fp64 rotation, one rounding); cos/sin once
-//     per (token, pair).  For paged keys, prefill_gather_kernel packs each
-//     key's cache row (latent and rotated k_R) into the workspace.
+//  1. prefill_rope_kernel: cos/sin of every query's RoPE pairs [Tq][32] (fp64
+//     angle, fp32 cos/sin: the rule of the absorb and append kernels) and, for
+//     packed keys, k_R' [Tk, 64] in bf16 (fp64 rotation, one rounding).  The
+//     query's RoPE part is rotated by the attention kernel as it loads the
+//     query (fp32 fused multiply-adds, then bf16, the MFMA operand).  For paged
+//     keys, prefill_gather_kernel packs each key's cache row (latent and
+//     rotated k_R) into the workspace.
 //  2. prefill_decompress_kernel: k_C [T, H, 128] and v [T, H, 128] in bf16, a
 //     bf16 MFMA GEMM with fp32 accumulation: each wave holds its 32 weight rows
 //     in registers, and the latent streams through LDS, 32 tokens at a time,
@@ -56,40 +58,31 @@ __device__ __forceinline__ int pf_seq_of(const int32_t* __restrict__ cu, int n_s
   return lo;
 }
 
-// grid Tq (one work-group per query token).  k_rope non-null (packed keys,
-// cu_k == cu_q): the key of the same token is rotated too.
-__global__ void __launch_bounds__(256) prefill_rope_kernel(const uint16_t* __restrict__ q_rope,
-                                                           const uint16_t* __restrict__ k_rope,
+// One thread per (query token t, RoPE pair p): cos/sin of the pair's angle at
+// the query's position go to cs[t][p] (float2), by the RoPE rule of the absorb
+// and append kernels (fp64 angle, fp32 cos/sin); the attention kernel rotates
+// the query's RoPE part with them as it loads the query.  k_rope non-null
+// (packed keys, cu_k == cu_q, so the key of token t sits at the same
+// position): the key pair is rotated here too (fp64 rotation, one rounding).
+__global__ void __launch_bounds__(256) prefill_rope_kernel(const uint16_t* __restrict__ k_rope,
                                                            const int32_t* __restrict__ cu_q,
-                                                           const int32_t* __restrict__ cu_k, int n_seq, int H,
-                                                           uint16_t* __restrict__ qr_out, uint16_t* __restrict__ kr_out,
+                                                           const int32_t* __restrict__ cu_k, int n_seq, int total_q,
+                                                           float* __restrict__ cs, uint16_t* __restrict__ kr_out,
                                                            RopeFreqs f) {
-  __shared__ float s_cs[kPfDr / 2], s_sn[kPfDr / 2];
-  const int t = blockIdx.x, tid = threadIdx.x;
-  if (tid < kPfDr / 2) {
-    const int b = pf_seq_of(cu_q, n_seq, t);
-    const int pos = (t - cu_q[b]) + (cu_k[b + 1] - cu_k[b]) - (cu_q[b + 1] - cu_q[b]);
-    float cs, sn;
-    rope_cos_sin(pos, f.inv_freq[tid], &cs, &sn);
-    s_cs[tid] = cs;
-    s_sn[tid] = sn;
-  }
-  __syncthreads();
-  for (int i = tid; i < H * (kPfDr / 2); i += 256) {
-    const int s = i / (kPfDr / 2), p = i % (kPfDr / 2);
-    const int64_t at = ((int64_t)t * H + s) * kPfDr + 2 * p;
-    const uint32_t x2 = *(const uint32_t*)(q_rope + at);
-    float ox, oy;
-    rope_pair(bf16_bits_to_f32((uint16_t)(x2 & 0xffffu)), bf16_bits_to_f32((uint16_t)(x2 >> 16)), s_cs[p], s_sn[p], &ox,
-              &oy);
-    *(uint32_t*)(qr_out + at) = (uint32_t)f32_to_bf16_bits(ox) | ((uint32_t)f32_to_bf16_bits(oy) << 16);
-  }
-  if (k_rope && tid < kPfDr / 2) {
-    const int64_t at = (int64_t)t * kPfDr + 2 * tid;
+  constexpr int kPairs = kPfDr / 2;
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int t = (int)(i / kPairs), p = (int)(i % kPairs);
+  if (t >= total_q) return;
+  const int b = pf_seq_of(cu_q, n_seq, t);
+  const int pos = (t - cu_q[b]) + (cu_k[b + 1] - cu_k[b]) - (cu_q[b + 1] - cu_q[b]);
+  float c, sn;
+  rope_cos_sin(pos, f.inv_freq[p], &c, &sn);
+  *(float2*)(cs + 2 * i) = make_float2(c, sn);
+  if (k_rope) {
+    const int64_t at = (int64_t)t * kPfDr + 2 * p;
     const uint32_t x2 = *(const uint32_t*)(k_rope + at);
     float ox, oy;
-    rope_pair(bf16_bits_to_f32((uint16_t)(x2 & 0xffffu)), bf16_bits_to_f32((uint16_t)(x2 >> 16)), s_cs[tid],
-              s_sn[tid], &ox, &oy);
+    rope_pair(bf16_bits_to_f32((uint16_t)(x2 & 0xffffu)), bf16_bits_to_f32((uint16_t)(x2 >> 16)), c, sn, &ox, &oy);
     *(uint32_t*)(kr_out + at) = (uint32_t)f32_to_bf16_bits(ox) | ((uint32_t)f32_to_bf16_bits(oy) << 16);
   }
 }
@@ -312,7 +305,8 @@ __device__ __forceinline__ uint32_t stage_off(int r, int c) {
 
 struct PrefillArgs {
   const uint16_t* q_nope;     // [T][H][128]
-  const uint16_t* q_rot;      // [T][H][64] rotated
+  const uint16_t* q_rope;     // [Tq][H][64] unrotated
+  const float* cs;            // [Tq][32] (cos, sin) of each query's RoPE pairs
   const uint16_t* k_c;        // [T][H][128]
   const uint16_t* k_rot;      // [T][64] rotated
   const uint16_t* v;          // [T][H][128]
@@ -352,11 +346,25 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
   bf16x8 qf[kQk];
   {
     const bf16x8* qn = (const bf16x8*)(a.q_nope + ((int64_t)(cu0 + q) * H + s) * kPfDn) + half;
-    const bf16x8* qr = (const bf16x8*)(a.q_rot + ((int64_t)(cu0 + q) * H + s) * kPfDr) + half;
+    // the RoPE part, rotated here: k-step kk holds pairs 8 (kk - 8) + 4 half .. +3
+    const bf16x8* qr = (const bf16x8*)(a.q_rope + ((int64_t)(cu0 + q) * H + s) * kPfDr) + half;
+    const f32x4* csq = (const f32x4*)(a.cs + (int64_t)(cu0 + q) * kPfDr) + 2 * half;   // 2 pairs per f32x4
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) qf[kk] = qn[2 * kk];
 #pragma unroll
-    for (int kk = 8; kk < kQk; ++kk) qf[kk] = qr[2 * (kk - 8)];
+    for (int kk = 8; kk < kQk; ++kk) {
+      const bf16x8 raw = qr[2 * (kk - 8)];
+      const f32x4 c01 = csq[4 * (kk - 8)], c23 = csq[4 * (kk - 8) + 1];
+      const float cv[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+      bf16x8 rot;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float x = (float)raw[2 * e], y = (float)raw[2 * e + 1], c = cv[2 * e], sn = cv[2 * e + 1];
+        rot[2 * e] = (__bf16)fmaf(x, c, -(y * sn));
+        rot[2 * e + 1] = (__bf16)fmaf(x, sn, y * c);
+      }
+      qf[kk] = rot;
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);             // queries resident before any stage load is queued
 
@@ -565,14 +573,15 @@ bool prefill_supported(const mla_dims& d) {
 namespace {
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace: k_C, v [Tk][H][128], q_R' [Tq][H][64], k_R' [Tk][64] (bf16), then,
+// workspace: k_C, v [Tk][H][128] (bf16), the queries' (cos, sin) [Tq][32] (float2), k_R' [Tk][64] (bf16), then,
 // for paged keys, the packed latent rows [Tk][d_c] (bf16); 256-byte aligned pieces
 struct PrefillWs {
-  uint16_t *kc, *vv, *qr, *kr;
+  uint16_t *kc, *vv, *kr;
+  float* cs;
   uint16_t* ckv;   // paged keys: the packed latent rows
 };
 size_t prefill_ws_bytes(int64_t tq, int64_t tk, int64_t H, bool paged) {
-  return up256(tk * H * kPfDn * 2) + up256(tk * H * kPfDv * 2) + up256(tq * H * kPfDr * 2) + up256(tk * kPfDr * 2) +
+  return up256(tk * H * kPfDn * 2) + up256(tk * H * kPfDv * 2) + up256(tq * kPfDr * 4) + up256(tk * kPfDr * 2) +
          (paged ? up256(tk * kPfDc * 2) : 0);
 }
 PrefillWs carve(void* ws, int64_t tq, int64_t tk, int64_t H) {
@@ -582,8 +591,8 @@ PrefillWs carve(void* ws, int64_t tq, int64_t tk, int64_t H) {
   p += up256(tk * H * kPfDn * 2);
   w.vv = reinterpret_cast<uint16_t*>(p);
   p += up256(tk * H * kPfDv * 2);
-  w.qr = reinterpret_cast<uint16_t*>(p);
-  p += up256(tq * H * kPfDr * 2);
+  w.cs = reinterpret_cast<float*>(p);
+  p += up256(tq * kPfDr * 4);
   w.kr = reinterpret_cast<uint16_t*>(p);
   p += up256(tk * kPfDr * 2);
   w.ckv = reinterpret_cast<uint16_t*>(p);
@@ -600,11 +609,12 @@ void launch_decompress(const mla_dims& d, const uint16_t* c_kv, const void* w_uk
 }
 
 void launch_attention(const mla_dims& d, int32_t n_seq, const int32_t* cu_q, const int32_t* cu_k, int32_t max_q,
-                      const void* q_nope, const PrefillWs& w, const void* gate, void* out, float* lse,
-                      hipStream_t st) {
+                      const void* q_nope, const void* q_rope, const PrefillWs& w, const void* gate, void* out,
+                      float* lse, hipStream_t st) {
   PrefillArgs a;
   a.q_nope = static_cast<const uint16_t*>(q_nope);
-  a.q_rot = w.qr;
+  a.q_rope = static_cast<const uint16_t*>(q_rope);
+  a.cs = w.cs;
   a.k_c = w.kc;
   a.k_rot = w.kr;
   a.v = w.vv;
@@ -636,10 +646,11 @@ mla_status launch_prefill(const mla_dims& d, int32_t n_seq, const int32_t* cu_se
                           void* out, float* lse, hipStream_t st) {
   const PrefillWs w = carve(ws, total_tokens, total_tokens, d.n_heads);
   const RopeFreqs f = make_rope_freqs(d);
-  hipLaunchKernelGGL(prefill_rope_kernel, dim3(total_tokens), dim3(256), 0, st, static_cast<const uint16_t*>(q_rope),
-                     static_cast<const uint16_t*>(k_rope), cu_seqlens, cu_seqlens, n_seq, d.n_heads, w.qr, w.kr, f);
+  hipLaunchKernelGGL(prefill_rope_kernel, dim3((unsigned)(((int64_t)total_tokens * (kPfDr / 2) + 255) / 256)), dim3(256),
+                     0, st, static_cast<const uint16_t*>(k_rope), cu_seqlens, cu_seqlens, n_seq, total_tokens, w.cs,
+                     w.kr, f);
   launch_decompress(d, static_cast<const uint16_t*>(c_kv), w_uk, w_uv, w, total_tokens, st);
-  launch_attention(d, n_seq, cu_seqlens, cu_seqlens, max_seqlen, q_nope, w, gate, out, lse, st);
+  launch_attention(d, n_seq, cu_seqlens, cu_seqlens, max_seqlen, q_nope, q_rope, w, gate, out, lse, st);
   return launch_status();
 }
 
@@ -650,8 +661,8 @@ mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t*
                                 hipStream_t st) {
   const PrefillWs w = carve(ws, total_q, total_k, d.n_heads);
   const RopeFreqs f = make_rope_freqs(d);
-  hipLaunchKernelGGL(prefill_rope_kernel, dim3(total_q), dim3(256), 0, st, static_cast<const uint16_t*>(q_rope),
-                     nullptr, cu_q, cu_k, n_seq, d.n_heads, w.qr, nullptr, f);
+  hipLaunchKernelGGL(prefill_rope_kernel, dim3((unsigned)(((int64_t)total_q * (kPfDr / 2) + 255) / 256)), dim3(256), 0,
+                     st, nullptr, cu_q, cu_k, n_seq, total_q, w.cs, nullptr, f);
   const int64_t bb = (int64_t)mla_cache_block_bytes(&d);
   const uint8_t* pool8 = static_cast<const uint8_t*>(cache_pool);
   if (d.cache_dtype == MLA_FP8_E4M3)
@@ -661,7 +672,7 @@ mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t*
     hipLaunchKernelGGL(prefill_gather_kernel<false>, dim3((unsigned)(((int64_t)total_k * 72 + 255) / 256)), dim3(256), 0,
                        st, pool8, bb, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k, w.ckv, w.kr);
   launch_decompress(d, w.ckv, w_uk, w_uv, w, total_k, st);
-  launch_attention(d, n_seq, cu_q, cu_k, max_q, q_nope, w, gate, out, lse, st);
+  launch_attention(d, n_seq, cu_q, cu_k, max_q, q_nope, q_rope, w, gate, out, lse, st);
   return launch_status();
 }
 
