@@ -79,6 +79,10 @@ def parse():
                     help="sequences of the workload the CPU oracle is timed on (0 = skip)")
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode+combine calls (for profiling)")
+    ap.add_argument("--flush-mib", type=int, default=0,
+                    help="write a scratch buffer of this many MiB before every step (outside the kernels' events) so "
+                         "that a cache smaller than the 256 MB MALL is read from HBM; the step time is then the sum "
+                         "of per-step event brackets instead of the outer bracket")
     ap.add_argument("--upstream", action="store_true",
                     help="start the step from the hidden state: mla_project_down (W_DQ, W_DKV, W_KR and the append) "
                          "and mla_absorb_from_latent (W_UQ and the absorb) replace the append and the absorb")
@@ -205,18 +209,24 @@ def main():
     setup_s = time.time() - t0
     stream = torch.cuda.current_stream()
 
-    def run_step(ev_pair=None):
+    def run_step(ev=None):
+        """ev: events recorded before the decode, after it and after the combine, plus (with
+        --flush-mib) around the whole step."""
         if args.decode_only:
-            if ev_pair:
-                ev_pair[0].record(stream)
+            if ev:
+                ev[0].record(stream)
             M.decode(d, step.q_abs, pool, table, seqlens, args.num_splits, step.workspace, step.o_latent,
                      step.lse, stream=stream)
-            if ev_pair:
-                ev_pair[1].record(stream)
+            if ev:
+                ev[1].record(stream)
             if step.needs_combine:
                 M.combine(d, seqlens, table.shape[1], step.workspace, step.o_latent, step.lse,
                           args.num_splits, stream=stream)
+            if ev:
+                ev[2].record(stream)
             return
+        if ev and len(ev) > 3:
+            ev[3].record(stream)
         dd = step.d
         if args.upstream:
             M.project_down(dd, h_new, w_down, d_cq, step_inputs["new_seq_id"], step_inputs["new_pos"], table, pool,
@@ -228,17 +238,21 @@ def main():
                             step_inputs["w_uk"], step_inputs["new_c_kv"], step_inputs["new_k_rope"],
                             step_inputs["new_seq_id"], step_inputs["new_pos"], table, pool,
                             q_abs=step.q_abs.view(n_tok, H, -1), stream=stream)
-        if ev_pair:
-            ev_pair[0].record(stream)
+        if ev:
+            ev[0].record(stream)
         M.decode(dd, step.q_abs, pool, table, seqlens, args.num_splits, step.workspace, step.o_latent,
                  step.lse, stream=stream)
-        if ev_pair:
-            ev_pair[1].record(stream)
+        if ev:
+            ev[1].record(stream)
         if step.needs_combine:
             M.combine(dd, seqlens, table.shape[1], step.workspace, step.o_latent, step.lse, args.num_splits,
                       stream=stream)
+        if ev:
+            ev[2].record(stream)
         M.up_proj(dd, step.o_latent.view(n_tok, H, -1), step_inputs["w_uv"], out=step.out, stream=stream,
                   gate=gate)
+        if ev and len(ev) > 3:
+            ev[4].record(stream)
 
     if args.decode_only:   # the queries must exist once
         M.absorb_q(d, step_inputs["q_nope"], step_inputs["q_rope"], step_inputs["q_pos"], step_inputs["w_uk"],
@@ -246,17 +260,25 @@ def main():
     for _ in range(args.warmup):
         run_step()
     torch.cuda.synchronize()
-    evs = [(TimingEvent(), TimingEvent()) for _ in range(args.steps)]
+    n_ev = 5 if args.flush_mib > 0 else 3
+    evs = [tuple(TimingEvent() for _ in range(n_ev)) for _ in range(args.steps)]
+    scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
+        if scratch is not None:
+            scratch.fill_(i & 255)      # evicts the cache from the MALL; outside the step's events
         run_step(evs[i])
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
-    ms_step = ms_total / args.steps
-    dec_ms = sum(a.elapsed_time(b) for a, b in evs) / args.steps
+    if scratch is not None:
+        ms_step = sum(e[3].elapsed_time(e[4]) for e in evs) / args.steps
+    else:
+        ms_step = ms_total / args.steps
+    dec_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    dec_comb_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
 
     total_tokens = int(inp["seqlens"].to(torch.int64).sum())
     cache_bytes = total_tokens * (bb // w.block_size)              # the cache read once
@@ -287,8 +309,11 @@ def main():
                    "d_rope": w.d_rope, "d_nope": w.d_nope, "d_v": w.d_v, "seqlen": w.seqlen,
                    "block_size": w.block_size, "cache_dtype": w.cache_dtype, "output_gate": bool(args.gated),
                    "from_hidden_state": bool(args.upstream),
+                   "cache_flush_mib": args.flush_mib,
                    "parallelism": "single GPU"},
         "decode_ms": round(dec_ms, 4),
+        "decode_combine_ms": round(dec_comb_ms, 4),
+        "decode_combine_tokens_per_s": round(n_tok / (dec_comb_ms * 1e-3), 1),
         "decode_hbm_gbps": round(dec_gbps, 1),
         "decode_tflops": round(dec_tflops, 1),
         "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
@@ -406,8 +431,18 @@ def cpu_baseline(w, inp, n_seqs):
         cores = max(int(p.get("num_threads", 1)) for p in threadpool_info()) if threadpool_info() else 1
     except Exception:
         cores = torch.get_num_threads()
+    model = ""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(len(seqs) * w.q_per_seq / dt, 4), "unit": "tokens/s", "cores": cores,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": model, "os_cpu_count": os.cpu_count(),
+            "torch_threads": torch.get_num_threads(),
             "sample": f"{len(seqs)} of {w.batch} sequences x {w.q_per_seq} query rows, all {w.n_heads} heads, "
                       f"{int(inp['seqlens'][0])} cached tokens each, float64 numpy ({dt:.1f} s)"}
 
