@@ -110,6 +110,9 @@ mla_status check_decode_args(const mla_dims* d, int32_t n_seq, int32_t q_per_seq
   if (n_seq <= 0 || q_per_seq <= 0 || max_blocks <= 0 || num_splits < 0) return MLA_ERR_INVALID_ARG;
   if (static_cast<int64_t>(max_blocks) * d->block_size > (1LL << 30)) return MLA_ERR_UNSUPPORTED;
   if (static_cast<int64_t>(n_seq) * q_per_seq * d->n_heads > (1LL << 31) - 1) return MLA_ERR_UNSUPPORTED;
+  // the decode kernels index the 32-token key tiles of all sequences in 32 bits
+  if (static_cast<int64_t>(n_seq) * ((static_cast<int64_t>(max_blocks) * d->block_size + 31) / 32) > (1LL << 31) - 1)
+    return MLA_ERR_UNSUPPORTED;
   return MLA_OK;
 }
 

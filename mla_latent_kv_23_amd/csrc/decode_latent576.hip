@@ -60,8 +60,11 @@ constexpr int kOffScan = kOffFlag + 16;                     // 4 ints
 constexpr int kOffMisc = kOffScan + 16;                     // 2 ints
 static_assert(kOffMisc + 8 <= kOffP + kPBufBytes, "scratch inside P buffer 0");
 
-// epilogue staging: 64 rows of 512 fp32, padded by 16 bytes so that 8 lanes
-// writing 8 consecutive rows at one column hit 8 different 16-byte slots
+// epilogue staging: one row of 512 bf16 per pair, padded by 16 bytes (bf16
+// cache); 64 rows of 512 fp32, padded by 16 bytes so that 8 lanes writing 8
+// consecutive rows at one column hit 8 different 16-byte slots (fp8 cache)
+constexpr int kYRow = kDc * 2 + 16;
+static_assert(kPairs * kYRow <= kOffP, "epilogue staging fits in the tile stages");
 constexpr int kXRow = kDc * 4 + 16;
 static_assert(64 * kXRow <= kOffP, "epilogue staging fits in the tile stages");
 
@@ -83,7 +86,7 @@ struct Args {
 };
 
 // wait until at most n tiles' worth of this wave's loads are still in flight
-__device__ __forceinline__ void wait_tiles(int64_t n) {
+__device__ __forceinline__ void wait_tiles(int n) {
   if (n >= 3) wait_vmcnt<3 * kLoadsPerWave>();
   else if (n == 2) wait_vmcnt<2 * kLoadsPerWave>();
   else if (n == 1) wait_vmcnt<kLoadsPerWave>();
@@ -91,7 +94,7 @@ __device__ __forceinline__ void wait_tiles(int64_t n) {
 }
 
 
-__device__ __forceinline__ void wait_tiles_fp8(int64_t n) {
+__device__ __forceinline__ void wait_tiles_fp8(int n) {
   if (n >= 3) wait_vmcnt<3 * kF8LoadsPerWave>();
   else if (n == 2) wait_vmcnt<2 * kF8LoadsPerWave>();
   else if (n == 1) wait_vmcnt<kF8LoadsPerWave>();
@@ -131,9 +134,12 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
   lds_barrier();
   int wave_off = 0;
   for (int w = 0; w < wave; ++w) wave_off += scan[w];
-  const int64_t N = (int64_t)scan[0] + scan[1] + scan[2] + scan[3];
+  // Tile indices are 32-bit (the host bounds the tile count below 2^31); the
+  // count and the unit's range are wave-uniform and live in scalar registers.
+  const int N = __builtin_amdgcn_readfirstlane(scan[0]) + __builtin_amdgcn_readfirstlane(scan[1]) +
+                __builtin_amdgcn_readfirstlane(scan[2]) + __builtin_amdgcn_readfirstlane(scan[3]);
   const int excl = wave_off + incl - local;
-  const int64_t T0 = unit_first_tile(unit, N, G), T1 = unit_first_tile(unit + 1, N, G);
+  const int T0 = (int)unit_first_tile(unit, N, G), T1 = (int)unit_first_tile(unit + 1, N, G);
   lds_i32* misc = (lds_i32*)(lds + kOffMisc);
   if (local > 0 && T0 >= excl && T0 < excl + local) {
     int start = excl, b = s_lo;
@@ -213,26 +219,18 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
 
   // ---- the pieces: one per sequence overlapping [T0, T1)
   int b = b_first;
-  int64_t seq_start = b_first_start;
+  int seq_start = b_first_start;
   for (;;) {
     const int32_t L = seq_len(b);
-    const int64_t seq_end = seq_start + tiles_of(L);
-    const int64_t p0 = seq_start > T0 ? seq_start : T0;
-    const int64_t p1 = seq_end < T1 ? seq_end : T1;
+    const int seq_end = seq_start + tiles_of(L);
+    const int p0 = seq_start > T0 ? seq_start : T0;
+    const int p1 = seq_end < T1 ? seq_end : T1;
     const bool whole = seq_start >= T0 && seq_end <= T1;
     const int32_t* bt_row = block_table + (int64_t)b * a.max_blocks;
 
-    // queries of this sequence: B operand fragments, pair my_pair, dims 16k + 8*half .. +7
-    if (qk_wave) {
-      const int64_t row = ((int64_t)b * a.q_per_seq + my_j) * a.n_heads + my_s;
-      const bf16x8* src = (const bf16x8*)(a.q_abs + row * kDk) + half;
-#pragma unroll
-      for (int k = 0; k < kQSteps; ++k) q[k] = src[2 * k];
-    }
-    __builtin_amdgcn_s_waitcnt(0);           // queries resident before any tile load is queued
     float m_ref = -INFINITY, l_part = 0.f;
     // source of tile T of this sequence (rows beyond L or a padded block entry read block 0, masked)
-    auto tile_src = [&](int64_t T, int* valid) -> const uint8_t* {
+    auto tile_src = [&](int T, int* valid) -> const uint8_t* {
       const int tok0 = (int)(T - seq_start) * kTile;
       *valid = min(kTile, L - tok0);
       const int32_t blk = bt_row[tok0 / a.block_size];
@@ -243,13 +241,13 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       return a.pool + (int64_t)blk * a.block_bytes + (int64_t)(tok0 % a.block_size) * kRowBytes;
     };
     // rows of tile T that hold tokens of the sequence (0 for a padding block entry)
-    auto tile_valid = [&](int64_t T) -> int {
+    auto tile_valid = [&](int T) -> int {
       const int tok0 = (int)(T - seq_start) * kTile;
       return bt_row[tok0 / a.block_size] < 0 ? 0 : min(kTile, L - tok0);
     };
     // issue this wave's share of the loads of tile T: bf16 straight into ring
     // stage T % kStages; fp8 into staging slot T % 3 (expanded later)
-    auto load_tile = [&](int64_t T) {
+    auto load_tile = [&](int T) {
       if constexpr (!kFp8) {
         int valid;
         const uint8_t* src = tile_src(T, &valid);
@@ -263,19 +261,33 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       }
     };
     // wait until at most n tiles' loads of this wave are still in flight
-    auto wait_tile = [&](int64_t n) {
+    auto wait_tile = [&](int n) {
       if constexpr (!kFp8) wait_tiles(n);
       else wait_tiles_fp8(n);
     };
     // fp8: staged tile T -> bf16 buffer T % 2
-    auto expand = [&](int64_t T) {
+    auto expand = [&](int T) {
       expand_tile_fp8(lds + kOffF + (int)(T % kF8Slots) * kF8StageBytes, lds + (int)(T & 1) * kTileBytes, wave);
     };
     // LDS address of tile T's bf16 image
-    auto tile_base = [&](int64_t T) -> uint32_t {
+    auto tile_base = [&](int T) -> uint32_t {
       const int slot = kFp8 ? (int)(T & 1) : (int)(T % kStages);
       return (uint32_t)(uintptr_t)(lds + slot * kTileBytes);
     };
+
+    // The first tiles of the piece are queued right behind the queries, so
+    // the two fetches overlap; one full wait then leaves the compiler no query
+    // load pending inside the tile loop.
+    // queries of this sequence: B operand fragments, pair my_pair, dims 16k + 8*half .. +7
+    if (qk_wave) {
+      const int64_t row = ((int64_t)b * a.q_per_seq + my_j) * a.n_heads + my_s;
+      const bf16x8* src = (const bf16x8*)(a.q_abs + row * kDk) + half;
+#pragma unroll
+      for (int k = 0; k < kQSteps; ++k) q[k] = src[2 * k];
+    }
+    int pre = 0;                         // tiles of the first attempt already issued
+    for (; pre < kStages - 2 && p0 + pre < p1; ++pre) load_tile(p0 + pre);
+    __builtin_amdgcn_s_waitcnt(0);           // queries and the first tiles resident
 
     for (;;) {                               // attempts: a second one only after a reference jump
 #pragma unroll
@@ -285,8 +297,9 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         for (int i = 0; i < 16; ++i) o15[i] = 0.f;
       }
       l_part = 0.f;
-      int64_t T_issue = p0;                  // loads in flight cover [T, T_issue)
-      for (int st = 0; st < kStages - 1 && T_issue < p1; ++st) load_tile(T_issue++);
+      int T_issue = p0 + pre;            // loads in flight cover [T, T_issue)
+      pre = 0;                               // a second attempt loads every tile again
+      while (T_issue - p0 < kStages - 1 && T_issue < p1) load_tile(T_issue++);
       bool redo = false;                     // a reference jumped during this attempt (wave-uniform)
       wait_tile(T_issue - 1 - p0);           // tile p0 has landed
       lds_barrier();
@@ -299,7 +312,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       // weights go to P buffer T % 2.  The scale is positive (checked by the
       // API), so the max of the raw scores gives the max of the scaled ones and
       // the scale folds into one FMA per weight.
-      auto softmax = [&](const f32x16& sacc, const float (&s_rope)[16], int64_t T) {
+      auto softmax = [&](const f32x16& sacc, const float (&s_rope)[16], int T) {
         const int tok0 = (int)(T - seq_start) * kTile;
         float sv[16], sc[16];
         if constexpr (kFp8) {
@@ -377,7 +390,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       };
 
       // ---- O^T += V^T P^T for tile T: this wave's 128 dims x all 128 pairs
-      auto pv = [&](uint32_t tb, int64_t T) {
+      auto pv = [&](uint32_t tb, int T) {
         f32x16 t15 = {};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
@@ -421,7 +434,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       // the slot of T, and tile T+1 is expanded into the bf16 buffer of T-1
       // (whose PV also finished before it).  The second publishes the expanded
       // tile T+1 and ends PV(T).
-      for (int64_t T = p0; T < p1; ++T) {
+      for (int T = p0; T < p1; ++T) {
         const uint32_t tb = tile_base(T);
         if (qk_wave) {
           // ---- S^T = K Q^T for this wave's 32 pairs: lane holds pair my_pair, tokens 8(i/4)+4*half+i%4.
@@ -489,11 +502,12 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     }
 
     // ---- finish the piece.  The accumulators go out through LDS (free now:
-    // every load has landed and every wave is past the last tile), 64 pairs at
-    // a time, so that each store instruction writes 1 KB of one output row
-    // instead of 32-byte pieces of 32 rows.  A piece that is a whole sequence
-    // is normalised on the way (bf16 o_lat and lse); any other piece leaves its
-    // raw partial (relative to 2^m) and (m, l) in slot unit + b.
+    // every load has landed and every wave is past the last tile): each lane
+    // rounds its pair's values to bf16 into one 1 KB row per pair, so that each
+    // store instruction writes 1 KB of one output row instead of 32-byte pieces
+    // of 32 rows.  A piece that is a whole sequence is normalised on the way
+    // (bf16 o_lat and lse); any other piece leaves its raw partial (relative to
+    // 2^m) and (m, l) in slot unit + b.
     const int64_t slot_row0 = (int64_t)(unit + b) * rows_per_seq;
     float l_tot;
     {
@@ -510,13 +524,17 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       s_l[my_pair] = l_tot;
       s_m[my_pair] = m_ref;
     }
+    if constexpr (!kFp8) {
+      lds_barrier();                               // every pair's l is in LDS
+      // a partial is stored raw (a factor of 1 is exact), a whole sequence normalised
+      const bool norm = whole;
 #pragma unroll
-    for (int hp = 0; hp < (kPB + 1) / 2; ++hp) {   // pairs 64*hp .. 64*hp+63
-      constexpr int kHalfPairs = kPB == 1 ? 32 : 64;
-#pragma unroll
-      for (int pbl = 0; pbl < kHalfPairs / 32; ++pbl) {
-        const int pb = 2 * hp + pbl;
-        lds_u8* xrow = lds + (32 * pbl + (lane & 31)) * kXRow + (128 * wave + 4 * half) * 4;
+      for (int pb = 0; pb < kPB; ++pb) {
+        const int pair = 32 * pb + (lane & 31);
+        const float l = s_l[pair];
+        const float inv = !norm ? 1.0f : l > 0.f ? 1.0f / l : 0.f;
+        // lane: dims 128 wave + 32 db + 8 (i / 4) + 4 half + i % 4 of its pair
+        lds_u8* yrow = lds + pair * kYRow + (128 * wave + 4 * half) * 2;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -525,34 +543,73 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
             if (kSplitTile && db * kPB + pb == 15) v = f32x4{o15[4 * qq], o15[4 * qq + 1], o15[4 * qq + 2], o15[4 * qq + 3]};
             else v = f32x4{o[db * kPB + pb][4 * qq], o[db * kPB + pb][4 * qq + 1], o[db * kPB + pb][4 * qq + 2],
                            o[db * kPB + pb][4 * qq + 3]};
-            *(lds_f32x4*)(xrow + (32 * db + 8 * qq) * 4) = v;
+            // hardware pack, round to nearest even
+            const bf16x2 lo = __builtin_convertvector(f32x2{v[0] * inv, v[1] * inv}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector(f32x2{v[2] * inv, v[3] * inv}, bf16x2);
+            *(lds_u32x2*)(yrow + (32 * db + 8 * qq) * 2) = u32x2{*(const uint32_t*)&lo, *(const uint32_t*)&hi};
           }
       }
-      lds_barrier();                              // the rows (and s_l, s_m) are in LDS
-      // thread t: 16-byte chunk t % 128 of rows t / 128 + 2k
-      const int c = tid & 127;
+      lds_barrier();                                // the rows (and s_l, s_m) are in LDS
+      {
+        // thread t: 16-byte chunk t % 64 of rows t / 64 + 4k (one wave writes one 1 KB row)
+        const int c = tid & 63;
+        uint16_t* const dst0 = (norm ? a.o_final + (int64_t)b * rows_per_seq * kDc : a.ws_o + slot_row0 * kDc) + 8 * c;
 #pragma unroll 4
-      for (int k = 0; k < kHalfPairs / 2; ++k) {
-        const int r = (tid >> 7) + 2 * k;
-        const int pair = 64 * hp + r;
-        if (kPB != 4 && pair / hpw >= a.q_per_seq) continue;   // padding
-        const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
-        const f32x4 v = *(const lds_f32x4*)(lds + r * kXRow + c * 16);
-        if (!whole) {
-          u32x2 pk2;
-          pk2[0] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-          pk2[1] = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-          *(u32x2*)(a.ws_o + (slot_row0 + row_in_seq) * kDc + 4 * c) = pk2;
-        } else {
-          const float l = s_l[pair];
-          const float inv = l > 0.f ? 1.0f / l : 0.f;
-          u32x2 pk2;
-          pk2[0] = (uint32_t)f32_to_bf16_bits(v[0] * inv) | ((uint32_t)f32_to_bf16_bits(v[1] * inv) << 16);
-          pk2[1] = (uint32_t)f32_to_bf16_bits(v[2] * inv) | ((uint32_t)f32_to_bf16_bits(v[3] * inv) << 16);
-          *(u32x2*)(a.o_final + ((int64_t)b * rows_per_seq + row_in_seq) * kDc + 4 * c) = pk2;
+        for (int k = 0; k < 8 * kPB; ++k) {
+          const int pair = (tid >> 6) + 4 * k;
+          if (kPB != 4 && pair / hpw >= a.q_per_seq) continue;   // padding
+          const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
+          const u32x4 v = *(const lds_u32x4*)(lds + pair * kYRow + c * 16);
+          *(u32x4*)(dst0 + (int64_t)row_in_seq * kDc) = v;
         }
       }
-      lds_barrier();                              // the staging rows are free again
+    } else {
+      // fp8: fp32 rows, 64 pairs at a time, rounded on the way out (the bf16
+      // staging above needs registers this instantiation does not have)
+#pragma unroll
+      for (int hp = 0; hp < (kPB + 1) / 2; ++hp) {   // pairs 64*hp .. 64*hp+63
+        constexpr int kHalfPairs = kPB == 1 ? 32 : 64;
+#pragma unroll
+        for (int pbl = 0; pbl < kHalfPairs / 32; ++pbl) {
+          const int pb = 2 * hp + pbl;
+          lds_u8* xrow = lds + (32 * pbl + (lane & 31)) * kXRow + (128 * wave + 4 * half) * 4;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) {
+              f32x4 v;
+              if (kSplitTile && db * kPB + pb == 15) v = f32x4{o15[4 * qq], o15[4 * qq + 1], o15[4 * qq + 2], o15[4 * qq + 3]};
+              else v = f32x4{o[db * kPB + pb][4 * qq], o[db * kPB + pb][4 * qq + 1], o[db * kPB + pb][4 * qq + 2],
+                             o[db * kPB + pb][4 * qq + 3]};
+              *(lds_f32x4*)(xrow + (32 * db + 8 * qq) * 4) = v;
+            }
+        }
+        lds_barrier();                              // the rows (and s_l, s_m) are in LDS
+        // thread t: 16-byte chunk t % 128 of rows t / 128 + 2k
+        const int c = tid & 127;
+#pragma unroll 4
+        for (int k = 0; k < kHalfPairs / 2; ++k) {
+          const int r = (tid >> 7) + 2 * k;
+          const int pair = 64 * hp + r;
+          if (kPB != 4 && pair / hpw >= a.q_per_seq) continue;   // padding
+          const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
+          const f32x4 v = *(const lds_f32x4*)(lds + r * kXRow + c * 16);
+          if (!whole) {
+            u32x2 pk2;
+            pk2[0] = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
+            pk2[1] = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
+            *(u32x2*)(a.ws_o + (slot_row0 + row_in_seq) * kDc + 4 * c) = pk2;
+          } else {
+            const float l = s_l[pair];
+            const float inv = l > 0.f ? 1.0f / l : 0.f;
+            u32x2 pk2;
+            pk2[0] = (uint32_t)f32_to_bf16_bits(v[0] * inv) | ((uint32_t)f32_to_bf16_bits(v[1] * inv) << 16);
+            pk2[1] = (uint32_t)f32_to_bf16_bits(v[2] * inv) | ((uint32_t)f32_to_bf16_bits(v[3] * inv) << 16);
+            *(u32x2*)(a.o_final + ((int64_t)b * rows_per_seq + row_in_seq) * kDc + 4 * c) = pk2;
+          }
+        }
+        lds_barrier();                              // the staging rows are free again
+      }
     }
     if (whole && tid < 32 * kPB && (kPB == 4 || tid / hpw < a.q_per_seq)) {
       const int pair = tid;
