@@ -263,6 +263,40 @@ def test_decode_tile_edges(lens, cache, cuda_device):
 
 
 @pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("block_size", [16, 32, 128, 256])
+def test_decode_block_sizes(block_size, cache, cuda_device):
+    """Paged blocks of 16 (not a whole 32-token tile: the generic decode), 32,
+    128 and 256 tokens (the tuned decode; a tile then starts inside a block),
+    for both cache formats: the append writes each block's layout and the
+    decode reads it through a shuffled block table with padded entries."""
+    import mla_latent_kv_23_amd as M
+    lens = [1, 200, 513]
+    w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=len(lens), cache_dtype=cache, block_size=block_size)
+    inp = S.make_inputs(w, 5150 + block_size, seqlens=torch.tensor(lens, dtype=torch.int32), spare_blocks=2)
+    U.say(f"[blocks] {cache} block_size={block_size}")
+    d = U.dims_of(w)
+    pos = S.query_positions(inp["seqlens"], 1).numpy()
+    q_abs = O.absorb_q(inp["q_nope"].double().numpy(), inp["q_rope"].double().numpy(),
+                       pos[:, :, None] * np.ones((1, 1, w.n_heads), np.int64), inp["w_uk"].double().numpy(),
+                       w.rope_base)
+    q_dev = U.to_act(q_abs, "bf16", cuda_device)
+    q_r = q_dev.double().cpu().numpy()
+    pool = U.gpu_pool(w, inp, cuda_device, poison=0xFF)
+    bt, L = inp["block_table"].to(cuda_device), inp["seqlens"].to(cuda_device)
+    cu = inp["cu_seqlens"].numpy()
+    for ns in [0, 1, 4]:
+        o_lat, lse, ws = M.decode(d, q_dev, pool, bt, L, num_splits=ns)
+        M.combine(d, L, bt.shape[1], ws, o_lat, lse, num_splits=ns)
+        for b, Lb in enumerate(lens):
+            c, kr = O.cached_token_values(inp["c_kv"][cu[b]:cu[b] + Lb].double().numpy(),
+                                          inp["k_rope"][cu[b]:cu[b] + Lb].double().numpy(), np.arange(Lb), cache,
+                                          w.rope_base)
+            want_o, want_lse = O.decode_absorbed_form(q_r[b], c, kr, pos[b], w.softmax_scale)
+            U.assert_close(o_lat[b], want_o, "bf16", f"o_lat L={Lb} splits={ns}")
+            U.assert_close(lse[b], want_lse, "bf16", f"lse L={Lb} splits={ns}")
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
 def test_decode_large_logit_jump(cache, cuda_device):
     """Late keys with much larger scores than the first tile: the kernel's per-pair
     reference max must move (second pass) and still match the oracle."""
