@@ -87,6 +87,38 @@ def test_prefill_paged_matches_oracle(heads, lens, qlens, cache, cuda_device):
         U.assert_close(lse[qs][:, heads_chk], want_lse, "bf16", f"lse seq {b} L={L} Lq={Lq}")
 
 
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
+@pytest.mark.parametrize("block_size", [16, 32, 128])
+def test_prefill_paged_block_sizes(block_size, cache, cuda_device):
+    """Chunked prefill reading the paged cache through blocks of 16, 32 and 128
+    tokens (a shuffled table with padded entries) in both cache formats."""
+    import mla_latent_kv_23_amd as M
+    lens, qlens = [300, 77], [100, 77]
+    w = V3.replace(n_heads=16, cache_dtype=cache, block_size=block_size)
+    inp = S.make_chunk_prefill_inputs(w, 6100 + block_size, torch.tensor(lens, dtype=torch.int32),
+                                      torch.tensor(qlens, dtype=torch.int32))
+    U.say(f"[prefill_paged blocks] block_size={block_size} cache={cache}")
+    d = U.dims_of(w)
+    dev = cuda_device
+    pool = U.gpu_pool(w, inp, dev)
+    out, lse, _ = M.prefill_paged(d, inp["q_nope"].to(dev), inp["q_rope"].to(dev), inp["cu_q"].to(dev), max(qlens),
+                                  inp["cu_k"].to(dev), sum(lens), pool, inp["block_table"].to(dev),
+                                  inp["w_uk"].to(dev), inp["w_uv"].to(dev))
+    torch.cuda.synchronize()
+    cu_q, cu_k = inp["cu_q"].tolist(), inp["cu_k"].tolist()
+    for b, (L, Lq) in enumerate(zip(lens, qlens)):
+        ks, qs = slice(cu_k[b], cu_k[b] + L), slice(cu_q[b], cu_q[b] + Lq)
+        c, kr = O.cached_token_values(inp["c_kv"][ks].double().numpy(), inp["k_rope"][ks].double().numpy(),
+                                      np.arange(L), w.cache_dtype, w.rope_base)
+        want_o, want_lse = O.prefill_chunk_mha_form(inp["q_nope"][qs].double().numpy(),
+                                                    inp["q_rope"][qs].double().numpy(), c, kr,
+                                                    inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
+                                                    w.softmax_scale, w.rope_base, heads=list(range(16)),
+                                                    operand_dtype="bf16")
+        U.assert_close(out[qs], want_o, "bf16", f"out seq {b} L={L} Lq={Lq}")
+        U.assert_close(lse[qs], want_lse, "bf16", f"lse seq {b} L={L} Lq={Lq}")
+
+
 @pytest.mark.parametrize("paged", [False, True])
 def test_prefill_output_gate(paged, cuda_device):
     """Gated MLA in prefill: out = sigmoid(gate) * o against the oracle's gated
