@@ -196,11 +196,15 @@ def test_chain_vs_non_absorbed_oracle(name, cuda_device):
 
 
 @pytest.mark.parametrize("cache", ["bf16", "fp8"])
-@pytest.mark.parametrize("heads,sq", [(16, 1), (16, 2), (32, 1), (64, 1), (64, 2), (96, 1)])
+@pytest.mark.parametrize("heads,sq", [(16, 1), (16, 2), (32, 1), (64, 1), (64, 2), (96, 1),
+                                     (128, 4), (16, 4), (16, 8), (128, 3)])
 def test_decode_head_counts(heads, sq, cache, cuda_device):
     """The tuned decode with fewer (query row, head) pairs than a full
     128-pair work-group: one, two or three head groups of 32 or 64 pairs,
-    with padding pairs (16 heads x 1 row in 32 pairs) that must store nothing."""
+    with padding pairs (16 heads x 1 row in 32 pairs) that must store nothing;
+    and more query rows per sequence (4 or 8 new tokens, each row seeing the
+    cache up to its own position), including 3 rows, which no pair block
+    divides (the generic decode)."""
     import mla_latent_kv_23_amd as M
     w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=3, n_heads=heads, q_per_seq=sq, cache_dtype=cache)
     lens = [300, 33, 1000]
