@@ -221,9 +221,9 @@ mla_status mla_absorb_append(const mla_dims* dims, int32_t n_q, const void* q_no
  * Shapes: q_abs [n_seq, q_per_seq, H, d_c + d_rope] (act), cache_seqlens
  * [n_seq] int32 with q_per_seq <= L <= max_blocks * block_size,
  * block_table [n_seq, max_blocks].  Outputs o_latent [n_seq, q_per_seq, H, d_c]
- * (act) and lse [n_seq, q_per_seq, H] (float32).  Sizes beyond
+ * (act) and lse [n_seq, q_per_seq, H] (float32).  MLA_ERR_UNSUPPORTED when
  * max_blocks * block_size > 2^30, n_seq * q_per_seq * H >= 2^31 or
- * n_seq * ceil(max_blocks * block_size / 32) >= 2^31 give MLA_ERR_UNSUPPORTED.
+ * n_seq * ceil(max_blocks * block_size / 32) >= 2^31 (32-token key tiles).
  * The key range may be split over work-groups ("num_splits": 0 = automatic,
  * > 0 = that many work units); the partial results then go to `workspace`
  * (at least mla_decode_workspace_bytes) and mla_combine must follow with the

@@ -93,6 +93,12 @@ def test_unsupported_combinations(lib):
         assert lib.mla_up_proj(ctypes.byref(d), 4, FAKE, FAKE, FAKE, None) == 2
     big = M.make_dims(**{**V3, "d_rope": 130})
     assert lib.mla_up_proj(ctypes.byref(big), 4, FAKE, FAKE, FAKE, None) == 2
+    # decode size limits: a sequence longer than 2^30 tokens, and 2^31 key tiles of 32 tokens in all
+    d = M.make_dims(**V3)
+    r = ctypes.byref(d)
+    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, FAKE, (1 << 24) + 1, FAKE, 0, FAKE, 1 << 40, FAKE, FAKE, None) == 2
+    assert lib.mla_decode(r, 64, 1, FAKE, FAKE, FAKE, 1 << 24, FAKE, 0, FAKE, 1 << 40, FAKE, FAKE, None) == 2
+    assert lib.mla_decode_workspace_bytes(r, 64, 1, 1 << 24, 0) == 0
 
 
 def test_empty_calls_do_nothing(lib):
