@@ -25,8 +25,9 @@
 //    to bf16 and exchanged through LDS.  Should a later tile exceed the
 //    reference by more than 2^16, the reference is raised and the sequence
 //    piece is computed once more (never in practice; it keeps the result
-//    exact without ever rescaling the accumulators, which are only ever
-//    MFMA-updated, zeroed or stored raw).
+//    exact without ever rescaling the accumulators, which inside the tile
+//    loop are only ever MFMA-updated or zeroed; they are read out once, in
+//    the epilogue).
 //  * O^T += V^T P^T on bf16 MFMA 32x32x16: wave w owns latent dims
 //    128w..128w+127 for all 128 pairs (fp32 accumulators, 256 per lane); V^T
 //    comes straight from the row-major tile with the LDS transpose read.
