@@ -301,6 +301,41 @@ def test_decode_block_sizes(block_size, cache, cuda_device):
 
 
 @pytest.mark.parametrize("cache", ["bf16", "fp8"])
+def test_decode_reuses_one_workspace(cache, cuda_device):
+    """Two decodes in a row on one workspace and one output buffer, the second
+    with shorter sequences (fewer tiles, other split points): nothing left in
+    the partial slots by the first call may leak into the second."""
+    import mla_latent_kv_23_amd as M
+    w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=3, cache_dtype=cache)
+    inp = S.make_inputs(w, 8080, seqlens=torch.tensor([900, 257, 1500], dtype=torch.int32))
+    U.say(f"[reuse] {cache}")
+    d = U.dims_of(w)
+    pool = U.gpu_pool(w, inp, cuda_device, poison=0xFF)
+    bt = inp["block_table"].to(cuda_device)
+    cu = inp["cu_seqlens"].numpy()
+    ws = o_lat = lse = None
+    for lens in ([900, 257, 1500], [33, 200, 640]):
+        L_host = torch.tensor(lens, dtype=torch.int32)
+        pos = S.query_positions(L_host, 1).numpy()
+        q_abs = O.absorb_q(inp["q_nope"].double().numpy(), inp["q_rope"].double().numpy(),
+                           pos[:, :, None] * np.ones((1, 1, w.n_heads), np.int64), inp["w_uk"].double().numpy(),
+                           w.rope_base)
+        q_dev = U.to_act(q_abs, "bf16", cuda_device)
+        q_r = q_dev.double().cpu().numpy()
+        L = L_host.to(cuda_device)
+        o_lat, lse, ws = M.decode(d, q_dev, pool, bt, L, num_splits=7, workspace=ws, o_latent=o_lat, lse=lse)
+        M.combine(d, L, bt.shape[1], ws, o_lat, lse, num_splits=7)
+        for b, Lb in enumerate(lens):
+            # the cache holds the first call's tokens; a shorter length reads a prefix of them
+            c, kr = O.cached_token_values(inp["c_kv"][cu[b]:cu[b] + Lb].double().numpy(),
+                                          inp["k_rope"][cu[b]:cu[b] + Lb].double().numpy(), np.arange(Lb), cache,
+                                          w.rope_base)
+            want_o, want_lse = O.decode_absorbed_form(q_r[b], c, kr, pos[b], w.softmax_scale)
+            U.assert_close(o_lat[b], want_o, "bf16", f"o_lat L={Lb}")
+            U.assert_close(lse[b], want_lse, "bf16", f"lse L={Lb}")
+
+
+@pytest.mark.parametrize("cache", ["bf16", "fp8"])
 def test_decode_large_logit_jump(cache, cuda_device):
     """Late keys with much larger scores than the first tile: the kernel's per-pair
     reference max must move (second pass) and still match the oracle."""
