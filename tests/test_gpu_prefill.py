@@ -40,6 +40,34 @@ def test_prefill_matches_oracle(heads, lens, cuda_device):
         U.assert_close(lse[sl], want_lse, "bf16", f"lse seq {b} L={L}")
 
 
+def test_prefill_reuses_one_workspace(cuda_device):
+    """Two prefills in a row on one workspace (sized for the larger), the second
+    with fewer and shorter prompts: the decompressed keys and values, the
+    rotation table and the rotated k_R of the first call may not leak into it."""
+    import mla_latent_kv_23_amd as M
+    w = V3.replace(n_heads=16)
+    dev = cuda_device
+    ws = None
+    for seed, lens in ((7001, [300, 129]), (7002, [65])):
+        inp = S.make_prefill_inputs(w, seed, torch.tensor(lens, dtype=torch.int32))
+        U.say(f"[prefill reuse] lens={lens}")
+        d = U.dims_of(w)
+        out, lse, ws = M.prefill(d, inp["q_nope"].to(dev), inp["q_rope"].to(dev), inp["c_kv"].to(dev),
+                                 inp["k_rope"].to(dev), inp["cu_seqlens"].to(dev), max(lens), inp["w_uk"].to(dev),
+                                 inp["w_uv"].to(dev), workspace=ws)
+        torch.cuda.synchronize()
+        cu = inp["cu_seqlens"].tolist()
+        for b, L in enumerate(lens):
+            sl = slice(cu[b], cu[b] + L)
+            want_o, want_lse = O.prefill_mha_form(inp["q_nope"][sl].double().numpy(),
+                                                  inp["q_rope"][sl].double().numpy(),
+                                                  inp["c_kv"][sl].double().numpy(), inp["k_rope"][sl].double().numpy(),
+                                                  inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
+                                                  w.softmax_scale, w.rope_base, operand_dtype="bf16")
+            U.assert_close(out[sl], want_o, "bf16", f"out seq {b} L={L}")
+            U.assert_close(lse[sl], want_lse, "bf16", f"lse seq {b} L={L}")
+
+
 def test_prefill_rejects_unsupported_dims(cuda_device):
     import mla_latent_kv_23_amd as M
     w = S.WORKLOADS["tiny_fp32"]
