@@ -195,6 +195,45 @@ def test_chain_vs_non_absorbed_oracle(name, cuda_device):
     U.assert_close(lse, ref["lse"], w.act_dtype, "lse")
 
 
+def test_decode_step_runs_on_the_callers_stream(cuda_device):
+    """The whole step on a side stream that is first held back by a spin kernel:
+    a launch that ignored the stream argument would run before its inputs exist
+    and break the result."""
+    import mla_latent_kv_23_amd as M
+    if not hasattr(torch.cuda, "_sleep"):
+        pytest.skip("torch.cuda._sleep is not available")
+    w, inp = _inputs("v3_bs64_ctx8k")
+    U.say("[stream] v3_bs64_ctx8k on a side stream")
+    d = U.dims_of(w)
+    dev = cuda_device
+    B, sq = inp["q_nope"].shape[:2]
+    new_rows = U.new_tokens(inp, sq)
+    old = torch.ones(inp["c_kv"].shape[0], dtype=torch.bool)
+    old[new_rows] = False
+    pool = U.gpu_pool(w, inp, dev, poison=0xFF, rows=torch.nonzero(old)[:, 0])
+    step = M.DecodeStep(d, B, sq, inp["block_table"].shape[1], device=dev)
+    n_tok = B * sq
+    args = dict(
+        q_nope=inp["q_nope"].reshape(n_tok, w.n_heads, -1).to(dev),
+        q_rope=inp["q_rope"].reshape(n_tok, w.n_heads, -1).to(dev),
+        q_pos=U.q_positions_flat(inp, sq).to(dev),
+        new_c_kv=inp["c_kv"][new_rows].to(dev), new_k_rope=inp["k_rope"][new_rows].to(dev),
+        new_seq_id=inp["tok_seq"][new_rows].to(dev), new_pos=inp["tok_pos"][new_rows].to(dev),
+        block_table=inp["block_table"].to(dev), seqlens=inp["seqlens"].to(dev), pool=pool,
+        w_uk=inp["w_uk"].to(dev), w_uv=inp["w_uv"].to(dev))
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()                    # default priority
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)             # a bounded spin of some milliseconds ahead of the step
+        out, o_lat, lse = step.run(**args, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref = O.decode_batch(inp, q_per_seq=sq, scale=w.softmax_scale, base=w.rope_base, cache_dtype=w.cache_dtype)
+    U.assert_close(out.view(B, sq, w.n_heads, w.d_v), ref["o"], w.act_dtype, "o")
+    U.assert_close(o_lat, ref["o_lat"], w.act_dtype, "o_lat")
+    U.assert_close(lse, ref["lse"], w.act_dtype, "lse")
+
+
 @pytest.mark.parametrize("cache", ["bf16", "fp8"])
 @pytest.mark.parametrize("heads,sq", [(16, 1), (16, 2), (32, 1), (64, 1), (64, 2), (96, 1),
                                      (128, 4), (16, 4), (16, 8), (128, 3)])
