@@ -68,6 +68,43 @@ def test_prefill_reuses_one_workspace(cuda_device):
             U.assert_close(lse[sl], want_lse, "bf16", f"lse seq {b} L={L}")
 
 
+def test_prefill_paged_runs_on_the_callers_stream(cuda_device):
+    """Chunked prefill (gather, rotation, decompression, attention) on a side
+    stream held back by a spin kernel: every launch must follow the stream."""
+    import mla_latent_kv_23_amd as M
+    if not hasattr(torch.cuda, "_sleep"):
+        pytest.skip("torch.cuda._sleep is not available")
+    lens, qlens = [700, 200], [200, 33]
+    w = V3.replace(n_heads=16)
+    inp = S.make_chunk_prefill_inputs(w, 7300, torch.tensor(lens, dtype=torch.int32),
+                                      torch.tensor(qlens, dtype=torch.int32))
+    U.say("[prefill_paged stream]")
+    d = U.dims_of(w)
+    dev = cuda_device
+    pool = U.gpu_pool(w, inp, dev)
+    args = [inp["q_nope"].to(dev), inp["q_rope"].to(dev), inp["cu_q"].to(dev), max(qlens), inp["cu_k"].to(dev),
+            sum(lens), pool, inp["block_table"].to(dev), inp["w_uk"].to(dev), inp["w_uv"].to(dev)]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()                    # default priority
+    with torch.cuda.stream(side):
+        torch.cuda._sleep(20_000_000)             # a bounded spin of some milliseconds ahead of the call
+        out, lse, _ = M.prefill_paged(d, *args, stream=side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    cu_q, cu_k = inp["cu_q"].tolist(), inp["cu_k"].tolist()
+    for b, (L, Lq) in enumerate(zip(lens, qlens)):
+        ks, qs = slice(cu_k[b], cu_k[b] + L), slice(cu_q[b], cu_q[b] + Lq)
+        c, kr = O.cached_token_values(inp["c_kv"][ks].double().numpy(), inp["k_rope"][ks].double().numpy(),
+                                      np.arange(L), w.cache_dtype, w.rope_base)
+        want_o, want_lse = O.prefill_chunk_mha_form(inp["q_nope"][qs].double().numpy(),
+                                                    inp["q_rope"][qs].double().numpy(), c, kr,
+                                                    inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
+                                                    w.softmax_scale, w.rope_base, heads=list(range(16)),
+                                                    operand_dtype="bf16")
+        U.assert_close(out[qs], want_o, "bf16", f"out seq {b} L={L} Lq={Lq}")
+        U.assert_close(lse[qs], want_lse, "bf16", f"lse seq {b} L={L} Lq={Lq}")
+
+
 def test_prefill_rejects_unsupported_dims(cuda_device):
     import mla_latent_kv_23_amd as M
     w = S.WORKLOADS["tiny_fp32"]
