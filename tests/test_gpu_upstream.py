@@ -133,11 +133,13 @@ def test_absorb_from_latent_matches_oracle(n_tok, cuda_device):
     _assert_rotated_close(q_abs[..., w.d_c:].double().cpu().numpy(), want[..., w.d_c:], "rotated q_R")
 
 
-@pytest.mark.parametrize("gated", [False, True])
-def test_decode_step_from_hidden_states(gated, cuda_device):
+@pytest.mark.parametrize("gated,side", [(False, False), (True, False), (True, True)])
+def test_decode_step_from_hidden_states(gated, side, cuda_device):
     """DecodeStep.run_from_hidden: down-projection + append, query path + absorb, decode,
     combine and the (gated) up-projection, against the oracle's chain: the new tokens'
-    latents and keys from project_down, the queries from query_from_latent."""
+    latents and keys from project_down, the queries from query_from_latent.  With
+    `side`, the step runs on a side stream held back by a spin kernel, so a launch
+    that ignored the stream argument would run before its inputs exist."""
     import mla_latent_kv_23_amd as M
     w = V3.replace(batch=2)
     lens = [300, 70]
@@ -153,11 +155,22 @@ def test_decode_step_from_hidden_states(gated, cuda_device):
     q_pos = S.query_positions(inp["seqlens"], 1).reshape(-1)
     gate = S.make_gate_logits(w, 832, 2) if gated else None
     step = M.DecodeStep(d, 2, 1, table.shape[1], device=dev)
-    out, _, _ = step.run_from_hidden(
+    args = dict(
         h=up["h"].to(dev), w_down=up["w_down"].to(dev), d_cq=up["d_cq"], w_uq=up["w_uq"].to(dev),
         q_pos=q_pos.to(dev), new_seq_id=inp["tok_seq"][new_rows].to(dev), new_pos=inp["tok_pos"][new_rows].to(dev),
         block_table=table, seqlens=inp["seqlens"].to(dev), pool=pool, w_uk=inp["w_uk"].to(dev),
         w_uv=inp["w_uv"].to(dev), gate=None if gate is None else gate.to(dev))
+    if not side:
+        out, _, _ = step.run_from_hidden(**args)
+    else:
+        if not hasattr(torch.cuda, "_sleep"):
+            pytest.skip("torch.cuda._sleep is not available")
+        torch.cuda.synchronize()
+        stream = torch.cuda.Stream()              # default priority
+        with torch.cuda.stream(stream):
+            torch.cuda._sleep(20_000_000)         # a bounded spin of some milliseconds ahead of the step
+            out, _, _ = step.run_from_hidden(**args, stream=stream)
+        torch.cuda.current_stream().wait_stream(stream)
     torch.cuda.synchronize()
     cq, ckv, kr = O.project_down(up["h"].double().numpy(), up["w_down"].double().numpy(), up["d_cq"], w.d_c, w.d_rope)
     q_abs = O.query_from_latent(cq, up["w_uq"].double().numpy(), q_pos.numpy(), inp["w_uk"].double().numpy(), w.d_nope,
