@@ -34,9 +34,12 @@
  *    MLA_ERR_LAUNCH if the runtime rejected a launch.  Faults inside a kernel
  *    surface at the caller's next synchronisation.  No call synchronises.
  *  - Integer index arrays (positions, sequence ids, block tables, lengths) are
- *    int32 device arrays; their CONTENTS are trusted: the host cannot read
- *    them without synchronising.  Kernels skip (never dereference) block-table
- *    entries < 0 and tokens whose position falls outside the sequence's table.
+ *    int32 device arrays; the host cannot read them without synchronising, so
+ *    their contents are checked by the kernels: a block-table entry < 0 or
+ *    >= n_pool_blocks (the pool size every call that reads or writes the pool
+ *    takes) is padding and is never dereferenced, and a token whose position
+ *    falls outside its sequence's table is skipped.  What padding means for
+ *    each call is stated with it.
  *  - No call keeps mutable global state; concurrent calls on different streams
  *    are safe as long as their output/workspace buffers do not overlap.
  */
@@ -116,6 +119,8 @@ const char* mla_status_string(mla_status status);
  * Shapes: q_nope [n_tok, H, d_nope], q_rope [n_tok, H, d_rope] (unrotated),
  * pos [n_tok] int32 (>= 0), w_uk [H, d_nope, d_c], q_abs [n_tok, H, d_c + d_rope]
  * (output, act dtype; accumulation in float32).  n_tok may be 0 (no launch).
+ * With d_rope = 0 there is no RoPE part: q_rope and pos may be null and are
+ * not read; with d_rope > 0 a null q_rope or pos is MLA_ERR_INVALID_ARG.
  */
 mla_status mla_absorb_q(const mla_dims* dims, int32_t n_tok, const void* q_nope,
                         const void* q_rope, const int32_t* pos, const void* w_uk,
@@ -220,8 +225,11 @@ mla_status mla_absorb_append(const mla_dims* dims, int32_t n_q, const void* q_no
  *   o_lat[b, j, s, :] = sum_t exp(z_t - lse) * c_t
  * Shapes: q_abs [n_seq, q_per_seq, H, d_c + d_rope] (act), cache_seqlens
  * [n_seq] int32 with q_per_seq <= L <= max_blocks * block_size,
- * block_table [n_seq, max_blocks].  Outputs o_latent [n_seq, q_per_seq, H, d_c]
- * (act) and lse [n_seq, q_per_seq, H] (float32).  MLA_ERR_UNSUPPORTED when
+ * block_table [n_seq, max_blocks], cache_pool: n_pool_blocks (> 0) blocks.
+ * The tokens of a block-table entry < 0 or >= n_pool_blocks are left out of
+ * the softmax (never read); a query row that sees no token gets o_lat = 0
+ * and lse = -inf.  Outputs o_latent [n_seq, q_per_seq, H, d_c] (act) and
+ * lse [n_seq, q_per_seq, H] (float32).  MLA_ERR_UNSUPPORTED when
  * max_blocks * block_size > 2^30, n_seq * q_per_seq * H >= 2^31 or
  * n_seq * ceil(max_blocks * block_size / 32) >= 2^31 (32-token key tiles).
  * The key range may be split over work-groups ("num_splits": 0 = automatic,
@@ -231,10 +239,11 @@ mla_status mla_absorb_append(const mla_dims* dims, int32_t n_q, const void* q_no
  * mla_decode_needs_combine; calling it when it has none is a cheap no-op.
  */
 mla_status mla_decode(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
-                      const void* q_abs, const void* cache_pool, const int32_t* block_table,
-                      int32_t max_blocks, const int32_t* cache_seqlens, int32_t num_splits,
-                      void* workspace, size_t workspace_bytes, void* o_latent, float* lse,
-                      mla_stream_t stream);
+                      const void* q_abs, const void* cache_pool, int64_t n_pool_blocks,
+                      const int32_t* block_table, int32_t max_blocks,
+                      const int32_t* cache_seqlens, int32_t num_splits, void* workspace,
+                      size_t workspace_bytes, void* o_latent, float* lse, mla_stream_t stream);
+
 
 /* 1 if mla_decode with these arguments leaves partials for mla_combine, else 0. */
 int32_t mla_decode_needs_combine(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
@@ -286,8 +295,15 @@ mla_status mla_up_proj_gated(const mla_dims* dims, int32_t n_tok, const void* o_
  *   query_i = [q_nope[i,s] | RoPE(q_rope[i,s], i)]
  *   z_t = softmax_scale <query_i, key_t>,  out[i,s] = sum_t softmax(z)_t value_t,
  *   lse[i,s] = ln sum_t exp(z_t).
- * The rotated keys and queries, the decompressed keys and values and the
- * softmax weights are rounded to bf16 as MFMA operands (fp32 accumulation).
+ * RoPE follows the rule of mla_dims.rope_base (the rotated pair formed in
+ * float64 and rounded to float32; the rotated key is then stored in bf16, as a
+ * bf16 cache holds it).  The decompression multiplies the bf16 latent by the
+ * bf16 weights with float32 sums; the attention's operands -- the query, the
+ * decompressed key and value, the rotated keys and the softmax weights -- are
+ * fp16 (each bf16 input converts exactly, each computed operand is rounded to
+ * nearest even) with float32 sums.  Decompressed keys and values must stay
+ * inside fp16's range (|x| < 65504).  The parity tests compare with the form
+ * above computed exactly.
  * Sequences are packed: cu_seqlens [n_seq + 1] (device int32, trusted: 0 =
  * cu[0] <= cu[1] <= ... <= cu[n_seq] = total_tokens, every length <= max_seqlen,
  * a host value); q_nope [T, H, d_nope], q_rope [T, H, d_rope] (unrotated),
@@ -322,22 +338,25 @@ mla_status mla_prefill(const mla_dims* dims, int32_t n_seq, const int32_t* cu_se
  *   query_j = [q_nope[j,s] | RoPE(q_rope[j,s], Lk_b - Lq_b + j)]
  * cu_q, cu_k [n_seq + 1]: device int32, trusted (0 = cu[0] <= ... <=
  * cu[n_seq] = total_q / total_k, Lq_b <= Lk_b, every Lq_b <= max_q, a host
- * value).  cache_pool and block_table [n_seq, max_blocks] as mla_decode; the
- * blocks covering tokens 0..Lk_b - 1 must be valid (trusted; a negative entry
- * there is read as a zero latent and key, one beyond the pool is not caught).  q_nope
+ * value).  cache_pool (n_pool_blocks > 0 blocks) and block_table [n_seq,
+ * max_blocks] as mla_decode; the blocks covering tokens 0..Lk_b - 1 should
+ * be valid: an entry there that is < 0 or >= n_pool_blocks is never read and
+ * its tokens enter as a zero latent and key.  q_nope
  * [total_q, H, d_nope], q_rope [total_q, H, d_rope] (unrotated), w_uk, w_uv,
  * gate (null or [total_q, H, d_v]), out [total_q, H, d_v] and lse [total_q, H]
  * as mla_prefill.  workspace: at least mla_prefill_paged_workspace_bytes,
  * 16-byte aligned.  Supported: the dims of mla_prefill with a bf16 or fp8
  * cache (else MLA_ERR_UNSUPPORTED); an fp8 latent enters the decompression as
- * bf16(code * scale), rounded once.  total_q = 0 launches nothing.
+ * its codes (exact) and the token's scale multiplies the float32 sums
+ * (W (code * scale) = scale * (W code)), before k_C and v are rounded to
+ * bf16.  total_q = 0 launches nothing.
  */
 size_t mla_prefill_paged_workspace_bytes(const mla_dims* dims, int32_t total_q, int32_t total_k);
 mla_status mla_prefill_paged(const mla_dims* dims, int32_t n_seq, const int32_t* cu_q,
                              int32_t total_q, int32_t max_q, const int32_t* cu_k, int32_t total_k,
                              const void* q_nope, const void* q_rope, const void* cache_pool,
-                             const int32_t* block_table, int32_t max_blocks, const void* w_uk,
-                             const void* w_uv, const void* gate, void* workspace,
+                             int64_t n_pool_blocks, const int32_t* block_table, int32_t max_blocks,
+                             const void* w_uk, const void* w_uv, const void* gate, void* workspace,
                              size_t workspace_bytes, void* out, float* lse, mla_stream_t stream);
 
 #ifdef __cplusplus

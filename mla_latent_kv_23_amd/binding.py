@@ -58,7 +58,7 @@ SIGNATURES = {
     "mla_absorb_q": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P, _P, _P]),
     "mla_append_cache": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P, _I64, _P]),
     "mla_decode_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I32, _I32]),
-    "mla_decode": (ctypes.c_int, [_DP, _I32, _I32, _P, _P, _P, _I32, _P, _I32, _P, _SZ, _P, _P, _P]),
+    "mla_decode": (ctypes.c_int, [_DP, _I32, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _P, _SZ, _P, _P, _P]),
     "mla_decode_needs_combine": (_I32, [_DP, _I32, _I32, _I32, _I32]),
     "mla_combine": (ctypes.c_int, [_DP, _I32, _I32, _P, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "mla_up_proj": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P]),
@@ -73,8 +73,8 @@ SIGNATURES = {
                                         _P, _P, _SZ, _P]),
     "mla_absorb_from_latent_workspace_bytes": (_SZ, [_DP, _I32, _I32]),
     "mla_absorb_from_latent": (ctypes.c_int, [_DP, _I32, _I32, _P, _P, _P, _P, _P, _P, _SZ, _P]),
-    "mla_prefill_paged": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _P, _P, _I32, _P, _P, _P, _P,
-                                         _SZ, _P, _P, _P]),
+    "mla_prefill_paged": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _I32, _P, _P, _P, _I64, _P, _I32, _P, _P, _P,
+                                         _P, _SZ, _P, _P, _P]),
 }
 
 
@@ -124,6 +124,14 @@ def act_torch_dtype(d: Dims):
 
 def cache_block_bytes(d: Dims) -> int:
     return load_library().mla_cache_block_bytes(ctypes.byref(d))
+
+
+def _pool_blocks(d: Dims, pool) -> int:
+    """Whole blocks in a uint8 pool tensor (the pool size the kernels bound block ids by)."""
+    bb = cache_block_bytes(d)
+    if pool.dtype != torch.uint8 or bb == 0 or pool.numel() % bb:
+        raise ValueError("pool must be a uint8 tensor of whole blocks")
+    return pool.numel() // bb
 
 
 def absorb_q(d: Dims, q_nope, q_rope, pos, w_uk, q_abs=None, stream=None):
@@ -176,8 +184,9 @@ def decode(d: Dims, q_abs, pool, block_table, seqlens, num_splits: int = 0, work
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    n_pool_blocks = _pool_blocks(d, pool)
     _check("mla_decode", load_library().mla_decode(
-        ctypes.byref(d), n_seq, q_per_seq, _ptr(q_abs, "q_abs", at), _ptr(pool, "pool", torch.uint8),
+        ctypes.byref(d), n_seq, q_per_seq, _ptr(q_abs, "q_abs", at), _ptr(pool, "pool", torch.uint8), n_pool_blocks,
         _ptr(block_table, "block_table", torch.int32), max_blocks, _ptr(seqlens, "seqlens", torch.int32),
         num_splits, _ptr(workspace, "workspace"), ws_bytes, _ptr(o_latent, "o_latent", at),
         _ptr(lse, "lse", torch.float32), _stream(stream)))
@@ -290,7 +299,8 @@ def prefill_paged(d: Dims, q_nope, q_rope, cu_q, max_q: int, cu_k, total_k: int,
     _check("mla_prefill_paged", load_library().mla_prefill_paged(
         ctypes.byref(d), n_seq, _ptr(cu_q, "cu_q", torch.int32), Tq, max_q, _ptr(cu_k, "cu_k", torch.int32),
         total_k, _ptr(q_nope, "q_nope", at), _ptr(q_rope, "q_rope", at), _ptr(pool, "pool", torch.uint8),
-        _ptr(block_table, "block_table", torch.int32), block_table.shape[1], _ptr(w_uk, "w_uk", at),
+        _pool_blocks(d, pool), _ptr(block_table, "block_table", torch.int32), block_table.shape[1],
+        _ptr(w_uk, "w_uk", at),
         _ptr(w_uv, "w_uv", at), _ptr(gate, "gate", at), _ptr(workspace, "workspace"), ws_bytes,
         _ptr(out, "out", at), _ptr(lse, "lse", torch.float32), _stream(stream)))
     return out, lse, workspace

@@ -217,11 +217,12 @@ int32_t mla_decode_needs_combine(const mla_dims* d, int32_t n_seq, int32_t q_per
 }
 
 mla_status mla_decode(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const void* q_abs,
-                      const void* cache_pool, const int32_t* block_table, int32_t max_blocks,
+                      const void* cache_pool, int64_t n_pool_blocks, const int32_t* block_table, int32_t max_blocks,
                       const int32_t* cache_seqlens, int32_t num_splits, void* workspace, size_t workspace_bytes,
                       void* o_latent, float* lse, mla_stream_t stream) {
   const mla_status s = check_decode_args(d, n_seq, q_per_seq, max_blocks, num_splits);
   if (s != MLA_OK) return s;
+  if (n_pool_blocks <= 0) return MLA_ERR_INVALID_ARG;
   if (!q_abs || !cache_pool || !block_table || !cache_seqlens || !o_latent || !lse) return MLA_ERR_INVALID_ARG;
   const DecodePlan plan = make_plan(*d, n_seq, q_per_seq, max_blocks, num_splits);
   if (plan.ws_bytes > 0 && (!workspace || workspace_bytes < plan.ws_bytes)) return MLA_ERR_WORKSPACE;
@@ -229,10 +230,10 @@ mla_status mla_decode(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (plan.kind == 1) {
     if (!aligned16(q_abs) || !aligned16(cache_pool) || !aligned16(o_latent)) return MLA_ERR_INVALID_ARG;
-    return launch_decode576(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, block_table, max_blocks, cache_seqlens,
-                            workspace, o_latent, lse, st);
+    return launch_decode576(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, n_pool_blocks, block_table, max_blocks,
+                            cache_seqlens, workspace, o_latent, lse, st);
   }
-  return launch_decode_generic(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, block_table, max_blocks,
+  return launch_decode_generic(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, n_pool_blocks, block_table, max_blocks,
                                cache_seqlens, plan.ws_bytes ? workspace : nullptr, o_latent, lse, st);
 }
 
@@ -315,13 +316,14 @@ size_t mla_prefill_paged_workspace_bytes(const mla_dims* d, int32_t total_q, int
 
 mla_status mla_prefill_paged(const mla_dims* d, int32_t n_seq, const int32_t* cu_q, int32_t total_q, int32_t max_q,
                              const int32_t* cu_k, int32_t total_k, const void* q_nope, const void* q_rope,
-                             const void* cache_pool, const int32_t* block_table, int32_t max_blocks,
-                             const void* w_uk, const void* w_uv, const void* gate, void* workspace,
+                             const void* cache_pool, int64_t n_pool_blocks, const int32_t* block_table,
+                             int32_t max_blocks, const void* w_uk, const void* w_uv, const void* gate, void* workspace,
                              size_t workspace_bytes, void* out, float* lse, mla_stream_t stream) {
   const mla_status s = dims_supported(d);
   if (s != MLA_OK) return s;
   if (!prefill_supported(*d) || d->cache_dtype == MLA_F32) return MLA_ERR_UNSUPPORTED;
-  if (n_seq <= 0 || total_q < 0 || max_q < 0 || total_k < 0 || max_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (n_seq <= 0 || total_q < 0 || max_q < 0 || total_k < 0 || max_blocks <= 0 || n_pool_blocks <= 0)
+    return MLA_ERR_INVALID_ARG;
   if (total_q == 0) return MLA_OK;
   if (!cu_q || !cu_k || !q_nope || !q_rope || !cache_pool || !block_table || !w_uk || !w_uv || !out || !lse)
     return MLA_ERR_INVALID_ARG;
@@ -334,8 +336,9 @@ mla_status mla_prefill_paged(const mla_dims* d, int32_t n_seq, const int32_t* cu
   if (!aligned16(q_nope) || !aligned16(q_rope) || !aligned16(cache_pool) || !aligned16(w_uk) || !aligned16(w_uv) ||
       !aligned16(workspace) || !aligned16(out) || (gate && !aligned16(gate)))
     return MLA_ERR_INVALID_ARG;
-  return launch_prefill_paged(*d, n_seq, cu_q, total_q, max_q, cu_k, total_k, q_nope, q_rope, cache_pool, block_table,
-                              max_blocks, w_uk, w_uv, gate, workspace, out, lse, static_cast<hipStream_t>(stream));
+  return launch_prefill_paged(*d, n_seq, cu_q, total_q, max_q, cu_k, total_k, q_nope, q_rope, cache_pool,
+                              n_pool_blocks, block_table, max_blocks, w_uk, w_uv, gate, workspace, out, lse,
+                              static_cast<hipStream_t>(stream));
 }
 
 namespace {

@@ -82,6 +82,7 @@ struct Args {
   uint16_t* ws_o;               // partials [slots][q_per_seq*H][512] bf16, raw (relative to 2^m)
   float* ws_stats;              // partials [slots][q_per_seq*H][2] = (m in log2 units, l)
   int64_t block_bytes;
+  int64_t n_pool_blocks;        // block ids outside [0, n_pool_blocks) are padding, never read
   int32_t max_blocks, block_size, n_seq, q_per_seq, n_heads, units, heads_per_wg;
   float scale_log2;             // softmax_scale * log2(e)
 };
@@ -230,12 +231,14 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     const int32_t* bt_row = block_table + (int64_t)b * a.max_blocks;
 
     float m_ref = -INFINITY, l_part = 0.f;
-    // source of tile T of this sequence (rows beyond L or a padded block entry read block 0, masked)
+    // a block-table entry names a block of the pool (else it is padding: its tokens are masked, never read)
+    auto in_pool = [&](int32_t blk) { return blk >= 0 && (int64_t)blk < a.n_pool_blocks; };
+    // source of tile T of this sequence (rows beyond L or a padding block entry read block 0, masked)
     auto tile_src = [&](int T, int* valid) -> const uint8_t* {
       const int tok0 = (int)(T - seq_start) * kTile;
       *valid = min(kTile, L - tok0);
       const int32_t blk = bt_row[tok0 / a.block_size];
-      if (blk < 0) {
+      if (!in_pool(blk)) {
         *valid = 0;
         return a.pool;
       }
@@ -244,20 +247,26 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     // rows of tile T that hold tokens of the sequence (0 for a padding block entry)
     auto tile_valid = [&](int T) -> int {
       const int tok0 = (int)(T - seq_start) * kTile;
-      return bt_row[tok0 / a.block_size] < 0 ? 0 : min(kTile, L - tok0);
+      return in_pool(bt_row[tok0 / a.block_size]) ? min(kTile, L - tok0) : 0;
     };
+    // bit T % kStages: tile T lies in a padding block (bf16 cache; the fp8
+    // cache masks such rows through their scales)
+    uint32_t stage_pad = 0;
     // issue this wave's share of the loads of tile T: bf16 straight into ring
     // stage T % kStages; fp8 into staging slot T % 3 (expanded later)
     auto load_tile = [&](int T) {
       if constexpr (!kFp8) {
         int valid;
         const uint8_t* src = tile_src(T, &valid);
+        const uint32_t bit = 1u << (T % kStages);
+        stage_pad = valid == 0 ? (stage_pad | bit) : (stage_pad & ~bit);
         issue_tile(src, valid, lds + (int)(T % kStages) * kTileBytes, wave, lane);
       } else {
         const int tok0 = (int)(T - seq_start) * kTile;
         const int32_t blk = bt_row[tok0 / a.block_size];
-        const uint8_t* bp = blk < 0 ? a.pool : a.pool + (int64_t)blk * a.block_bytes;
-        issue_tile_fp8(bp, blk < 0 ? 0 : tok0 % a.block_size, a.block_size, tile_valid(T),
+        const bool ok = in_pool(blk);
+        const uint8_t* bp = ok ? a.pool + (int64_t)blk * a.block_bytes : a.pool;
+        issue_tile_fp8(bp, ok ? tok0 % a.block_size : 0, a.block_size, tile_valid(T),
                        lds + kOffF + (int)(T % kF8Slots) * kF8StageBytes, wave, lane);
       }
     };
@@ -300,14 +309,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       l_part = 0.f;
       int T_issue = p0 + pre;            // loads in flight cover [T, T_issue)
       pre = 0;                               // a second attempt loads every tile again
-      while (T_issue - p0 < kStages - 1 && T_issue < p1) load_tile(T_issue++);
       bool redo = false;                     // a reference jumped during this attempt (wave-uniform)
-      wait_tile(T_issue - 1 - p0);           // tile p0 has landed
-      lds_barrier();
-      if constexpr (kFp8) {
-        expand(p0);
-        lds_barrier();
-      }
 
       // ---- softmax of tile T against the reference max (exp2 domain); the
       // weights go to P buffer T % 2.  The scale is positive (checked by the
@@ -334,6 +336,10 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
+          if ((stage_pad >> (T % kStages)) & 1u) {   // a tile of a padding block (wave-uniform): all masked
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sv[i] = -INFINITY;
+          }
         }
         // causal / length mask: only a tile reaching past the first query row's
         // last visible token needs it (wave-uniform test)
@@ -424,6 +430,14 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
           for (int i = 0; i < 16; ++i) o15[i] += t15[i];
         }
       };
+
+      while (T_issue - p0 < kStages - 1 && T_issue < p1) load_tile(T_issue++);
+      wait_tile(T_issue - 1 - p0);           // tile p0 has landed
+      lds_barrier();
+      if constexpr (kFp8) {
+        expand(p0);
+        lds_barrier();
+      }
 
       // bf16: one barrier per tile, after the weights are written: it
       // publishes P(T) (buffer T % 2) and tile T+1 (each wave waits for its own
@@ -672,8 +686,9 @@ int64_t decode576_default_units(const mla_dims& d, int32_t q_per_seq, int cu_cou
 }
 
 mla_status launch_decode576(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
-                            const void* q_abs, const void* pool, const int32_t* block_table, int32_t max_blocks,
-                            const int32_t* seqlens, void* ws, void* o_lat, float* lse, hipStream_t st) {
+                            const void* q_abs, const void* pool, int64_t n_pool_blocks, const int32_t* block_table,
+                            int32_t max_blocks, const int32_t* seqlens, void* ws, void* o_lat, float* lse,
+                            hipStream_t st) {
   Args a;
   a.q_abs = static_cast<const uint16_t*>(q_abs);
   a.pool = static_cast<const uint8_t*>(pool);
@@ -682,6 +697,7 @@ mla_status launch_decode576(const mla_dims& d, const DecodePlan& plan, int32_t n
   a.ws_o = static_cast<uint16_t*>(ws);
   a.ws_stats = static_cast<float*>(ws) + plan.ws_stats_offset_floats;
   a.block_bytes = static_cast<int64_t>(mla_cache_block_bytes(&d));
+  a.n_pool_blocks = n_pool_blocks;
   a.max_blocks = max_blocks;
   a.block_size = d.block_size;
   a.n_seq = n_seq;

@@ -33,14 +33,21 @@ constexpr int kTile = kDecodeTile;                          // 32 tokens
 constexpr int kTileBytes = kTile * kRowBytes;               // 36864
 constexpr int kLoadsPerWave = kTileBytes / 1024 / 4;        // 9 wave-wide 16-byte loads per wave per tile
 
-// LDS tile layout: row r, 16-byte chunk c lives in 1 KB block
-// (r / 8) * 9 + c / 8 at byte (r % 8) * 128 + 16 * ((c % 8) ^ swz(r % 8)).
-// swz is a permutation of 0..7 (16-byte reads of 8 rows at one chunk hit 8
-// different bank groups) and, within each aligned group of 4 rows, swz >> 1 is
-// a permutation of 0..3 (transpose reads of 4 rows x 32 bytes do not collide).
+// LDS tile layout.  gfx950's LDS has 64 banks of 4 bytes and serves a 16-byte
+// read for 16 lanes per cycle, so a read is free of bank conflicts when each
+// group of 16 lanes touches 16 different 16-byte slots of a 256-byte line.
+// Row r, 16-byte chunk c lives in 1 KB block (r / 8) * 9 + c / 8, at row
+// position rpos(r) = (r % 8) ^ ((r / 8) % 2) (odd 8-row groups swap adjacent
+// rows) and slot (c % 8) ^ swz(r % 8) of that row's 128 bytes.
+//  * 16-byte reads of 16 consecutive rows at one chunk (the QK operand): rows
+//    r and r + 8 sit in opposite halves of the 256-byte line (rpos parity
+//    differs) and swz is a permutation, so all 16 slots differ.
+//  * transpose reads of 4 rows x 32 bytes per 16 lanes (the PV operand):
+//    within each aligned group of 4 rows, swz >> 1 is a permutation of 0..3.
 __device__ __forceinline__ int swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+__device__ __forceinline__ int rpos(int r) { return (r & 7) ^ ((r >> 3) & 1); }
 __device__ __forceinline__ uint32_t tile_off(int r, int c) {
-  return ((r >> 3) * 9 + (c >> 3)) * 1024 + (r & 7) * 128 + 16 * ((c & 7) ^ swz(r & 7));
+  return ((r >> 3) * 9 + (c >> 3)) * 1024 + rpos(r) * 128 + 16 * ((c & 7) ^ swz(r & 7));
 }
 
 __device__ __forceinline__ void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
@@ -63,9 +70,10 @@ __device__ __forceinline__ int xcd_unit(int i, int G) {
 }
 
 // Copy one tile (32 rows starting at `src`) into LDS stage `dst`.  Wave w
-// loads rows 8w..8w+7: nine 1 KB blocks, one per instruction; lane l brings
-// row 8w + l/8, logical chunk 8i + ((l % 8) ^ swz(l / 8)).  Rows at or beyond
-// `valid` re-read row 0 (finite data; their probabilities are 0).
+// loads rows 8w..8w+7: nine 1 KB blocks, one per instruction; lane l (row
+// position l/8 of its block) brings row 8w + ((l/8) ^ (w % 2)), logical chunk
+// 8i + ((l % 8) ^ swz(row % 8)).  Rows at or beyond `valid` re-read row 0
+// (finite data; their probabilities are 0).
 // The direct-to-LDS loads are written in assembly: the compiler's wait-count
 // bookkeeping treats a pending LDS DMA as a possible writer of every LDS read,
 // which makes it wait for all LDS reads at once instead of only the oldest.
@@ -77,7 +85,7 @@ __device__ __forceinline__ int xcd_unit(int i, int G) {
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"
 __device__ __forceinline__ void issue_tile(const uint8_t* src, int valid, lds_u8* dst, int wave, int lane) {
-  const int rho = lane >> 3;
+  const int rho = (lane >> 3) ^ (wave & 1);    // the row whose position is lane / 8
   const int row = 8 * wave + rho;
   const uint32_t lane_off = (row < valid ? row * kRowBytes : 0) + 16 * ((lane & 7) ^ swz(rho));
   // LDS base and source are wave-uniform: pin them to scalar registers
@@ -189,8 +197,8 @@ __device__ __forceinline__ void expand_tile_fp8(const lds_u8* stage, lds_u8* dst
   asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(lane));
   const int r = 8 * wave + (lane >> 3), m = lane & 7, sw = swz(r & 7);
   // logical chunk 16i + 2m + e of row r sits at tile_off(r, 16i + 2m + e) =
-  // base_e + 2048 i (block 2i + m/4 of the row group, position (2(m % 4) + e) ^ swz)
-  const uint32_t row_base = ((r >> 3) * 9 + (m >> 2)) * 1024 + (r & 7) * 128;
+  // base_e + 2048 i (block 2i + m/4 of the row group, slot (2(m % 4) + e) ^ swz)
+  const uint32_t row_base = ((r >> 3) * 9 + (m >> 2)) * 1024 + rpos(r) * 128;
   const uint32_t base0 = row_base + 16 * ((2 * (m & 3)) ^ sw);
   const uint32_t base1 = row_base + 16 * ((2 * (m & 3) + 1) ^ sw);
   const u32x4 kr = *(const lds_u32x4*)(stage + kF8OffRope + 1024 * wave + 16 * lane);

@@ -28,6 +28,7 @@ __global__ void __launch_bounds__(256) absorb_generic_kernel(
     for (int n = 0; n < d_nope; ++n) acc = fmaf(sh_q[n], Act<T>::ld(w, static_cast<int64_t>(n) * d_c + c), acc);
     Act<T>::st(q_abs, row * d_k + c, acc);
   }
+  if (d_rope == 0) return;                  // no RoPE part: q_rope and pos may be null
   const int p = pos[t];
   for (int i = threadIdx.x; i < d_rope / 2; i += blockDim.x) {
     float cs, sn, ox, oy;
@@ -59,8 +60,8 @@ __global__ void __launch_bounds__(256) append_generic_kernel(
 // ----------------------------------------------------------------------------
 template <typename T, bool kFp8>
 __global__ void __launch_bounds__(256) decode_generic_kernel(
-    const T* __restrict__ q_abs, const uint8_t* __restrict__ pool, const int32_t* __restrict__ block_table,
-    int max_blocks, const int32_t* __restrict__ seqlens, int q_per_seq, int H, int d_c, int d_rope,
+    const T* __restrict__ q_abs, const uint8_t* __restrict__ pool, int64_t n_pool_blocks,
+    const int32_t* __restrict__ block_table, int max_blocks, const int32_t* __restrict__ seqlens, int q_per_seq, int H, int d_c, int d_rope,
     int block_size, int64_t block_bytes, float scale, int n_splits, T* __restrict__ o_final,
     float* __restrict__ lse_final, float* __restrict__ ws_o, float* __restrict__ ws_stats) {
   extern __shared__ float sh[];             // q [d_c + d_rope] | p [256] | acc [d_c]
@@ -89,7 +90,7 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
   for (int tc = t0; tc < t1; tc += 256) {
     const int t = tc + threadIdx.x;
     float z = -INFINITY;
-    if (t < t1 && bt[t / block_size] >= 0) {
+    if (t < t1 && bt[t / block_size] >= 0 && bt[t / block_size] < n_pool_blocks) {
       const uint8_t* blk = pool + static_cast<int64_t>(bt[t / block_size]) * block_bytes;
       const int slot = t % block_size;
       float dot = 0.f;
@@ -138,7 +139,8 @@ __global__ void __launch_bounds__(256) decode_generic_kernel(
         float a = acc[r] * alpha;
         for (int u = 0; u < nt; ++u) {
           const int tt = tc + u;
-          if (bt[tt / block_size] < 0) continue;    // padding entry: weight 0, never read
+          // padding entry or one outside the pool: weight 0, never read
+          if (bt[tt / block_size] < 0 || bt[tt / block_size] >= n_pool_blocks) continue;
           const uint8_t* blk = pool + static_cast<int64_t>(bt[tt / block_size]) * block_bytes;
           const int slot = tt % block_size;
           float v;
@@ -290,9 +292,9 @@ mla_status launch_append_generic(const mla_dims& d, int32_t n_tok, const void* c
 }
 
 mla_status launch_decode_generic(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
-                                 const void* q_abs, const void* pool, const int32_t* block_table,
-                                 int32_t max_blocks, const int32_t* seqlens, void* ws, void* o_lat, float* lse,
-                                 hipStream_t st) {
+                                 const void* q_abs, const void* pool, int64_t n_pool_blocks,
+                                 const int32_t* block_table, int32_t max_blocks, const int32_t* seqlens, void* ws,
+                                 void* o_lat, float* lse, hipStream_t st) {
   const int64_t bb = static_cast<int64_t>(mla_cache_block_bytes(&d));
   dim3 grid(n_seq * q_per_seq * d.n_heads, plan.n_splits);
   const size_t shm = sizeof(float) * (d.d_c + d.d_rope + 256);
@@ -300,17 +302,17 @@ mla_status launch_decode_generic(const mla_dims& d, const DecodePlan& plan, int3
   float* ws_stats = ws_o ? ws_o + plan.ws_stats_offset_floats : nullptr;
   if (d.cache_dtype == MLA_F32)
     hipLaunchKernelGGL((decode_generic_kernel<float, false>), grid, dim3(256), shm, st, (const float*)q_abs,
-                       (const uint8_t*)pool, block_table, max_blocks, seqlens, q_per_seq, d.n_heads, d.d_c,
+                       (const uint8_t*)pool, n_pool_blocks, block_table, max_blocks, seqlens, q_per_seq, d.n_heads, d.d_c,
                        d.d_rope, d.block_size, bb, d.softmax_scale, plan.n_splits, (float*)o_lat, lse, ws_o,
                        ws_stats);
   else if (d.cache_dtype == MLA_BF16)
     hipLaunchKernelGGL((decode_generic_kernel<uint16_t, false>), grid, dim3(256), shm, st,
-                       (const uint16_t*)q_abs, (const uint8_t*)pool, block_table, max_blocks, seqlens, q_per_seq,
+                       (const uint16_t*)q_abs, (const uint8_t*)pool, n_pool_blocks, block_table, max_blocks, seqlens, q_per_seq,
                        d.n_heads, d.d_c, d.d_rope, d.block_size, bb, d.softmax_scale, plan.n_splits,
                        (uint16_t*)o_lat, lse, ws_o, ws_stats);
   else
     hipLaunchKernelGGL((decode_generic_kernel<uint16_t, true>), grid, dim3(256), shm, st,
-                       (const uint16_t*)q_abs, (const uint8_t*)pool, block_table, max_blocks, seqlens, q_per_seq,
+                       (const uint16_t*)q_abs, (const uint8_t*)pool, n_pool_blocks, block_table, max_blocks, seqlens, q_per_seq,
                        d.n_heads, d.d_c, d.d_rope, d.block_size, bb, d.softmax_scale, plan.n_splits,
                        (uint16_t*)o_lat, lse, ws_o, ws_stats);
   return launch_status();

@@ -66,9 +66,9 @@ mla_status launch_append_generic(const mla_dims& d, int32_t n_tok, const void* c
                                  int32_t n_seq, int32_t max_blocks, void* pool, int64_t n_pool_blocks,
                                  hipStream_t st);
 mla_status launch_decode_generic(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
-                                 const void* q_abs, const void* pool, const int32_t* block_table,
-                                 int32_t max_blocks, const int32_t* seqlens, void* ws, void* o_lat, float* lse,
-                                 hipStream_t st);
+                                 const void* q_abs, const void* pool, int64_t n_pool_blocks,
+                                 const int32_t* block_table, int32_t max_blocks, const int32_t* seqlens, void* ws,
+                                 void* o_lat, float* lse, hipStream_t st);
 mla_status launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
                           const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st);
 mla_status launch_combine_stream(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
@@ -82,7 +82,8 @@ mla_status launch_prefill(const mla_dims& d, int32_t n_seq, const int32_t* cu_se
                           void* out, float* lse, hipStream_t st);
 mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t* cu_q, int32_t total_q, int32_t max_q,
                                 const int32_t* cu_k, int32_t total_k, const void* q_nope, const void* q_rope,
-                                const void* cache_pool, const int32_t* block_table, int32_t max_blocks,
+                                const void* cache_pool, int64_t n_pool_blocks, const int32_t* block_table,
+                                int32_t max_blocks,
                                 const void* w_uk, const void* w_uv, const void* gate, void* ws, void* out, float* lse,
                                 hipStream_t st);
 size_t project_down_workspace_bytes(const mla_dims& d, int64_t n_tok, int64_t d_model, int64_t d_cq);

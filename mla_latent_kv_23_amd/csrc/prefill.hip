@@ -11,17 +11,30 @@
 // rotated.
 //
 // Launches:
+// Precision: the latent and the weights enter the decompression as the bf16
+// values they are; everything the attention contracts -- the query, k_C, the
+// rotated k_R, v and the softmax weights -- is an fp16 operand of the matrix
+// units (fp32 sums).  bf16 inputs convert to fp16 exactly (same exponent
+// range for these magnitudes, 3 more significand bits), and each rounding of
+// a computed operand (k_C, v, the weights, the rotated q_R) is 8 times finer
+// than a bf16 one would be.  Computed operands must stay inside fp16's range
+// (|x| < 65504).
 //  1. prefill_rope_kernel: cos/sin of every query's RoPE pairs [Tq][32] (fp64
 //     angle, fp32 cos/sin: the rule of the absorb and append kernels) and, for
-//     packed keys, k_R' [Tk, 64] in bf16 (fp64 rotation, one rounding).  The
+//     packed keys, k_R' [Tk, 64] (fp64 rotation, rounded to fp32 and then to
+//     bf16 as a bf16 cache stores it; kept as its exact fp16 value).  The
 //     query's RoPE part is rotated by the attention kernel as it loads the
-//     query (fp32 fused multiply-adds, then bf16, the MFMA operand).  For paged
-//     keys, prefill_gather_kernel packs each key's cache row (latent and
-//     rotated k_R) into the workspace.
-//  2. prefill_decompress_kernel: k_C [T, H, 128] and v [T, H, 128] in bf16, a
+//     query (the pair formed in fp64, rounded to fp32, then to the fp16
+//     operand).  For paged keys, prefill_gather_kernel packs each key's cache
+//     row (latent and rotated k_R, the latter as fp16) into the workspace; an
+//     fp8 latent is packed as its codes (exact in bf16) with the token's scale
+//     beside it.
+//  2. prefill_decompress_kernel: k_C [T, H, 128] and v [T, H, 128] in fp16, a
 //     bf16 MFMA GEMM with fp32 accumulation: each wave holds its 32 weight rows
 //     in registers, and the latent streams through LDS, 32 tokens at a time,
-//     shared by the K and V waves of a head.
+//     shared by the K and V waves of a head.  With an fp8 cache the fp32 sums
+//     over the codes are multiplied by the token's scale before the rounding
+//     (W (code * scale) = scale * (W code)).
 //  3. prefill_attn_kernel: causal flash attention per (sequence, head, block of
 //     128 queries), one wave per 32 queries:
 //     * key blocks of 64 rows [k_C | k_R | v] (640 B) are staged in LDS with
@@ -44,6 +57,24 @@ namespace mla {
 namespace {
 
 constexpr int kPfDc = 512, kPfDn = 128, kPfDr = 64, kPfDv = 128;
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) f16x8 lds_f16x8;
+typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+
+// fp16 bits of a float (round to nearest even)
+__device__ __forceinline__ uint32_t f16_bits(float x) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x); }
+// eight bf16 values (16 bytes) as eight fp16 values: exact for every bf16 inside fp16's normal range
+__device__ __forceinline__ u32x4 bf16x8_to_f16x8(u32x4 v) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    r[i] = f16_bits(__uint_as_float(v[i] << 16)) | (f16_bits(__uint_as_float(v[i] & 0xffff0000u)) << 16);
+  return r;
+}
 
 // ---------------------------------------------------------------- 1. RoPE
 
@@ -83,33 +114,28 @@ __global__ void __launch_bounds__(256) prefill_rope_kernel(const uint16_t* __res
     const uint32_t x2 = *(const uint32_t*)(k_rope + at);
     float ox, oy;
     rope_pair(bf16_bits_to_f32((uint16_t)(x2 & 0xffffu)), bf16_bits_to_f32((uint16_t)(x2 >> 16)), c, sn, &ox, &oy);
-    *(uint32_t*)(kr_out + at) = (uint32_t)f32_to_bf16_bits(ox) | ((uint32_t)f32_to_bf16_bits(oy) << 16);
+    // rounded to bf16 as a bf16 cache stores it, then held as that value in fp16 (exact)
+    *(uint32_t*)(kr_out + at) = f16_bits(bf16_bits_to_f32(f32_to_bf16_bits(ox))) |
+                                (f16_bits(bf16_bits_to_f32(f32_to_bf16_bits(oy))) << 16);
   }
-}
-
-// bf16(code * scale) rounded once (to nearest even) from the exact product: the
-// product of a 4-bit and a 24-bit significand is exact in fp64; it is
-// narrowed to fp32 rounding to odd (toward zero, then the last bit set when
-// inexact), which keeps the final rounding to bf16 a single correct one.
-__device__ __forceinline__ uint16_t pf_scaled_bf16(float code, float scale) {
-  const double x = (double)code * (double)scale;
-  float f = __double2float_rz(x);
-  if ((double)f != x) f = __uint_as_float(__float_as_uint(f) | 1u);
-  return f32_to_bf16_bits(f);
 }
 
 // Paged keys: one thread per (key token, 16-byte piece of its cache row):
 // the row of key t (block_table[b][p / block_size] * block_size + p %
 // block_size, p its position) is copied into the packed latent [t][d_c] and
 // the packed rotated key [t][d_R] (the cache holds k_R already rotated).
-// fp8 cache: the latent is dequantised, code * scale rounded once to bf16
-// (the E4M3FN code converts to bf16 exactly); 16 codes per thread.
+// fp8 cache: the latent goes in as its E4M3FN codes, each exactly a bf16
+// (16 codes per thread), and the token's scale to sc_out[t]; the
+// decompression applies the scale to its fp32 sums.  A block-table entry
+// outside [0, n_pool_blocks) is never read: its tokens get a zero latent and
+// key (and scale 0).
 template <bool kFp8>
 __global__ void __launch_bounds__(256) prefill_gather_kernel(const uint8_t* __restrict__ pool, int64_t block_bytes,
+                                                             int64_t n_pool_blocks,
                                                              const int32_t* __restrict__ block_table, int max_blocks,
                                                              int block_size, const int32_t* __restrict__ cu_k,
                                                              int n_seq, int total_k, uint16_t* __restrict__ c_out,
-                                                             uint16_t* __restrict__ kr_out) {
+                                                             uint16_t* __restrict__ kr_out, float* __restrict__ sc_out) {
   constexpr int kCPieces = kFp8 ? kPfDc / 16 : kPfDc / 8;   // latent pieces (16 codes or 8 bf16 each)
   constexpr int kPieces = kCPieces + kPfDr / 8;
   const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -119,11 +145,12 @@ __global__ void __launch_bounds__(256) prefill_gather_kernel(const uint8_t* __re
   const int p = t - cu_k[b];
   const int64_t blk = block_table[(int64_t)b * max_blocks + p / block_size];
   const int slot = p % block_size;
-  if (blk < 0) {   // a padding entry inside the length (a caller error): zeros, nothing is read
+  if (blk < 0 || blk >= n_pool_blocks) {   // padding inside the length (a caller error): zeros, nothing is read
     if (piece < kCPieces) {
       u32x4* dst = (u32x4*)(c_out + (int64_t)t * kPfDc + (kFp8 ? 16 : 8) * piece);
       dst[0] = u32x4{0, 0, 0, 0};
       if (kFp8) dst[1] = u32x4{0, 0, 0, 0};
+      if (kFp8 && piece == 0) sc_out[t] = 0.f;
     } else {
       *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * (piece - kCPieces)) = u32x4{0, 0, 0, 0};
     }
@@ -133,27 +160,27 @@ __global__ void __launch_bounds__(256) prefill_gather_kernel(const uint8_t* __re
   if constexpr (!kFp8) {
     const u32x4 v = *(const u32x4*)(base + ((int64_t)slot * (kPfDc + kPfDr) + 8 * piece) * 2);
     if (piece < kCPieces) *(u32x4*)(c_out + (int64_t)t * kPfDc + 8 * piece) = v;
-    else *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * (piece - kCPieces)) = v;
+    else *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * (piece - kCPieces)) = bf16x8_to_f16x8(v);
   } else {
     if (piece < kCPieces) {
       const u32x4 codes = *(const u32x4*)(base + (int64_t)slot * kPfDc + 16 * piece);
-      const float scale = *(const float*)(base + (int64_t)block_size * kPfDc + 4 * slot);
+      if (piece == 0) sc_out[t] = *(const float*)(base + (int64_t)block_size * kPfDc + 4 * slot);
       uint32_t outw[8];
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
+        // scale 1: every E4M3FN code is exactly a bf16
         const bf16x2 lo = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], 1.0f, false);   // codes 4w, 4w+1
         const bf16x2 hi = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes[w], 1.0f, true);    // codes 4w+2, 4w+3
-        outw[2 * w] = (uint32_t)pf_scaled_bf16((float)lo[0], scale) | ((uint32_t)pf_scaled_bf16((float)lo[1], scale) << 16);
-        outw[2 * w + 1] =
-            (uint32_t)pf_scaled_bf16((float)hi[0], scale) | ((uint32_t)pf_scaled_bf16((float)hi[1], scale) << 16);
+        outw[2 * w] = *(const uint32_t*)&lo;
+        outw[2 * w + 1] = *(const uint32_t*)&hi;
       }
       u32x4* dst = (u32x4*)(c_out + (int64_t)t * kPfDc + 16 * piece);
       dst[0] = u32x4{outw[0], outw[1], outw[2], outw[3]};
       dst[1] = u32x4{outw[4], outw[5], outw[6], outw[7]};
     } else {
       const int q = piece - kCPieces;
-      *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * q) =
-          *(const u32x4*)(base + (int64_t)block_size * (kPfDc + 4) + ((int64_t)slot * kPfDr + 8 * q) * 2);
+      *(u32x4*)(kr_out + (int64_t)t * kPfDr + 8 * q) = bf16x8_to_f16x8(
+          *(const u32x4*)(base + (int64_t)block_size * (kPfDc + 4) + ((int64_t)slot * kPfDr + 8 * q) * 2));
     }
   }
 }
@@ -188,6 +215,12 @@ __device__ __forceinline__ u32x2 pf_pack4(float a, float b, float c, float d) {
   r[1] = (uint32_t)f32_to_bf16_bits(c) | ((uint32_t)f32_to_bf16_bits(d) << 16);
   return r;
 }
+__device__ __forceinline__ u32x2 pf_pack4_f16(float a, float b, float c, float d) {
+  u32x2 r;
+  r[0] = f16_bits(a) | (f16_bits(b) << 16);
+  r[1] = f16_bits(c) | (f16_bits(d) << 16);
+  return r;
+}
 
 // grid H * G, block 512 (8 waves).  Work-group (head s, token group g) writes
 // k_C = W_UK[s] c (waves 0-3, dims 32 w ..) and v = W_UV[s] c (waves 4-7) for
@@ -195,11 +228,12 @@ __device__ __forceinline__ u32x2 pf_pack4(float a, float b, float c, float d) {
 // 512-long contraction, 128 VGPRs) in registers for the life of the
 // work-group, so only the latent streams: 32 tokens x 1 KB per stage through a
 // four-stage LDS ring filled by direct-to-LDS loads (one 1 KB row per
-// instruction, 16-byte chunk p of row r holding logical chunk p ^ (r % 8), so
-// that eight rows read at one chunk hit distinct banks), three stages in
-// flight.  The K and V halves share every latent tile; the work-groups of
+// instruction, 16-byte chunk p of row r holding logical chunk p ^ (r % 16), so
+// that the 16 rows one 16-lane group reads at one chunk hit 16 different
+// 16-byte slots of the LDS's 64 banks), three stages in flight.  The K and V halves share every latent tile; the work-groups of
 // one token group run on one XCD and share the tiles in its L2.
 __global__ void __launch_bounds__(512, 1) prefill_decompress_kernel(const uint16_t* __restrict__ c_kv,
+                                                                    const float* __restrict__ tok_scale,
                                                                     const uint16_t* __restrict__ w_uk,
                                                                     const uint16_t* __restrict__ w_uv,
                                                                     uint16_t* __restrict__ kc, uint16_t* __restrict__ vv,
@@ -232,7 +266,7 @@ __global__ void __launch_bounds__(512, 1) prefill_decompress_kernel(const uint16
     for (int rr = 0; rr < 4; ++rr) {
       const int r = 4 * wave + rr;
       const int t = min((j0 + j) * kDcTok + r, T - 1);   // past the end: the last token (finite, not stored)
-      dma16(c_kv + (int64_t)t * kPfDc, (uint32_t)(16 * (lane ^ (r & 7))), stage + (uint32_t)(r * 1024));
+      dma16(c_kv + (int64_t)t * kPfDc, (uint32_t)(16 * (lane ^ (r & 15))), stage + (uint32_t)(r * 1024));
     }
   };
   // operations this wave queued after tile j's loads, when it waits for them: the
@@ -261,12 +295,12 @@ __global__ void __launch_bounds__(512, 1) prefill_decompress_kernel(const uint16
     bf16x8 bf[kDcAhead];
 #pragma unroll
     for (int ks = 0; ks < kDcAhead; ++ks)
-      bf[ks] = *(const lds_bf16x8*)(uintptr_t)(brow + 16 * ((2 * ks + half) ^ (lr & 7)));
+      bf[ks] = *(const lds_bf16x8*)(uintptr_t)(brow + 16 * ((2 * ks + half) ^ (lr & 15)));
 #pragma unroll
     for (int ks = 0; ks < kDcKs; ++ks) {
       const bf16x8 cur = bf[ks % kDcAhead];
       if (ks + kDcAhead < kDcKs)
-        bf[ks % kDcAhead] = *(const lds_bf16x8*)(uintptr_t)(brow + 16 * ((2 * (ks + kDcAhead) + half) ^ (lr & 7)));
+        bf[ks % kDcAhead] = *(const lds_bf16x8*)(uintptr_t)(brow + 16 * ((2 * (ks + kDcAhead) + half) ^ (lr & 15)));
       acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[ks], cur, acc, 0, 0, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x100, kDcAhead, 0);
@@ -281,10 +315,15 @@ __global__ void __launch_bounds__(512, 1) prefill_decompress_kernel(const uint16
     // T are skipped by the lane's predicate, the instructions still issue)
     const int t = (j0 + j) * kDcTok + lr;
     if (t < T) {
+      if (tok_scale) {                       // fp8 latent: the sums were over the codes
+        const float sc = tok_scale[t];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] *= sc;
+      }
       uint16_t* dst = out + (int64_t)t * H * kPfDv;
 #pragma unroll
       for (int gg = 0; gg < 4; ++gg)
-        *(u32x2*)(dst + 8 * gg) = pf_pack4(acc[4 * gg], acc[4 * gg + 1], acc[4 * gg + 2], acc[4 * gg + 3]);
+        *(u32x2*)(dst + 8 * gg) = pf_pack4_f16(acc[4 * gg], acc[4 * gg + 1], acc[4 * gg + 2], acc[4 * gg + 3]);
     }
   }
 }
@@ -298,18 +337,20 @@ constexpr int kStage = kKBlk / 8 * kRowBlocks * 1024;   // 40960
 constexpr int kQk = (kPfDn + kPfDr) / 16;    // 12 QK k-steps
 constexpr int kKf = 8;                       // K fragments in flight ahead of the MFMA chain
 
-// staged row r, 16-byte chunk c (c < 16: k_C, 16..23: k_R, 24..39: v)
+// staged row r, 16-byte chunk c (c < 16: k_C, 16..23: k_R, 24..39: v); the
+// row position and slot swizzle of the decode tile (rpos, swz), so 16 lanes
+// reading 16 rows at one chunk hit 16 different slots
 __device__ __forceinline__ uint32_t stage_off(int r, int c) {
-  return ((r >> 3) * kRowBlocks + (c >> 3)) * 1024 + (r & 7) * 128 + 16 * ((c & 7) ^ swz(r & 7));
+  return ((r >> 3) * kRowBlocks + (c >> 3)) * 1024 + rpos(r) * 128 + 16 * ((c & 7) ^ swz(r & 7));
 }
 
 struct PrefillArgs {
   const uint16_t* q_nope;     // [T][H][128]
   const uint16_t* q_rope;     // [Tq][H][64] unrotated
   const float* cs;            // [Tq][32] (cos, sin) of each query's RoPE pairs
-  const uint16_t* k_c;        // [T][H][128]
-  const uint16_t* k_rot;      // [T][64] rotated
-  const uint16_t* v;          // [T][H][128]
+  const uint16_t* k_c;        // [T][H][128] fp16
+  const uint16_t* k_rot;      // [T][64] rotated, fp16
+  const uint16_t* v;          // [T][H][128] fp16
   const int32_t* cu_q;        // [n_seq + 1] query offsets
   const int32_t* cu_k;        // [n_seq + 1] key offsets
   const uint16_t* gate;       // [Tq][H][128] output-gate logits, or null
@@ -343,25 +384,31 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
   const int q = min(qw + lr, Lq - 1);                  // this lane's query (past the end: a copy of the last)
 
   // queries: B operand, query q, dims 16k + 8 half .. +7 (k < 8: q_nope, else the rotated part)
-  bf16x8 qf[kQk];
+  f16x8 qf[kQk];
   {
     const bf16x8* qn = (const bf16x8*)(a.q_nope + ((int64_t)(cu0 + q) * H + s) * kPfDn) + half;
     // the RoPE part, rotated here: k-step kk holds pairs 8 (kk - 8) + 4 half .. +3
     const bf16x8* qr = (const bf16x8*)(a.q_rope + ((int64_t)(cu0 + q) * H + s) * kPfDr) + half;
     const f32x4* csq = (const f32x4*)(a.cs + (int64_t)(cu0 + q) * kPfDr) + 2 * half;   // 2 pairs per f32x4
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) qf[kk] = qn[2 * kk];
+    for (int kk = 0; kk < 8; ++kk) {
+      const bf16x8 raw = qn[2 * kk];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) qf[kk][e] = (_Float16)(float)raw[e];   // exact
+    }
 #pragma unroll
     for (int kk = 8; kk < kQk; ++kk) {
       const bf16x8 raw = qr[2 * (kk - 8)];
       const f32x4 c01 = csq[4 * (kk - 8)], c23 = csq[4 * (kk - 8) + 1];
       const float cv[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
-      bf16x8 rot;
+      f16x8 rot;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const float x = (float)raw[2 * e], y = (float)raw[2 * e + 1], c = cv[2 * e], sn = cv[2 * e + 1];
-        rot[2 * e] = (__bf16)fmaf(x, c, -(y * sn));
-        rot[2 * e + 1] = (__bf16)fmaf(x, sn, y * c);
+        // the RoPE rule of the absorb: the pair formed in fp64, rounded to fp32, then to the fp16 operand
+        float ox, oy;
+        rope_pair((float)raw[2 * e], (float)raw[2 * e + 1], cv[2 * e], cv[2 * e + 1], &ox, &oy);
+        rot[2 * e] = (_Float16)ox;
+        rot[2 * e + 1] = (_Float16)oy;
       }
       qf[kk] = rot;
     }
@@ -390,7 +437,8 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
   }
 
   // stage loads: wave w brings rows 16w .. 16w+15 of the block, five 1 KB
-  // blocks per 8 rows; lane l: row 16w + 8g + l/8, logical chunk 8cb + ((l % 8) ^ swz(l / 8))
+  // blocks per 8 rows; lane l (row position l/8): row 16w + 8g + ((l/8) ^ g),
+  // logical chunk 8cb + ((l % 8) ^ swz(row % 8))
   const int last_key = min(L, off + q0 + kQBlk) - 1;
   const int n_kblk = last_key / kKBlk + 1;
   auto load_stage = [&](int kbk, int par) {   // par = kbk % 2 (a constant where the caller knows it)
@@ -399,9 +447,10 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
     const int64_t row0 = ck0 + key0;
 #pragma unroll
     for (int g = 0; g < 2; ++g) {
-      const int r = 16 * wave + 8 * g + (lane >> 3);
+      const int rho = (lane >> 3) ^ g;           // the row (of 8) at position lane / 8 (rpos of row 8(2w + g) + rho)
+      const int r = 16 * wave + 8 * g + rho;
       const int re = key0 + r < L ? r : 0;       // past the end: the block's first key (finite, masked)
-      const int sl = (lane & 7) ^ swz(lane >> 3);
+      const int sl = (lane & 7) ^ swz(rho);
       const uint32_t m0 = dst + (uint32_t)(((2 * wave + g) * kRowBlocks) * 1024);
       // k_C chunks 0..15 and v chunks 24..39 (per-head rows of 256 B), k_R chunks 16..23 (128 B rows)
       const uint32_t hoff = (uint32_t)((re * H + s) * (kPfDn * 2)) + 16 * sl;
@@ -431,15 +480,15 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
     f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
     for (int t = 0; t < 2; ++t) {
-      bf16x8 kf[kKf];
+      f16x8 kf[kKf];
 #pragma unroll
-      for (int kk = 0; kk < kKf; ++kk) kf[kk] = *(const lds_bf16x8*)(uintptr_t)(tb + kb[kk % 4] + 1024 * (kk / 4) + 20480 * t);
+      for (int kk = 0; kk < kKf; ++kk) kf[kk] = *(const lds_f16x8*)(uintptr_t)(tb + kb[kk % 4] + 1024 * (kk / 4) + 20480 * t);
 #pragma unroll
       for (int kk = 0; kk < kQk; ++kk) {
-        const bf16x8 cur = kf[kk % kKf];
+        const f16x8 cur = kf[kk % kKf];
         if (kk + kKf < kQk)
-          kf[kk % kKf] = *(const lds_bf16x8*)(uintptr_t)(tb + kb[kk % 4] + 1024 * ((kk + kKf) / 4) + 20480 * t);
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(cur, qf[kk], sacc[t], 0, 0, 0);
+          kf[kk % kKf] = *(const lds_f16x8*)(uintptr_t)(tb + kb[kk % 4] + 1024 * ((kk + kKf) / 4) + 20480 * t);
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur, qf[kk], sacc[t], 0, 0, 0);
       }
     }
     // issue order per half: kKf K reads, then (MFMA, read) pairs, then the last kKf MFMAs, so that kKf
@@ -491,20 +540,20 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
       m_ref = m_new;
     }
     const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
-    bf16x8 pb[4];                            // B operand of PV k-step 2t + j: regs 8j .. 8j+7 of half t
-    const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
+    f16x8 pb[4];                             // B operand of PV k-step 2t + j: regs 8j .. 8j+7 of half t
+    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
     float psum = 0.f;
 #pragma unroll
     for (int t = 0; t < 2; ++t)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        bf16x8 v8;
+        f16x8 v8;
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const f32x2 pv = {__builtin_amdgcn_exp2f(fmaf(sv[t][8 * j + e], sl2, neg_m)),
                             __builtin_amdgcn_exp2f(fmaf(sv[t][8 * j + e + 1], sl2, neg_m))};
-          const bf16x2 p2 = __builtin_convertvector(pv, bf16x2);
-          psum = __builtin_amdgcn_fdot2_f32_bf16(p2, ones, psum, false);
+          const f16x2 p2 = __builtin_convertvector(pv, f16x2);   // round to nearest even; weights <= 2^8
+          psum = __builtin_amdgcn_fdot2(p2, ones, psum, false);   // sum of the rounded weights
           v8[e] = p2[0];
           v8[e + 1] = p2[1];
         }
@@ -518,10 +567,12 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) {
         const uint32_t base = tb + 10240 * ks + 1024 * (db >> 1);
-        const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(base + vb[(db & 1) * 2]));
-        const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(uintptr_t)(base + vb[(db & 1) * 2 + 1]));
-        const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb[ks], o[db], 0, 0, 0);
+        const f16x4 lo = __builtin_bit_cast(
+            f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + vb[(db & 1) * 2])));
+        const f16x4 hi = __builtin_bit_cast(
+            f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + vb[(db & 1) * 2 + 1])));
+        const f16x8 vf = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pb[ks], o[db], 0, 0, 0);
       }
   };
   load_stage(0, 0);
@@ -573,16 +624,18 @@ bool prefill_supported(const mla_dims& d) {
 namespace {
 size_t up256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-// workspace: k_C, v [Tk][H][128] (bf16), the queries' (cos, sin) [Tq][32] (float2), k_R' [Tk][64] (bf16), then,
-// for paged keys, the packed latent rows [Tk][d_c] (bf16); 256-byte aligned pieces
+// workspace: k_C, v [Tk][H][128] (fp16), the queries' (cos, sin) [Tq][32] (float2), k_R' [Tk][64] (fp16), then,
+// for paged keys, the packed latent rows [Tk][d_c] (bf16) and the tokens' fp8 scales [Tk] (fp32); 256-byte
+// aligned pieces
 struct PrefillWs {
   uint16_t *kc, *vv, *kr;
   float* cs;
   uint16_t* ckv;   // paged keys: the packed latent rows
+  float* sc;       // paged keys: the per-token scales of an fp8 latent
 };
 size_t prefill_ws_bytes(int64_t tq, int64_t tk, int64_t H, bool paged) {
   return up256(tk * H * kPfDn * 2) + up256(tk * H * kPfDv * 2) + up256(tq * kPfDr * 4) + up256(tk * kPfDr * 2) +
-         (paged ? up256(tk * kPfDc * 2) : 0);
+         (paged ? up256(tk * kPfDc * 2) + up256(tk * 4) : 0);
 }
 PrefillWs carve(void* ws, int64_t tq, int64_t tk, int64_t H) {
   uint8_t* p = static_cast<uint8_t*>(ws);
@@ -596,14 +649,16 @@ PrefillWs carve(void* ws, int64_t tq, int64_t tk, int64_t H) {
   w.kr = reinterpret_cast<uint16_t*>(p);
   p += up256(tk * kPfDr * 2);
   w.ckv = reinterpret_cast<uint16_t*>(p);
+  p += up256(tk * kPfDc * 2);
+  w.sc = reinterpret_cast<float*>(p);   // (carved past the end for packed keys, never used there)
   return w;
 }
 
-void launch_decompress(const mla_dims& d, const uint16_t* c_kv, const void* w_uk, const void* w_uv, const PrefillWs& w,
-                       int32_t total_k, hipStream_t st) {
+void launch_decompress(const mla_dims& d, const uint16_t* c_kv, const float* tok_scale, const void* w_uk,
+                       const void* w_uv, const PrefillWs& w, int32_t total_k, hipStream_t st) {
   // token groups: about one work-group per CU (256) over the heads
   const int G = std::max(1, std::min(256 / std::max(d.n_heads, 1), (total_k + kDcTok - 1) / kDcTok));
-  hipLaunchKernelGGL(prefill_decompress_kernel, dim3(d.n_heads * G), dim3(512), 0, st, c_kv,
+  hipLaunchKernelGGL(prefill_decompress_kernel, dim3(d.n_heads * G), dim3(512), 0, st, c_kv, tok_scale,
                      static_cast<const uint16_t*>(w_uk), static_cast<const uint16_t*>(w_uv), w.kc, w.vv, total_k,
                      d.n_heads, G);
 }
@@ -649,14 +704,15 @@ mla_status launch_prefill(const mla_dims& d, int32_t n_seq, const int32_t* cu_se
   hipLaunchKernelGGL(prefill_rope_kernel, dim3((unsigned)(((int64_t)total_tokens * (kPfDr / 2) + 255) / 256)), dim3(256),
                      0, st, static_cast<const uint16_t*>(k_rope), cu_seqlens, cu_seqlens, n_seq, total_tokens, w.cs,
                      w.kr, f);
-  launch_decompress(d, static_cast<const uint16_t*>(c_kv), w_uk, w_uv, w, total_tokens, st);
+  launch_decompress(d, static_cast<const uint16_t*>(c_kv), nullptr, w_uk, w_uv, w, total_tokens, st);
   launch_attention(d, n_seq, cu_seqlens, cu_seqlens, max_seqlen, q_nope, q_rope, w, gate, out, lse, st);
   return launch_status();
 }
 
 mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t* cu_q, int32_t total_q, int32_t max_q,
                                 const int32_t* cu_k, int32_t total_k, const void* q_nope, const void* q_rope,
-                                const void* cache_pool, const int32_t* block_table, int32_t max_blocks,
+                                const void* cache_pool, int64_t n_pool_blocks, const int32_t* block_table,
+                                int32_t max_blocks,
                                 const void* w_uk, const void* w_uv, const void* gate, void* ws, void* out, float* lse,
                                 hipStream_t st) {
   const PrefillWs w = carve(ws, total_q, total_k, d.n_heads);
@@ -665,13 +721,16 @@ mla_status launch_prefill_paged(const mla_dims& d, int32_t n_seq, const int32_t*
                      st, nullptr, cu_q, cu_k, n_seq, total_q, w.cs, nullptr, f);
   const int64_t bb = (int64_t)mla_cache_block_bytes(&d);
   const uint8_t* pool8 = static_cast<const uint8_t*>(cache_pool);
-  if (d.cache_dtype == MLA_FP8_E4M3)
+  const bool f8 = d.cache_dtype == MLA_FP8_E4M3;
+  if (f8)
     hipLaunchKernelGGL(prefill_gather_kernel<true>, dim3((unsigned)(((int64_t)total_k * 40 + 255) / 256)), dim3(256), 0,
-                       st, pool8, bb, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k, w.ckv, w.kr);
+                       st, pool8, bb, n_pool_blocks, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k,
+                       w.ckv, w.kr, w.sc);
   else
     hipLaunchKernelGGL(prefill_gather_kernel<false>, dim3((unsigned)(((int64_t)total_k * 72 + 255) / 256)), dim3(256), 0,
-                       st, pool8, bb, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k, w.ckv, w.kr);
-  launch_decompress(d, w.ckv, w_uk, w_uv, w, total_k, st);
+                       st, pool8, bb, n_pool_blocks, block_table, max_blocks, d.block_size, cu_k, n_seq, total_k,
+                       w.ckv, w.kr, w.sc);
+  launch_decompress(d, w.ckv, f8 ? w.sc : nullptr, w_uk, w_uv, w, total_k, st);
   launch_attention(d, n_seq, cu_q, cu_k, max_q, q_nope, q_rope, w, gate, out, lse, st);
   return launch_status();
 }

@@ -85,22 +85,25 @@ __device__ __forceinline__ void absorb_body(const AbsorbArgs& aa, int s, int cbl
   // cos/sin run while the slab loads are in flight (loads complete in order).
   const int pairs = d_rope / 2;
   const int n_rope = ((n_tok - cblk + ny - 1) / ny) * pairs;
-  auto rope_item = [&](int i, int* t, int* p) {
+  auto rope_item = [&](int i, int* t, int* p) {   // only called with pairs > 0
     *t = cblk + ny * (i / pairs);
     *p = i % pairs;
   };
-  // (indices clamped so the loads need no branch; unused ones are dropped below)
-  int32_t r_pos[2];
-  uint32_t r_q[2];
-  double r_f[2];
+  // (indices clamped so the loads need no branch; unused ones are dropped below).
+  // Without a RoPE part (d_rope = 0) q_rope and pos may be null and nothing is read.
+  int32_t r_pos[2] = {0, 0};
+  uint32_t r_q[2] = {0u, 0u};
+  double r_f[2] = {0.0, 0.0};
+  if (pairs > 0) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    int t, p;
-    rope_item(min(tid + 256 * j, max(n_rope - 1, 0)), &t, &p);
-    t = min(t, n_tok - 1);
-    r_pos[j] = pos[t];
-    r_q[j] = *(const uint32_t*)(q_rope + ((int64_t)t * H + s) * d_rope + 2 * p);
-    r_f[j] = freqs.inv_freq[p];
+    for (int j = 0; j < 2; ++j) {
+      int t, p;
+      rope_item(min(tid + 256 * j, max(n_rope - 1, 0)), &t, &p);
+      t = min(t, n_tok - 1);
+      r_pos[j] = pos[t];
+      r_q[j] = *(const uint32_t*)(q_rope + ((int64_t)t * H + s) * d_rope + 2 * p);
+      r_f[j] = freqs.inv_freq[p];
+    }
   }
   // slab loads (W_UK[s][:, cblk*128 .. +127]) and the first block's queries, all in flight together
   const uint16_t* wsrc = w_uk + (int64_t)s * kNope * d_c + cblk * kAbsorbCols;
@@ -130,15 +133,17 @@ __device__ __forceinline__ void absorb_body(const AbsorbArgs& aa, int s, int cbl
     return (uint32_t*)(q_abs + ((int64_t)t * H + s) * d_k + d_c + 2 * p);
   };
   // computed for every lane (clamped items included) so the preloads stay ahead of the slab
+  if (pairs > 0) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const uint32_t v = rotate(r_pos[j], r_q[j], r_f[j]);
-    if (tid + 256 * j < n_rope) *rope_dst(tid + 256 * j) = v;
-  }
-  for (int i = tid + 512; i < n_rope; i += 256) {   // more than 512 rotations: rest loaded here
-    int t, p;
-    rope_item(i, &t, &p);
-    *rope_dst(i) = rotate(pos[t], *(const uint32_t*)(q_rope + ((int64_t)t * H + s) * d_rope + 2 * p), freqs.inv_freq[p]);
+    for (int j = 0; j < 2; ++j) {
+      const uint32_t v = rotate(r_pos[j], r_q[j], r_f[j]);
+      if (tid + 256 * j < n_rope) *rope_dst(tid + 256 * j) = v;
+    }
+    for (int i = tid + 512; i < n_rope; i += 256) {   // more than 512 rotations: rest loaded here
+      int t, p;
+      rope_item(i, &t, &p);
+      *rope_dst(i) = rotate(pos[t], *(const uint32_t*)(q_rope + ((int64_t)t * H + s) * d_rope + 2 * p), freqs.inv_freq[p]);
+    }
   }
   // the first block's queries are consumed here, together with the slab, so
   // that both sets of loads share one memory latency

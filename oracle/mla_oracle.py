@@ -208,7 +208,7 @@ def _softmax_rows(z: np.ndarray):
 
 
 def decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scale, base,
-                    heads: Optional[Sequence[int]] = None, operand_dtype: Optional[str] = None):
+                    heads: Optional[Sequence[int]] = None):
     """One sequence, non-absorbed (MHA) form.
 
     q_nope [s_q, H, d_nope], q_rope [s_q, H, d_R] (unrotated), q_pos [s_q];
@@ -218,11 +218,8 @@ def decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scal
     explicitly, key = [k_C | k_R], query = [q_nope | RoPE(q_R)], and standard
     causal softmax attention runs over tokens t <= position of the query.
     Returns o [s_q, h, d_v], o_lat [s_q, h, d_c], lse [s_q, h] over the chosen heads.
-    operand_dtype (e.g. "bf16"): round the latent, the rotated query part and
-    the decompressed k_C and v to that storage type before they are used, the
-    points where a kernel that runs this form on bf16 matrix units rounds them
-    (the latent of a bf16 cache is already on that grid; an fp8 one,
-    code * scale, is rounded once).
+    Nothing is rounded: the rotated query part, the decompressed k_C and v and
+    the softmax are exact float64 values.
     """
     q_nope = np.asarray(q_nope, dtype=F64)
     q_pos = np.asarray(q_pos, dtype=np.int64)
@@ -231,9 +228,6 @@ def decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scal
     heads = list(range(H)) if heads is None else list(heads)
     qr = rope(q_rope, q_pos[:, None], base)                              # [s_q, H, d_R]
     c_cached = np.asarray(c_cached, dtype=F64)
-    if operand_dtype is not None:
-        qr = store_value(qr, operand_dtype)
-        c_cached = store_value(c_cached, operand_dtype)
     visible = np.arange(L)[None, :] <= q_pos[:, None]                   # [s_q, L]
     o = np.zeros((s_q, len(heads), w_uv.shape[1]))
     o_lat = np.zeros((s_q, len(heads), c_cached.shape[1]))
@@ -241,8 +235,6 @@ def decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scal
     for hi, s in enumerate(heads):
         k_c = c_cached @ np.asarray(w_uk[s], dtype=F64).T                 # [L, d_nope]
         v = c_cached @ np.asarray(w_uv[s], dtype=F64).T                   # [L, d_v]
-        if operand_dtype is not None:
-            k_c, v = store_value(k_c, operand_dtype), store_value(v, operand_dtype)
         key = np.concatenate([k_c, kr_cached], axis=1)                    # [L, d_nope + d_R]
         query = np.concatenate([q_nope[:, s, :], qr[:, s, :]], axis=1)    # [s_q, d_nope + d_R]
         z = scale * (query @ key.T)                                       # [s_q, L]
@@ -255,7 +247,7 @@ def decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scal
 
 
 def prefill_mha_form(q_nope, q_rope, c_kv, k_rope_raw, w_uk, w_uv, scale, base,
-                     heads: Optional[Sequence[int]] = None, operand_dtype: Optional[str] = None):
+                     heads: Optional[Sequence[int]] = None):
     """Prefill of one sequence in the MHA form ([P1] 双重投影, training/prefill
     column: every head attends with k = [c W_UK^T | k_R], v = c W_UV^T).
 
@@ -264,19 +256,18 @@ def prefill_mha_form(q_nope, q_rope, c_kv, k_rope_raw, w_uk, w_uv, scale, base,
     [T, H, d_R] and k_rope_raw [T, d_R] are unrotated; c_kv [T, d_c] is the
     latent as produced (no cache rounding).  The rotated shared key enters the
     attention rounded to bf16, as it is stored in a bf16 cache (R4).
-    operand_dtype: as for decode_mha_form.
     Returns o [T, h, d_v] and lse [T, h] over the chosen heads.
     """
     T = np.asarray(c_kv).shape[0]
     pos = np.arange(T)
     kr = store_value(rope(k_rope_raw, pos, base), "bf16")
     o, _, lse = decode_mha_form(q_nope, q_rope, np.asarray(c_kv, dtype=F64), kr, pos, w_uk, w_uv, scale, base,
-                                heads, operand_dtype)
+                                heads)
     return o, lse
 
 
 def prefill_chunk_mha_form(q_nope, q_rope, c_cached, kr_cached, w_uk, w_uv, scale, base,
-                           heads: Optional[Sequence[int]] = None, operand_dtype: Optional[str] = None):
+                           heads: Optional[Sequence[int]] = None):
     """Chunked prefill of one sequence in the MHA form ([P1] 双重投影,
     training/prefill column): its last Lq tokens are the queries and attend to
     all L cached tokens up to their own position (R3: query j at L - Lq + j).
@@ -285,8 +276,7 @@ def prefill_chunk_mha_form(q_nope, q_rope, c_cached, kr_cached, w_uk, w_uv, scal
     and lse [Lq, h]."""
     L, Lq = np.asarray(c_cached).shape[0], np.asarray(q_nope).shape[0]
     q_pos = L - Lq + np.arange(Lq)
-    o, _, lse = decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scale, base, heads,
-                                operand_dtype)
+    o, _, lse = decode_mha_form(q_nope, q_rope, c_cached, kr_cached, q_pos, w_uk, w_uv, scale, base, heads)
     return o, lse
 
 

@@ -67,16 +67,19 @@ def test_invalid_arguments_are_rejected(lib):
     # NULL required pointers
     assert lib.mla_absorb_q(r, 4, None, FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.mla_append_cache(r, 4, FAKE, FAKE, FAKE, FAKE, None, 1, 1, FAKE, 1, None) == 1
-    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, FAKE, 1, None, 0, None, 0, FAKE, FAKE, None) == 1
+    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, 1, FAKE, 1, None, 0, None, 0, FAKE, FAKE, None) == 1
     assert lib.mla_up_proj(r, 4, FAKE, None, FAKE, None) == 1
     assert lib.mla_up_proj_gated(r, 4, FAKE, FAKE, None, FAKE, None) == 1   # the gate is required
     assert lib.mla_up_proj_gated(r, 4, FAKE, None, FAKE, FAKE, None) == 1
     assert lib.mla_combine(r, 1, 1, None, 1, 0, FAKE, 0, FAKE, FAKE, None) == 1
+    # the pool size bounds every block id the decode reads: an empty pool is rejected
+    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, 0, FAKE, 1, FAKE, 0, None, 0, FAKE, FAKE, None) == 1
+    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, -3, FAKE, 1, FAKE, 0, None, 0, FAKE, FAKE, None) == 1
     # sizes
     assert lib.mla_absorb_q(r, -1, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
-    assert lib.mla_decode(r, 0, 1, FAKE, FAKE, FAKE, 1, FAKE, 0, None, 0, FAKE, FAKE, None) == 1
-    assert lib.mla_decode(r, 1, 0, FAKE, FAKE, FAKE, 1, FAKE, 0, None, 0, FAKE, FAKE, None) == 1
-    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, FAKE, 1, FAKE, -2, None, 0, FAKE, FAKE, None) == 1
+    assert lib.mla_decode(r, 0, 1, FAKE, FAKE, 1, FAKE, 1, FAKE, 0, None, 0, FAKE, FAKE, None) == 1
+    assert lib.mla_decode(r, 1, 0, FAKE, FAKE, 1, FAKE, 1, FAKE, 0, None, 0, FAKE, FAKE, None) == 1
+    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, 1, FAKE, 1, FAKE, -2, None, 0, FAKE, FAKE, None) == 1
     assert lib.mla_append_cache(r, 4, FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, FAKE, 0, None) == 1
     # NULL dims and malformed dims
     assert lib.mla_absorb_q(None, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None) == 1
@@ -85,6 +88,23 @@ def test_invalid_arguments_are_rejected(lib):
         assert lib.mla_up_proj(ctypes.byref(db), 4, FAKE, FAKE, FAKE, None) == 1
     nan_scale = M.make_dims(**V3, softmax_scale=float("nan"))
     assert lib.mla_up_proj(ctypes.byref(nan_scale), 4, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_rope_arguments_depend_on_d_rope(lib):
+    """With a RoPE part (d_rope > 0) the absorb needs q_rope and pos; without one
+    (d_rope = 0: the dims stay valid) they may be null, which the kernels then never
+    read (the GPU parity test of d_rope = 0 runs the calls)."""
+    d = M.make_dims(**V3)
+    r = ctypes.byref(d)
+    assert lib.mla_absorb_q(r, 4, FAKE, None, FAKE, FAKE, FAKE, None) == 1     # q_rope missing
+    assert lib.mla_absorb_q(r, 4, FAKE, FAKE, None, FAKE, FAKE, None) == 1     # pos missing
+    assert lib.mla_absorb_append(r, 4, FAKE, FAKE, None, FAKE, FAKE, 0, None, None, None, None, None, 1, 1, None,
+                                 1, None) == 1
+    no_rope = M.make_dims(**{**V3, "d_rope": 0})
+    assert M.cache_block_bytes(no_rope) == 64 * 512 * 2
+    r0 = ctypes.byref(no_rope)
+    assert lib.mla_absorb_q(r0, 0, FAKE, None, None, FAKE, FAKE, None) == 0   # valid, nothing to do
+    assert lib.mla_absorb_q(r0, 4, None, None, None, FAKE, FAKE, None) == 1   # q_nope is still required
 
 
 def test_unsupported_combinations(lib):
@@ -96,8 +116,8 @@ def test_unsupported_combinations(lib):
     # decode size limits: a sequence longer than 2^30 tokens, and 2^31 key tiles of 32 tokens in all
     d = M.make_dims(**V3)
     r = ctypes.byref(d)
-    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, FAKE, (1 << 24) + 1, FAKE, 0, FAKE, 1 << 40, FAKE, FAKE, None) == 2
-    assert lib.mla_decode(r, 64, 1, FAKE, FAKE, FAKE, 1 << 24, FAKE, 0, FAKE, 1 << 40, FAKE, FAKE, None) == 2
+    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, 1, FAKE, (1 << 24) + 1, FAKE, 0, FAKE, 1 << 40, FAKE, FAKE, None) == 2
+    assert lib.mla_decode(r, 64, 1, FAKE, FAKE, 1, FAKE, 1 << 24, FAKE, 0, FAKE, 1 << 40, FAKE, FAKE, None) == 2
     assert lib.mla_decode_workspace_bytes(r, 64, 1, 1 << 24, 0) == 0
 
 
@@ -115,8 +135,8 @@ def test_workspace_size_is_checked_before_launch(lib):
     r = ctypes.byref(d)
     need = lib.mla_decode_workspace_bytes(r, 1, 1, 64, 8)
     assert need > 0 and lib.mla_decode_needs_combine(r, 1, 1, 64, 8) == 1
-    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, FAKE, 64, FAKE, 8, None, 0, FAKE, FAKE, None) == 3
-    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, FAKE, 64, FAKE, 8, FAKE, need - 1, FAKE, FAKE, None) == 3
+    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, 1, FAKE, 64, FAKE, 8, None, 0, FAKE, FAKE, None) == 3
+    assert lib.mla_decode(r, 1, 1, FAKE, FAKE, 1, FAKE, 64, FAKE, 8, FAKE, need - 1, FAKE, FAKE, None) == 3
     assert lib.mla_combine(r, 1, 1, FAKE, 64, 8, FAKE, need - 4, FAKE, FAKE, None) == 3
     assert lib.mla_decode_workspace_bytes(r, 0, 1, 64, 8) == 0
     # one split: no partials, no workspace, nothing for combine to do
@@ -151,16 +171,18 @@ def test_prefill_paged_arguments_are_checked_before_launch(lib):
     r = ctypes.byref(d)
     ws = lib.mla_prefill_paged_workspace_bytes(r, 50, 400)
     assert ws > lib.mla_prefill_workspace_bytes(r, 50)
-    # (dims, n_seq, cu_q, Tq, max_q, cu_k, Tk, q_nope, q_rope, pool, table, max_blocks, w_uk, w_uv, gate,
-    #  ws, ws_bytes, out, lse, stream)
-    args = [r, 2, FAKE, 50, 40, FAKE, 400, FAKE, FAKE, FAKE, FAKE, 8, FAKE, FAKE, None, FAKE, ws, FAKE, FAKE, None]
-    bad = list(args); bad[10] = None                      # block table missing
+    # (dims, n_seq, cu_q, Tq, max_q, cu_k, Tk, q_nope, q_rope, pool, n_pool_blocks, table, max_blocks, w_uk, w_uv,
+    #  gate, ws, ws_bytes, out, lse, stream)
+    args = [r, 2, FAKE, 50, 40, FAKE, 400, FAKE, FAKE, FAKE, 16, FAKE, 8, FAKE, FAKE, None, FAKE, ws, FAKE, FAKE, None]
+    bad = list(args); bad[11] = None                      # block table missing
     assert lib.mla_prefill_paged(*bad) == 1
     bad = list(args); bad[6] = 49                         # fewer cached tokens than queries
     assert lib.mla_prefill_paged(*bad) == 1
-    bad = list(args); bad[11] = 0                         # no blocks
+    bad = list(args); bad[12] = 0                         # no table columns
     assert lib.mla_prefill_paged(*bad) == 1
-    bad = list(args); bad[16] = ws - 1
+    bad = list(args); bad[10] = 0                         # an empty pool
+    assert lib.mla_prefill_paged(*bad) == 1
+    bad = list(args); bad[17] = ws - 1
     assert lib.mla_prefill_paged(*bad) == 3
     bad = list(args); bad[3] = 0
     assert lib.mla_prefill_paged(*bad) == 0

@@ -1,9 +1,10 @@
-"""GPU parity of the MHA-form prefill (mla_prefill) against the CPU oracle, on
+"""GPU parity of the MHA-form prefill (mla_prefill, mla_prefill_paged) against
+the CPU oracle's exact MHA form (float64 throughout: no operand is rounded), on
 packed sequences whose lengths cover one token, partial and several 64-key
-blocks and 128-query blocks, with 16 and 128 heads.  The oracle rounds the
-rotated query part and the decompressed keys and values to bf16, where the
-library's matrix-unit operands are rounded (mla.h states these points); the
-rest is float64.  All calls go through the C ABI."""
+blocks and 128-query blocks, with 16 and 128 heads, a 4096-token prompt, and
+bf16 and fp8 paged caches.  The library rotates the RoPE parts by the absorb's
+rule and runs the contractions on bf16 matrix units with fp32 sums; the bar is
+the bf16 one.  All calls go through the C ABI."""
 import numpy as np
 import pytest
 import torch
@@ -35,9 +36,35 @@ def test_prefill_matches_oracle(heads, lens, cuda_device):
         want_o, want_lse = O.prefill_mha_form(inp["q_nope"][sl].double().numpy(), inp["q_rope"][sl].double().numpy(),
                                               inp["c_kv"][sl].double().numpy(), inp["k_rope"][sl].double().numpy(),
                                               inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
-                                              w.softmax_scale, w.rope_base, operand_dtype="bf16")
+                                              w.softmax_scale, w.rope_base)
         U.assert_close(out[sl], want_o, "bf16", f"out seq {b} L={L}")
         U.assert_close(lse[sl], want_lse, "bf16", f"lse seq {b} L={L}")
+
+
+def test_prefill_long_prompt_sampled_heads(cuda_device):
+    """One 4096-token prompt and a short one, all 128 heads computed, checked
+    against the exact MHA form on sampled heads (every query row)."""
+    import mla_latent_kv_23_amd as M
+    w = V3
+    lens = [4096, 77]
+    heads_chk = [0, 41, 127]
+    inp = S.make_prefill_inputs(w, 4096, torch.tensor(lens, dtype=torch.int32))
+    U.say(f"[prefill long] lens={lens} heads={heads_chk}")
+    d = U.dims_of(w)
+    dev = cuda_device
+    out, lse, _ = M.prefill(d, inp["q_nope"].to(dev), inp["q_rope"].to(dev), inp["c_kv"].to(dev),
+                            inp["k_rope"].to(dev), inp["cu_seqlens"].to(dev), max(lens), inp["w_uk"].to(dev),
+                            inp["w_uv"].to(dev))
+    torch.cuda.synchronize()
+    cu = inp["cu_seqlens"].tolist()
+    for b, L in enumerate(lens):
+        sl = slice(cu[b], cu[b] + L)
+        want_o, want_lse = O.prefill_mha_form(inp["q_nope"][sl].double().numpy(), inp["q_rope"][sl].double().numpy(),
+                                              inp["c_kv"][sl].double().numpy(), inp["k_rope"][sl].double().numpy(),
+                                              inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
+                                              w.softmax_scale, w.rope_base, heads=heads_chk)
+        U.assert_close(out[sl][:, heads_chk], want_o, "bf16", f"out seq {b} L={L}")
+        U.assert_close(lse[sl][:, heads_chk], want_lse, "bf16", f"lse seq {b} L={L}")
 
 
 def test_prefill_reuses_one_workspace(cuda_device):
@@ -63,7 +90,7 @@ def test_prefill_reuses_one_workspace(cuda_device):
                                                   inp["q_rope"][sl].double().numpy(),
                                                   inp["c_kv"][sl].double().numpy(), inp["k_rope"][sl].double().numpy(),
                                                   inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
-                                                  w.softmax_scale, w.rope_base, operand_dtype="bf16")
+                                                  w.softmax_scale, w.rope_base)
             U.assert_close(out[sl], want_o, "bf16", f"out seq {b} L={L}")
             U.assert_close(lse[sl], want_lse, "bf16", f"lse seq {b} L={L}")
 
@@ -99,8 +126,7 @@ def test_prefill_paged_runs_on_the_callers_stream(cuda_device):
         want_o, want_lse = O.prefill_chunk_mha_form(inp["q_nope"][qs].double().numpy(),
                                                     inp["q_rope"][qs].double().numpy(), c, kr,
                                                     inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
-                                                    w.softmax_scale, w.rope_base, heads=list(range(16)),
-                                                    operand_dtype="bf16")
+                                                    w.softmax_scale, w.rope_base, heads=list(range(16)))
         U.assert_close(out[qs], want_o, "bf16", f"out seq {b} L={L} Lq={Lq}")
         U.assert_close(lse[qs], want_lse, "bf16", f"lse seq {b} L={L} Lq={Lq}")
 
@@ -146,8 +172,7 @@ def test_prefill_paged_matches_oracle(heads, lens, qlens, cache, cuda_device):
         want_o, want_lse = O.prefill_chunk_mha_form(inp["q_nope"][qs].double().numpy(),
                                                     inp["q_rope"][qs].double().numpy(), c, kr,
                                                     inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
-                                                    w.softmax_scale, w.rope_base, heads=heads_chk,
-                                                    operand_dtype="bf16")
+                                                    w.softmax_scale, w.rope_base, heads=heads_chk)
         U.assert_close(out[qs][:, heads_chk], want_o, "bf16", f"out seq {b} L={L} Lq={Lq}")
         U.assert_close(lse[qs][:, heads_chk], want_lse, "bf16", f"lse seq {b} L={L} Lq={Lq}")
 
@@ -178,8 +203,7 @@ def test_prefill_paged_block_sizes(block_size, cache, cuda_device):
         want_o, want_lse = O.prefill_chunk_mha_form(inp["q_nope"][qs].double().numpy(),
                                                     inp["q_rope"][qs].double().numpy(), c, kr,
                                                     inp["w_uk"].double().numpy(), inp["w_uv"].double().numpy(),
-                                                    w.softmax_scale, w.rope_base, heads=list(range(16)),
-                                                    operand_dtype="bf16")
+                                                    w.softmax_scale, w.rope_base, heads=list(range(16)))
         U.assert_close(out[qs], want_o, "bf16", f"out seq {b} L={L} Lq={Lq}")
         U.assert_close(lse[qs], want_lse, "bf16", f"lse seq {b} L={L} Lq={Lq}")
 
@@ -218,11 +242,10 @@ def test_prefill_output_gate(paged, cuda_device):
         if paged:
             c, kr = O.cached_token_values(inp["c_kv"][ks].double().numpy(), inp["k_rope"][ks].double().numpy(),
                                           np.arange(L), w.cache_dtype, w.rope_base)
-            o, l = O.prefill_chunk_mha_form(qn, qr, c, kr, wk, wv, w.softmax_scale, w.rope_base,
-                                            operand_dtype="bf16")
+            o, l = O.prefill_chunk_mha_form(qn, qr, c, kr, wk, wv, w.softmax_scale, w.rope_base)
         else:
             o, l = O.prefill_mha_form(qn, qr, inp["c_kv"][ks].double().numpy(), inp["k_rope"][ks].double().numpy(),
-                                      wk, wv, w.softmax_scale, w.rope_base, operand_dtype="bf16")
+                                      wk, wv, w.softmax_scale, w.rope_base)
         want = O.output_gate(o, gate[qs].double().numpy())
         U.assert_close(out[qs], want, "bf16", f"gated out seq {b}")
         U.assert_close(lse[qs], l, "bf16", f"lse seq {b}")
