@@ -244,6 +244,27 @@ mla_status mla_decode(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
                       const int32_t* cache_seqlens, int32_t num_splits, void* workspace,
                       size_t workspace_bytes, void* o_latent, float* lse, mla_stream_t stream);
 
+/*
+ * mla_decode_noalloc -- mla_decode followed by mla_combine, for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc).  Arguments, results and errors as
+ * mla_decode, without the workspace: the split partials go to a static
+ * device array inside the library, MLA_DECODE_NOALLOC_MAX_BYTES long, one per
+ * GPU the library runs on, held until the process ends.  A problem whose
+ * workspace (mla_decode_workspace_bytes with the same arguments) exceeds that
+ * size returns MLA_ERR_WORKSPACE before any launch.  Nothing is allocated
+ * and nothing needs clearing (every partial is written before it is read).
+ * All calls on one GPU share that GPU's array, which keeps the last call's
+ * partials: two calls that overlap in time on one GPU (different streams
+ * without ordering, or threads) race.  The first call on a device looks up
+ * the array's device address (hipGetSymbolAddress) with that device current.
+ */
+#define MLA_DECODE_NOALLOC_MAX_BYTES (64u << 20)
+mla_status mla_decode_noalloc(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
+                              const void* q_abs, const void* cache_pool, int64_t n_pool_blocks,
+                              const int32_t* block_table, int32_t max_blocks,
+                              const int32_t* cache_seqlens, int32_t num_splits, void* o_latent,
+                              float* lse, mla_stream_t stream);
 
 /* 1 if mla_decode with these arguments leaves partials for mla_combine, else 0. */
 int32_t mla_decode_needs_combine(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,

@@ -60,6 +60,7 @@ SIGNATURES = {
     "mla_decode_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I32, _I32]),
     "mla_decode": (ctypes.c_int, [_DP, _I32, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _P, _SZ, _P, _P, _P]),
     "mla_decode_needs_combine": (_I32, [_DP, _I32, _I32, _I32, _I32]),
+    "mla_decode_noalloc": (ctypes.c_int, [_DP, _I32, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P]),
     "mla_combine": (ctypes.c_int, [_DP, _I32, _I32, _P, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "mla_up_proj": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P]),
     "mla_up_proj_gated": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P, _P]),

@@ -3,9 +3,17 @@
 // status; no C++ exception crosses the boundary.
 #include <cmath>
 #include <cstring>
+#include <mutex>
 
 #include "mla_internal.h"
 #include "decode_latent576.h"
+
+// Scratch of mla_decode_noalloc: the split partials and their statistics live
+// in this array instead of a caller-provided workspace.  Each GPU the library
+// runs on holds its own copy until the process ends.  In host code the name is
+// only a stand-in for the symbol: the device address comes from
+// hipGetSymbolAddress, once per device (mla::noalloc_scratch).
+static __device__ __align__(256) uint8_t scratch[MLA_DECODE_NOALLOC_MAX_BYTES];
 
 namespace mla {
 
@@ -101,6 +109,25 @@ DecodePlan make_plan(const mla_dims& d, int32_t n_seq, int32_t q_per_seq, int32_
   p.ws_bytes =
       p.n_slots ? static_cast<size_t>(p.ws_stats_offset_floats + 2LL * p.n_slots * rows_per_slot) * sizeof(float) : 0;
   return p;
+}
+
+// The device address of `scratch` on the current device, looked up with that
+// device current on its first use and kept per device.
+constexpr int kMaxDevices = 256;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+mla_status noalloc_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MLA_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return MLA_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MLA_OK;
 }
 
 mla_status check_decode_args(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, int32_t max_blocks,
@@ -235,6 +262,33 @@ mla_status mla_decode(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const
   }
   return launch_decode_generic(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, n_pool_blocks, block_table, max_blocks,
                                cache_seqlens, plan.ws_bytes ? workspace : nullptr, o_latent, lse, st);
+}
+
+mla_status mla_decode_noalloc(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const void* q_abs,
+                              const void* cache_pool, int64_t n_pool_blocks, const int32_t* block_table,
+                              int32_t max_blocks, const int32_t* cache_seqlens, int32_t num_splits, void* o_latent,
+                              float* lse, mla_stream_t stream) {
+  const mla_status s = check_decode_args(d, n_seq, q_per_seq, max_blocks, num_splits);
+  if (s != MLA_OK) return s;
+  if (n_pool_blocks <= 0) return MLA_ERR_INVALID_ARG;
+  if (!q_abs || !cache_pool || !block_table || !cache_seqlens || !o_latent || !lse) return MLA_ERR_INVALID_ARG;
+  const DecodePlan plan = make_plan(*d, n_seq, q_per_seq, max_blocks, num_splits);
+  if (plan.ws_bytes > static_cast<size_t>(MLA_DECODE_NOALLOC_MAX_BYTES)) return MLA_ERR_WORKSPACE;
+  if (plan.kind == 1 && (!aligned16(q_abs) || !aligned16(cache_pool) || !aligned16(o_latent)))
+    return MLA_ERR_INVALID_ARG;
+  void* ws = nullptr;
+  if (plan.ws_bytes > 0) {
+    const mla_status g = noalloc_scratch(&ws);
+    if (g != MLA_OK) return g;
+  }
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  mla_status r = plan.kind == 1 ? launch_decode576(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, n_pool_blocks,
+                                                   block_table, max_blocks, cache_seqlens, ws, o_latent, lse, st)
+                                : launch_decode_generic(*d, plan, n_seq, q_per_seq, q_abs, cache_pool, n_pool_blocks,
+                                                        block_table, max_blocks, cache_seqlens, ws, o_latent, lse, st);
+  if (r == MLA_OK && plan.needs_combine)
+    r = launch_combine(*d, plan, n_seq, q_per_seq, cache_seqlens, ws, o_latent, lse, st);
+  return r;
 }
 
 mla_status mla_combine(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const int32_t* cache_seqlens,

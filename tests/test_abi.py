@@ -121,6 +121,20 @@ def test_unsupported_combinations(lib):
     assert lib.mla_decode_workspace_bytes(r, 64, 1, 1 << 24, 0) == 0
 
 
+def test_noalloc_decode_checks_before_any_launch(lib):
+    """The no-allocation decode rejects what mla_decode rejects, and a problem
+    whose partials exceed its static array, before touching the GPU."""
+    d = M.make_dims(**V3)
+    r = ctypes.byref(d)
+    # (dims, n_seq, q_per_seq, q_abs, pool, n_pool_blocks, table, max_blocks, seqlens, splits, o, lse, stream)
+    assert lib.mla_decode_noalloc(r, 1, 1, FAKE, FAKE, 1, FAKE, 1, None, 0, FAKE, FAKE, None) == 1
+    assert lib.mla_decode_noalloc(r, 1, 1, FAKE, FAKE, 0, FAKE, 1, FAKE, 0, FAKE, FAKE, None) == 1
+    # 4096 sequences x 128 heads of bf16 partials: far beyond 64 MiB
+    need = lib.mla_decode_workspace_bytes(r, 4096, 1, 128, 0)
+    assert need > 64 << 20
+    assert lib.mla_decode_noalloc(r, 4096, 1, FAKE, FAKE, 1, FAKE, 128, FAKE, 0, FAKE, FAKE, None) == 3
+
+
 def test_empty_calls_do_nothing(lib):
     d = M.make_dims(**V3)
     r = ctypes.byref(d)
