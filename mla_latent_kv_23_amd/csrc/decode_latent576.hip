@@ -11,15 +11,19 @@
 //  * A work-group serves 128 (query row, head) "pairs": all 128 heads of one
 //    query row, or 64 heads x 2 rows (grid.y picks the head group).
 //  * HBM -> LDS: each tile (32 rows x 1152 B, contiguous inside a paged block)
-//    is copied with 16-byte direct-to-LDS loads into a 4-stage ring, so up to
-//    three tiles are in flight while one is consumed.  In LDS a tile is a grid
-//    of 1 KB blocks, each holding 8 rows x 8 sixteen-byte chunks; inside a
-//    block the chunk position is XOR-swizzled by the row, which keeps both
-//    operand read patterns below free of LDS bank conflicts and lets one wave
-//    load a whole 1 KB block per instruction with a single per-lane offset.
+//    is copied with 16-byte direct-to-LDS loads into a 4-stage ring.  In LDS a
+//    tile is a grid of 1 KB blocks, each holding 8 rows x 8 sixteen-byte
+//    chunks; rows r and r + 8 of a tile sit in different halves of their 1 KB
+//    blocks and the chunk position is XOR-swizzled by the row, so the K reads
+//    and the V transpose reads below hit distinct LDS banks within each group
+//    of 16 lanes, and one wave loads a whole 1 KB block per instruction.
 //  * S^T = K Q^T on bf16 MFMA 32x32x16: wave w owns pairs 32w..32w+31 and
 //    keeps their queries in registers as the B operand; the K tile is the A
-//    operand (one 16-byte LDS read per lane per k-step).
+//    operand (one 16-byte LDS read per lane per k-step).  With all 128 pairs
+//    in one work-group (bf16 cache) the score tile is kept in VGPRs (the MFMAs
+//    are written as assembly), so that the 16 output tiles own the 256 AGPRs,
+//    and the nine loads of tile T+2 are issued one at a time between the
+//    MFMAs of QK(T) instead of in one burst after the barrier.
 //  * Online softmax in the exp2 domain against a per-pair reference max fixed
 //    by the first tile that shows the pair a key; P = 2^(z - ref) is rounded
 //    to bf16 and exchanged through LDS.  Should a later tile exceed the
@@ -31,6 +35,8 @@
 //  * O^T += V^T P^T on bf16 MFMA 32x32x16: wave w owns latent dims
 //    128w..128w+127 for all 128 pairs (fp32 accumulators, 256 per lane); V^T
 //    comes straight from the row-major tile with the LDS transpose read.
+#include <type_traits>
+
 #include "decode_tile.h"
 
 namespace mla {
@@ -103,6 +109,21 @@ __device__ __forceinline__ void wait_tiles_fp8(int n) {
   else wait_vmcnt<0>();
 }
 
+// QK with the score tile in VGPRs, written as assembly so that the compiler
+// cannot place the accumulator in AGPRs (those hold the 16 output tiles).
+// Back-to-back MFMAs accumulating into the same registers need no wait states;
+// the chain starts from the inline constant 0.  The vector ALU may read the
+// result only after the last MFMA has written it: mfma_to_valu waits 24
+// states, more than an 8-pass XDL op requires.  The A/B operands come from LDS
+// reads and global loads, never from vector ALU writes.
+__device__ __forceinline__ void mfma_qk_first(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_to_valu(f32x16& acc) { asm volatile("s_nop 15\n\ts_nop 7" : "+v"(acc)); }
+
 template <bool kFp8, int kPB>
 __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t* __restrict__ block_table,
                                                           const int32_t* __restrict__ seqlens) {
@@ -117,6 +138,8 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
   // queries) are given to work-groups of one XCD so they share its L2.
   const int unit = xcd_unit(blockIdx.x, G), hg = blockIdx.y;
   const int32_t max_len = a.max_blocks * a.block_size;
+  // block ids are 32-bit: a pool of 2^31 blocks or more bounds nothing below INT32_MAX
+  const int32_t npool32 = a.n_pool_blocks < INT32_MAX ? (int32_t)a.n_pool_blocks : INT32_MAX;
   // sequence length as used here: clamped to what the block table can address
   auto seq_len = [&](int b) -> int32_t { return min(max(seqlens[b], 0), max_len); };
 
@@ -208,12 +231,14 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
   lds_i32* s_flag = (lds_i32*)(lds + kOffFlag);
 
   // O^T tiles [db][pb] for dims 128*wave + 32*db, pairs 32*pb.  With 16
-  // tiles (kPB = 4), tiles 0..14 are MFMA accumulators (AGPRs) and tile 15 is
-  // kept in plain VGPRs (o15), getting each tile's contribution added with
-  // vector ALU ops, so that the MFMA accumulators (15 O tiles + the S tile) fit
-  // the 256 AGPRs.  The accumulators are only ever MFMA-updated, zeroed, or
-  // stored raw.
-  constexpr bool kSplitTile = kPB == 4;
+  // tiles (kPB = 4) they fill the 256 AGPRs, so the score tile has to live
+  // elsewhere: the bf16 cache keeps it in VGPRs (kAsmQK); the fp8 cache keeps
+  // tiles 0..14 as MFMA accumulators and tile 15 in plain VGPRs (o15), getting
+  // each tile's contribution added with vector ALU ops, so that the MFMA
+  // accumulators (15 O tiles + the S tile) fit the AGPRs.  The accumulators are
+  // only ever MFMA-updated, zeroed, or stored raw.
+  constexpr bool kAsmQK = !kFp8 && kPB == 4;
+  constexpr bool kSplitTile = kPB == 4 && !kAsmQK;
   constexpr int kOAcc = kSplitTile ? 15 : 4 * kPB;
   f32x16 o[kOAcc];
   float o15[kSplitTile ? 16 : 1];
@@ -233,17 +258,6 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     float m_ref = -INFINITY, l_part = 0.f;
     // a block-table entry names a block of the pool (else it is padding: its tokens are masked, never read)
     auto in_pool = [&](int32_t blk) { return blk >= 0 && (int64_t)blk < a.n_pool_blocks; };
-    // source of tile T of this sequence (rows beyond L or a padding block entry read block 0, masked)
-    auto tile_src = [&](int T, int* valid) -> const uint8_t* {
-      const int tok0 = (int)(T - seq_start) * kTile;
-      *valid = min(kTile, L - tok0);
-      const int32_t blk = bt_row[tok0 / a.block_size];
-      if (!in_pool(blk)) {
-        *valid = 0;
-        return a.pool;
-      }
-      return a.pool + (int64_t)blk * a.block_bytes + (int64_t)(tok0 % a.block_size) * kRowBytes;
-    };
     // rows of tile T that hold tokens of the sequence (0 for a padding block entry)
     auto tile_valid = [&](int T) -> int {
       const int tok0 = (int)(T - seq_start) * kTile;
@@ -254,13 +268,41 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     uint32_t stage_pad = 0;
     // issue this wave's share of the loads of tile T: bf16 straight into ring
     // stage T % kStages; fp8 into staging slot T % 3 (expanded later)
+    // Load cursor (bf16 cache): the block-table position of the next tile to
+    // load, with the entry after it fetched one block ahead, so that issuing a
+    // tile's loads never waits for a block-table read and needs no division.
+    int c_pos = 0, c_sub = 0;
+    int32_t c_blk = -1, c_nxt = -1;
+    const int tpb = a.block_size / kTile;              // tiles per cache block
+    auto cursor_at = [&](int T) {
+      const int t = T - seq_start;
+      c_pos = t / tpb;
+      c_sub = t - c_pos * tpb;
+      c_blk = bt_row[c_pos];
+      c_nxt = c_pos + 1 < a.max_blocks ? bt_row[c_pos + 1] : -1;
+    };
+    if constexpr (!kFp8) cursor_at(p0);
+    // bf16: prepare the loads of tile T (the cursor's tile) and advance the cursor
+    auto load_prep = [&](int T) -> TilePart {
+      const int tok0 = (int)(T - seq_start) * kTile;
+      const bool ok = c_blk >= 0 && c_blk < npool32;
+      const int valid = ok ? min(kTile, L - tok0) : 0;
+      const uint8_t* src = ok ? a.pool + (int64_t)c_blk * a.block_bytes + (int64_t)c_sub * (kTile * kRowBytes) : a.pool;
+      const uint32_t bit = 1u << (T % kStages);
+      stage_pad = valid == 0 ? (stage_pad | bit) : (stage_pad & ~bit);
+      if (++c_sub == tpb) {
+        c_sub = 0;
+        ++c_pos;
+        c_blk = c_nxt;
+        c_nxt = c_pos + 1 < a.max_blocks ? bt_row[c_pos + 1] : -1;
+      }
+      return tile_part_prep(src, valid, lds + (int)(T % kStages) * kTileBytes, wave, lane);
+    };
     auto load_tile = [&](int T) {
       if constexpr (!kFp8) {
-        int valid;
-        const uint8_t* src = tile_src(T, &valid);
-        const uint32_t bit = 1u << (T % kStages);
-        stage_pad = valid == 0 ? (stage_pad | bit) : (stage_pad & ~bit);
-        issue_tile(src, valid, lds + (int)(T % kStages) * kTileBytes, wave, lane);
+        const TilePart p = load_prep(T);
+#pragma unroll
+        for (int i = 0; i < kLoadsPerWave; ++i) tile_part_issue(p, i);
       } else {
         const int tok0 = (int)(T - seq_start) * kTile;
         const int32_t blk = bt_row[tok0 / a.block_size];
@@ -431,7 +473,8 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         }
       };
 
-      while (T_issue - p0 < kStages - 1 && T_issue < p1) load_tile(T_issue++);
+      // tiles ahead of the first: two when the loop issues during QK (kAsmQK), else three
+      while (T_issue - p0 < (kAsmQK ? kStages - 2 : kStages - 1) && T_issue < p1) load_tile(T_issue++);
       wait_tile(T_issue - 1 - p0);           // tile p0 has landed
       lds_barrier();
       if constexpr (kFp8) {
@@ -449,6 +492,42 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       // the slot of T, and tile T+1 is expanded into the bf16 buffer of T-1
       // (whose PV also finished before it).  The second publishes the expanded
       // tile T+1 and ends PV(T).
+      if constexpr (kAsmQK) {
+        // bf16, 4 pair blocks: the loads of tile T+2 go out one by one between
+        // the MFMAs of QK(T), into the stage of T-2 (free since the previous
+        // barrier); one barrier per tile publishes P(T) and tile T+1.
+        for (int T = p0; T < p1; ++T) {
+          const uint32_t tb = tile_base(T);
+          f32x16 sacc;
+          float s_rope[16];
+          auto qk = [&](const TilePart* lp) {
+            bf16x8 kf[kKAhead];
+#pragma unroll
+            for (int k = 0; k < kKAhead; ++k) kf[k] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (k / 4));
+#pragma unroll
+            for (int k = 0; k < kQSteps; ++k) {
+              const bf16x8 cur = kf[k % kKAhead];
+              if (k == 0) mfma_qk_first(sacc, cur, q[k]);
+              else mfma_qk(sacc, cur, q[k]);
+              if (k + kKAhead < kQSteps)
+                kf[k % kKAhead] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * ((k + kKAhead) / 4));
+              if (lp != nullptr && k % 4 == 1) tile_part_issue(*lp, k / 4);
+              __builtin_amdgcn_sched_barrier(0);
+            }
+            mfma_to_valu(sacc);
+          };
+          if (T_issue < p1) {
+            const TilePart lp = load_prep(T_issue++);
+            qk(&lp);
+          } else {
+            qk(nullptr);
+          }
+          softmax(sacc, s_rope, T);
+          if (T + 1 < p1) wait_tile(T_issue - 2 - T);   // tile T+1 has landed (T+2 may be in flight)
+          lds_barrier();
+          pv(tb, T);
+        }
+      } else {
       for (int T = p0; T < p1; ++T) {
         const uint32_t tb = tile_base(T);
         if (qk_wave) {
@@ -504,6 +583,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         pv(tb, T);
         if constexpr (kFp8) lds_barrier();
       }
+      }
       wait_vmcnt<0>();
       lds_barrier();                         // every wave is done with the last tile and P (the flags share P buffer 0)
       if (lane == 0) s_flag[wave] = redo ? 1 : 0;
@@ -511,11 +591,24 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       const bool any_redo = (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) != 0;
       lds_barrier();                         // flags read
       if (!any_redo) break;
+      if constexpr (!kFp8) cursor_at(p0);    // the second attempt loads from the first tile again
       // Some pair's reference rose by more than 2^16 after it had accumulated
       // weights: run the piece again.  Every reference now lies within 2^16 of
       // its pair's maximum over the piece, so the second pass cannot jump.
     }
 
+    // The epilogue derives its lane-dependent values again from an opaque copy
+    // of the lane id, so that the compiler does not compute them ahead of the
+    // tile loop and hold them (spilled to scratch) across it.
+    int lane_x = lane;
+    asm volatile("" : "+v"(lane_x));
+    const int e_half = lane_x >> 5;
+    const int e_pair = 32 * wave + (lane_x & 31);
+    const int e_j_raw = e_pair / hpw;
+    const bool e_pad = kPB == 4 ? false : e_j_raw >= a.q_per_seq;
+    const int e_j = kPB == 4 ? e_j_raw : min(e_j_raw, a.q_per_seq - 1);
+    const int e_s = hg * hpw + e_pair % hpw;
+    const int e_tid = 64 * wave + lane_x;
     // ---- finish the piece.  The accumulators go out through LDS (free now:
     // every load has landed and every wave is past the last tile): each lane
     // rounds its pair's values to bf16 into one 1 KB row per pair, so that each
@@ -530,26 +623,27 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
       l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
     }
-    if (lane < 32 && qk_wave) {
-      if (!whole && !pad) {
-        const int my_row = my_j * a.n_heads + my_s;
+    if (lane_x < 32 && qk_wave) {
+      if (!whole && !e_pad) {
+        const int my_row = e_j * a.n_heads + e_s;
         a.ws_stats[(slot_row0 + my_row) * 2] = m_ref;
         a.ws_stats[(slot_row0 + my_row) * 2 + 1] = l_tot;
       }
-      s_l[my_pair] = l_tot;
-      s_m[my_pair] = m_ref;
+      s_l[e_pair] = l_tot;
+      s_m[e_pair] = m_ref;
     }
     if constexpr (!kFp8) {
       lds_barrier();                               // every pair's l is in LDS
       // a partial is stored raw (a factor of 1 is exact), a whole sequence normalised
       const bool norm = whole;
+      auto stage = [&](auto norm_c) {
+      constexpr bool kNorm = decltype(norm_c)::value;
 #pragma unroll
       for (int pb = 0; pb < kPB; ++pb) {
-        const int pair = 32 * pb + (lane & 31);
-        const float l = s_l[pair];
-        const float inv = !norm ? 1.0f : l > 0.f ? 1.0f / l : 0.f;
+        const int pair = 32 * pb + (lane_x & 31);
+        const float inv = kNorm ? (s_l[pair] > 0.f ? 1.0f / s_l[pair] : 0.f) : 1.0f;
         // lane: dims 128 wave + 32 db + 8 (i / 4) + 4 half + i % 4 of its pair
-        lds_u8* yrow = lds + pair * kYRow + (128 * wave + 4 * half) * 2;
+        lds_u8* yrow = lds + pair * kYRow + (128 * wave + 4 * e_half) * 2;
 #pragma unroll
         for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -559,19 +653,23 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
             else v = f32x4{o[db * kPB + pb][4 * qq], o[db * kPB + pb][4 * qq + 1], o[db * kPB + pb][4 * qq + 2],
                            o[db * kPB + pb][4 * qq + 3]};
             // hardware pack, round to nearest even
-            const bf16x2 lo = __builtin_convertvector(f32x2{v[0] * inv, v[1] * inv}, bf16x2);
-            const bf16x2 hi = __builtin_convertvector(f32x2{v[2] * inv, v[3] * inv}, bf16x2);
+            if constexpr (kNorm) v = v * inv;
+            const bf16x2 lo = __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2);
+            const bf16x2 hi = __builtin_convertvector(f32x2{v[2], v[3]}, bf16x2);
             *(lds_u32x2*)(yrow + (32 * db + 8 * qq) * 2) = u32x2{*(const uint32_t*)&lo, *(const uint32_t*)&hi};
           }
       }
+      };
+      if (norm) stage(std::true_type{});
+      else stage(std::false_type{});
       lds_barrier();                                // the rows (and s_l, s_m) are in LDS
       {
         // thread t: 16-byte chunk t % 64 of rows t / 64 + 4k (one wave writes one 1 KB row)
-        const int c = tid & 63;
+        const int c = e_tid & 63;
         uint16_t* const dst0 = (norm ? a.o_final + (int64_t)b * rows_per_seq * kDc : a.ws_o + slot_row0 * kDc) + 8 * c;
 #pragma unroll 4
         for (int k = 0; k < 8 * kPB; ++k) {
-          const int pair = (tid >> 6) + 4 * k;
+          const int pair = (e_tid >> 6) + 4 * k;
           if (kPB != 4 && pair / hpw >= a.q_per_seq) continue;   // padding
           const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
           const u32x4 v = *(const lds_u32x4*)(lds + pair * kYRow + c * 16);
@@ -587,7 +685,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
 #pragma unroll
         for (int pbl = 0; pbl < kHalfPairs / 32; ++pbl) {
           const int pb = 2 * hp + pbl;
-          lds_u8* xrow = lds + (32 * pbl + (lane & 31)) * kXRow + (128 * wave + 4 * half) * 4;
+          lds_u8* xrow = lds + (32 * pbl + (lane_x & 31)) * kXRow + (128 * wave + 4 * e_half) * 4;
 #pragma unroll
           for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -601,10 +699,10 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         }
         lds_barrier();                              // the rows (and s_l, s_m) are in LDS
         // thread t: 16-byte chunk t % 128 of rows t / 128 + 2k
-        const int c = tid & 127;
+        const int c = e_tid & 127;
 #pragma unroll 4
         for (int k = 0; k < kHalfPairs / 2; ++k) {
-          const int r = (tid >> 7) + 2 * k;
+          const int r = (e_tid >> 7) + 2 * k;
           const int pair = 64 * hp + r;
           if (kPB != 4 && pair / hpw >= a.q_per_seq) continue;   // padding
           const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
@@ -626,14 +724,14 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         lds_barrier();                              // the staging rows are free again
       }
     }
-    if (whole && tid < 32 * kPB && (kPB == 4 || tid / hpw < a.q_per_seq)) {
-      const int pair = tid;
+    if (whole && e_tid < 32 * kPB && (kPB == 4 || e_tid / hpw < a.q_per_seq)) {
+      const int pair = e_tid;
       const int row_in_seq = (pair / hpw) * a.n_heads + hg * hpw + pair % hpw;
       const float l = s_l[pair], m = s_m[pair];
       a.lse_final[(int64_t)b * rows_per_seq + row_in_seq] = l > 0.f ? (m + log2f(l)) * 0.69314718055994530942f : -INFINITY;
     }
-    __syncthreads();                           // s_l / s_m and the LDS stages are free again
     if (seq_end >= T1) break;
+    lds_barrier();                             // s_l / s_m and the LDS stages are free again
     // next sequence holding tiles
     seq_start = seq_end;
     do {

@@ -73,53 +73,44 @@ __device__ __forceinline__ int xcd_unit(int i, int G) {
 // loads rows 8w..8w+7: nine 1 KB blocks, one per instruction; lane l (row
 // position l/8 of its block) brings row 8w + ((l/8) ^ (w % 2)), logical chunk
 // 8i + ((l % 8) ^ swz(row % 8)).  Rows at or beyond `valid` re-read row 0
-// (finite data; their probabilities are 0).
+// (finite data; their probabilities are 0).  tile_part_prep computes a wave's
+// share once; tile_part_issue(p, i) sends its block i, so that the nine loads
+// can be spread between other instructions.
 // The direct-to-LDS loads are written in assembly: the compiler's wait-count
 // bookkeeping treats a pending LDS DMA as a possible writer of every LDS read,
 // which makes it wait for all LDS reads at once instead of only the oldest.
 // Their completion is tracked here by hand (wait_tiles + barrier); being
 // invisible to the compiler only makes its own memory-count waits stricter.
+// They carry no memory clobber: the stage a load writes is read by no one
+// before a later barrier, which is itself ordered after the load.
 // M0 (the LDS destination of each load) is declared clobbered and left as the
 // last load set it; no other code in this kernel uses M0.
 // (the compiler notes that M0 is reserved; it is deliberately written here)
-#pragma clang diagnostic push
-#pragma clang diagnostic ignored "-Winline-asm"
-__device__ __forceinline__ void issue_tile(const uint8_t* src, int valid, lds_u8* dst, int wave, int lane) {
+struct TilePart {
+  uint64_t src;       // tile source, wave-uniform
+  uint32_t m0, off;   // LDS base of the wave's first block; per-lane source offset
+};
+__device__ __forceinline__ TilePart tile_part_prep(const uint8_t* src, int valid, lds_u8* dst, int wave, int lane) {
   const int rho = (lane >> 3) ^ (wave & 1);    // the row whose position is lane / 8
   const int row = 8 * wave + rho;
-  const uint32_t lane_off = (row < valid ? row * kRowBytes : 0) + 16 * ((lane & 7) ^ swz(rho));
+  TilePart p;
+  p.off = (row < valid ? row * kRowBytes : 0) + 16 * ((lane & 7) ^ swz(rho));
   // LDS base and source are wave-uniform: pin them to scalar registers
   // (readfirstlane yields a signed int: each half goes through uint32_t before widening)
-  const uint32_t m0 =
-      (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst + (uint32_t)(wave * kLoadsPerWave * 1024));
+  p.m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)dst + (uint32_t)(wave * kLoadsPerWave * 1024));
   const uint64_t sa = (uint64_t)(uintptr_t)src;
   const uint32_t s_hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(sa >> 32));
   const uint32_t s_lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)sa);
-  const uint64_t sv = ((uint64_t)s_hi << 32) | (uint64_t)s_lo;
-  uint32_t t;
-  static_assert(kLoadsPerWave == 9, "the load sequence below issues nine 1 KB blocks");
-  asm volatile(
-      "s_mov_b32 m0, %[m]\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[o], %[s]\n\t"
-      "v_add_u32 %[t], 0x80, %[o]\n\ts_add_u32 m0, %[m], 0x400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x100, %[o]\n\ts_add_u32 m0, %[m], 0x800\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x180, %[o]\n\ts_add_u32 m0, %[m], 0xc00\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x200, %[o]\n\ts_add_u32 m0, %[m], 0x1000\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x280, %[o]\n\ts_add_u32 m0, %[m], 0x1400\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x300, %[o]\n\ts_add_u32 m0, %[m], 0x1800\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x380, %[o]\n\ts_add_u32 m0, %[m], 0x1c00\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]\n\t"
-      "v_add_u32 %[t], 0x400, %[o]\n\ts_add_u32 m0, %[m], 0x2000\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %[t], %[s]"
-      : [t] "=&v"(t)
-      : [o] "v"(lane_off), [s] "s"(sv), [m] "s"(m0)
-      : "memory", "m0", "scc");
+  p.src = ((uint64_t)s_hi << 32) | (uint64_t)s_lo;
+  return p;
+}
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void tile_part_issue(const TilePart& p, int i) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[t], %[s]"
+               :
+               : [t] "v"(p.off + 0x80u * (uint32_t)i), [s] "s"(p.src), [m] "s"(p.m0 + 0x400u * (uint32_t)i)
+               : "m0");
 }
 
 // An fp8 cache tile (E4M3FN codes, one fp32 scale per token, bf16 k_R; the
