@@ -80,9 +80,13 @@ def parse():
     ap.add_argument("--decode-only", action="store_true",
                     help="time only the decode+combine calls (for profiling)")
     ap.add_argument("--flush-mib", type=int, default=0,
-                    help="write a scratch buffer of this many MiB before every step (outside the kernels' events) so "
+                    help="touch a scratch buffer of this many MiB before every step (outside the kernels' events) so "
                          "that a cache smaller than the 256 MB MALL is read from HBM; the step time is then the sum "
                          "of per-step event brackets instead of the outer bracket")
+    ap.add_argument("--flush-mode", choices=("read", "write"), default="read",
+                    help="how the scratch buffer evicts the cache: read it (clean lines, like the other layers' "
+                         "cache reads between two steps of one layer) or overwrite it (dirty lines, whose "
+                         "write-back then competes with the next step's reads)")
     ap.add_argument("--upstream", action="store_true",
                     help="start the step from the hidden state: mla_project_down (W_DQ, W_DKV, W_KR and the append) "
                          "and mla_absorb_from_latent (W_UQ and the absorb) replace the append and the absorb")
@@ -262,13 +266,16 @@ def main():
     torch.cuda.synchronize()
     n_ev = 5 if args.flush_mib > 0 else 3
     evs = [tuple(TimingEvent() for _ in range(n_ev)) for _ in range(args.steps)]
-    scratch = torch.empty(args.flush_mib << 20, dtype=torch.uint8, device=dev) if args.flush_mib > 0 else None
+    scratch = torch.zeros(args.flush_mib << 18, dtype=torch.float32, device=dev) if args.flush_mib > 0 else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
     for i in range(args.steps):
-        if scratch is not None:
-            scratch.fill_(i & 255)      # evicts the cache from the MALL; outside the step's events
+        if scratch is not None:         # evicts the cache from the MALL; outside the step's events
+            if args.flush_mode == "read":
+                scratch.sum()
+            else:
+                scratch.fill_(float(i & 255))
         run_step(evs[i])
     end.record(stream)
     torch.cuda.synchronize()
@@ -287,6 +294,19 @@ def main():
     dec_gbps = cache_bytes / (dec_ms * 1e-3) / 1e9
     dec_tflops = flops / (dec_ms * 1e-3) / 1e12
     tokens_per_s = n_tok / (ms_step * 1e-3)
+
+    # the decode kernel's bound: the HBM stream unless its flops per cache byte exceed the
+    # chip's ridge point (2.5 PFLOP/s / 8 TB/s = 312.5), as with two query rows or an fp8 cache
+    mfma_bound = flops / cache_bytes > BF16_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBPS * 1e9)
+    roofline = {"bound": "mfma" if mfma_bound else "hbm",
+                "achieved": round(dec_tflops if mfma_bound else dec_gbps, 1),
+                "peak": BF16_PEAK_TFLOPS if mfma_bound else HBM_PEAK_GBPS,
+                "unit": "TFLOP/s" if mfma_bound else "GB/s",
+                "frac": round(dec_tflops / BF16_PEAK_TFLOPS if mfma_bound else dec_gbps / HBM_PEAK_GBPS, 4),
+                # counter-measured bytes per launch exist for the V3 workload only
+                "traffic": measured_traffic() if w.name == "v3_bs64_ctx8k" else None,
+                "kernel": "decode576_kernel", "bytes_per_launch": cache_bytes, "flops_per_launch": flops,
+                "hbm_frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)}
 
     cpu = None
     if args.cpu_sample_seqs > 0:
@@ -310,16 +330,14 @@ def main():
                    "block_size": w.block_size, "cache_dtype": w.cache_dtype, "output_gate": bool(args.gated),
                    "from_hidden_state": bool(args.upstream),
                    "cache_flush_mib": args.flush_mib,
+                   **({"cache_flush_mode": args.flush_mode} if args.flush_mib > 0 else {}),
                    "parallelism": "single GPU"},
         "decode_ms": round(dec_ms, 4),
         "decode_combine_ms": round(dec_comb_ms, 4),
         "decode_combine_tokens_per_s": round(n_tok / (dec_comb_ms * 1e-3), 1),
         "decode_hbm_gbps": round(dec_gbps, 1),
         "decode_tflops": round(dec_tflops, 1),
-        "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                     "frac": round(dec_gbps / HBM_PEAK_GBPS, 4), "traffic": measured_traffic(),
-                     "kernel": "decode576_kernel", "bytes_per_launch": cache_bytes,
-                     "mfma_frac": round(dec_tflops / BF16_PEAK_TFLOPS, 4)},
+        "roofline": roofline,
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
