@@ -271,6 +271,25 @@ int32_t mla_decode_needs_combine(const mla_dims* dims, int32_t n_seq, int32_t q_
                                  int32_t max_blocks, int32_t num_splits);
 
 /*
+ * mla_check_block_table -- host-side check of a block table before a decode or
+ * a paged prefill (FlashMLA snippet: the block table maps a sequence's
+ * token t to block block_table[b][t / block_size] of the pool).  The kernels
+ * read an entry outside [0, n_pool_blocks) as padding (its tokens masked);
+ * this check finds such entries instead, for callers that want them reported.
+ * block_table [n_seq][max_blocks] and cache_seqlens [n_seq] are HOST int32
+ * arrays, read only.  For every sequence b, the entries
+ * 0 .. ceil(L_b / block_size) - 1 that its L_b = cache_seqlens[b] tokens use
+ * must lie in [0, n_pool_blocks); entries past them are not read.  A length
+ * outside [0, max_blocks * block_size] is an error too.  Returns MLA_OK, or
+ * MLA_ERR_INVALID_ARG with *first_bad (if not NULL) set to the flat index
+ * b * max_blocks + i of the first bad entry, or to -(b + 1) for a bad length
+ * of sequence b, or to INT64_MIN for bad sizes or pointers.  Launches nothing.
+ */
+mla_status mla_check_block_table(const int32_t* block_table, int32_t n_seq, int32_t max_blocks,
+                                 const int32_t* cache_seqlens, int32_t block_size,
+                                 int64_t n_pool_blocks, int64_t* first_bad);
+
+/*
  * mla_combine -- merge split partials by log-sum-exp (FlashMLA snippet: the
  * (o, lse) pair per split): lse = ln sum_k exp(lse_k),
  * o_lat = sum_k exp(lse_k - lse) o_k; a split that saw no token has

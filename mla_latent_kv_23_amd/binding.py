@@ -60,6 +60,7 @@ SIGNATURES = {
     "mla_decode_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I32, _I32]),
     "mla_decode": (ctypes.c_int, [_DP, _I32, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _P, _SZ, _P, _P, _P]),
     "mla_decode_needs_combine": (_I32, [_DP, _I32, _I32, _I32, _I32]),
+    "mla_check_block_table": (ctypes.c_int, [_P, _I32, _I32, _P, _I32, _I64, ctypes.POINTER(ctypes.c_int64)]),
     "mla_decode_noalloc": (ctypes.c_int, [_DP, _I32, _I32, _P, _P, _I64, _P, _I32, _P, _I32, _P, _P, _P]),
     "mla_combine": (ctypes.c_int, [_DP, _I32, _I32, _P, _I32, _I32, _P, _SZ, _P, _P, _P]),
     "mla_up_proj": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P]),
@@ -84,7 +85,9 @@ def load_library(path: Optional[str] = None) -> ctypes.CDLL:
     global _lib
     if _lib is not None and path is None:
         return _lib
-    p = path or LIB_PATH
+    # MLA_LIBRARY names another build of the same library to load instead
+    # (the host-AddressSanitizer build that the ABI checks run under)
+    p = path or os.environ.get("MLA_LIBRARY") or LIB_PATH
     if not os.path.exists(p):
         raise RuntimeError(f"libmla not built ({p} missing): run `python -m mla_latent_kv_23_amd.build`")
     lib = ctypes.CDLL(p)
@@ -168,6 +171,27 @@ def decode_workspace_bytes(d: Dims, n_seq: int, q_per_seq: int, max_blocks: int,
 
 def decode_needs_combine(d: Dims, n_seq: int, q_per_seq: int, max_blocks: int, num_splits: int = 0) -> bool:
     return bool(load_library().mla_decode_needs_combine(ctypes.byref(d), n_seq, q_per_seq, max_blocks, num_splits))
+
+
+def check_block_table(block_table, seqlens, block_size: int, n_pool_blocks: int) -> int:
+    """Host-side check of a block table (mla_check_block_table): block_table
+    [n_seq, max_blocks] and seqlens [n_seq] are CPU int32 tensors.  Returns 0,
+    or raises MLAError; the first bad entry's flat index (or -(b + 1) for a bad
+    length of sequence b) is the exception's `where`."""
+    for t, name in ((block_table, "block_table"), (seqlens, "seqlens")):
+        if t.is_cuda or t.dtype != torch.int32 or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous CPU int32 tensor")
+    n_seq, max_blocks = block_table.shape
+    if seqlens.numel() != n_seq:
+        raise ValueError("seqlens must hold one length per block-table row")
+    where = ctypes.c_int64(0)
+    code = load_library().mla_check_block_table(block_table.data_ptr(), n_seq, max_blocks, seqlens.data_ptr(),
+                                                block_size, n_pool_blocks, ctypes.byref(where))
+    if code != 0:
+        err = MLAError("mla_check_block_table", code)
+        err.where = where.value
+        raise err
+    return 0
 
 
 def decode(d: Dims, q_abs, pool, block_table, seqlens, num_splits: int = 0, workspace=None, o_latent=None,

@@ -43,9 +43,25 @@ def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *COMMON, "-c", src, "-o", obj]
+# AddressSanitizer on the host code only (argument checks, planning, the ABI
+# layer); the device code is compiled as usual.  Load the result with the
+# clang ASan runtime preloaded (see asan_runtime()).
+ASAN_FLAGS = ["-O1", "-g", "-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fno-omit-frame-pointer"]
+ASAN_BUILD = os.path.join(BUILD, "asan")
+ASAN_LIB = os.path.join(ASAN_BUILD, "libmla_asan.so")
+
+
+def asan_runtime() -> str:
+    """The clang AddressSanitizer runtime that matches hipcc's compiler."""
+    found = sorted(glob.glob("/opt/rocm/lib/llvm/lib/clang/*/lib/linux/libclang_rt.asan-x86_64.so"))
+    if not found:
+        raise RuntimeError("clang AddressSanitizer runtime not found under /opt/rocm/lib/llvm")
+    return found[-1]
+
+
+def _compile(src: str, out_dir: str = BUILD, extra=()) -> str:
+    obj = os.path.join(out_dir, os.path.basename(src) + ".o")
+    cmd = [hipcc(), *COMMON, *extra, "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -66,6 +82,23 @@ def build(verbose: bool = False) -> str:
     if verbose:
         print(f"built {LIB} from {len(srcs)} sources")
     return LIB
+
+
+def build_asan(verbose: bool = False) -> str:
+    """libmla_asan.so: the library with its host code under AddressSanitizer
+    (a checker of the host layer; the product library is build())."""
+    os.makedirs(ASAN_BUILD, exist_ok=True)
+    srcs = sources()
+    with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
+        objs = list(ex.map(lambda f: _compile(f, ASAN_BUILD, ASAN_FLAGS), srcs))
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-Xarch_host", "-fsanitize=address", "-o",
+           ASAN_LIB, *objs]
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+    if verbose:
+        print(f"built {ASAN_LIB} from {len(srcs)} sources")
+    return ASAN_LIB
 
 
 if __name__ == "__main__":

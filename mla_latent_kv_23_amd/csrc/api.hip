@@ -1,6 +1,7 @@
 // C ABI of libmla: host-side validation, decode planning and dispatch.  Every
 // entry point checks its arguments before launching anything and returns a
 // status; no C++ exception crosses the boundary.
+#include <cstdint>
 #include <cmath>
 #include <cstring>
 #include <mutex>
@@ -289,6 +290,28 @@ mla_status mla_decode_noalloc(const mla_dims* d, int32_t n_seq, int32_t q_per_se
   if (r == MLA_OK && plan.needs_combine)
     r = launch_combine(*d, plan, n_seq, q_per_seq, cache_seqlens, ws, o_latent, lse, st);
   return r;
+}
+
+mla_status mla_check_block_table(const int32_t* block_table, int32_t n_seq, int32_t max_blocks,
+                                 const int32_t* cache_seqlens, int32_t block_size, int64_t n_pool_blocks,
+                                 int64_t* first_bad) {
+  auto fail = [&](int64_t where) {
+    if (first_bad) *first_bad = where;
+    return MLA_ERR_INVALID_ARG;
+  };
+  if (n_seq < 0 || max_blocks <= 0 || block_size <= 0 || n_pool_blocks <= 0) return fail(INT64_MIN);
+  if (n_seq > 0 && (!block_table || !cache_seqlens)) return fail(INT64_MIN);
+  const int64_t max_len = static_cast<int64_t>(max_blocks) * block_size;
+  for (int32_t b = 0; b < n_seq; ++b) {
+    const int64_t L = cache_seqlens[b];
+    if (L < 0 || L > max_len) return fail(-static_cast<int64_t>(b) - 1);
+    const int64_t used = (L + block_size - 1) / block_size;
+    const int32_t* row = block_table + static_cast<int64_t>(b) * max_blocks;
+    for (int64_t i = 0; i < used; ++i)
+      if (row[i] < 0 || row[i] >= n_pool_blocks) return fail(static_cast<int64_t>(b) * max_blocks + i);
+  }
+  if (first_bad) *first_bad = 0;
+  return MLA_OK;
 }
 
 mla_status mla_combine(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const int32_t* cache_seqlens,

@@ -205,3 +205,30 @@ def test_prefill_paged_arguments_are_checked_before_launch(lib):
     f32 = M.make_dims(n_heads=4, d_c=64, d_rope=16, d_nope=32, d_v=32, act_dtype="f32", cache_dtype="f32")
     assert lib.mla_prefill_paged_workspace_bytes(ctypes.byref(f32), 50, 400) == 0
     assert lib.mla_prefill_paged(ctypes.byref(f32), *args[1:]) == 2
+
+
+def test_check_block_table_finds_the_first_bad_entry(lib):
+    """mla_check_block_table on host arrays: entries a sequence's tokens use
+    must name a pool block; entries past its length are not read."""
+    import torch
+    bs, npool = 64, 10
+    table = torch.tensor([[0, 1, 2, -1], [3, 4, 99, 7], [9, -5, 8, 8]], dtype=torch.int32)
+    # lengths 130 (entries 0..2), 128 (entries 0..1: 99 is past the length), 64 (entry 0)
+    assert M.check_block_table(table, torch.tensor([130, 128, 64], dtype=torch.int32), bs, npool) == 0
+    with pytest.raises(M.MLAError) as e:      # sequence 1 now uses entry 2 (= 99)
+        M.check_block_table(table, torch.tensor([130, 129, 64], dtype=torch.int32), bs, npool)
+    assert e.value.code == 1 and e.value.where == 1 * 4 + 2
+    with pytest.raises(M.MLAError) as e:      # sequence 2 now uses entry 1 (= -5)
+        M.check_block_table(table, torch.tensor([0, 0, 65], dtype=torch.int32), bs, npool)
+    assert e.value.where == 2 * 4 + 1
+    with pytest.raises(M.MLAError) as e:      # a length beyond max_blocks * block_size
+        M.check_block_table(table, torch.tensor([0, 257, 0], dtype=torch.int32), bs, npool)
+    assert e.value.where == -2
+    with pytest.raises(M.MLAError) as e:      # a negative length
+        M.check_block_table(table, torch.tensor([-1, 0, 0], dtype=torch.int32), bs, npool)
+    assert e.value.where == -1
+    where = ctypes.c_int64(0)
+    assert lib.mla_check_block_table(None, 1, 4, None, bs, npool, ctypes.byref(where)) == 1
+    assert where.value == -(1 << 63)
+    assert lib.mla_check_block_table(None, 0, 4, None, bs, npool, None) == 0     # no sequences: nothing read
+    assert lib.mla_check_block_table(table.data_ptr(), 3, 4, table.data_ptr(), 0, npool, None) == 1
