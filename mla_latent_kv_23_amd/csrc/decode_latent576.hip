@@ -393,22 +393,28 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
             sv[i] = t < vis ? sv[i] : -INFINITY;
           }
         }
-        float smax = sv[0];
-#pragma unroll
-        for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sv[i]);
-        {
-          // the pair's other 16 tokens live in lane l ^ 32
-          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
-          smax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
-        }
-        const float tmax = smax * sl2;
         // the reference is set by the first tile that shows this pair a key; a
         // later jump by more than 2^16 raises it (weights stay <= 2^16) and
         // marks the piece for a second pass
-        const bool had_ref = m_ref != -INFINITY;
-        const bool grow = tmax > m_ref + kRestartThreshold;
-        if (grow) m_ref = tmax;
-        redo |= __builtin_amdgcn_ballot_w64(grow && had_ref) != 0;
+        auto ref_update = [&]() {
+          float smax = sv[0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sv[i]);
+          // the pair's other 16 tokens live in lane l ^ 32
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(smax), __float_as_uint(smax), false, false);
+          smax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+          const float tmax = smax * sl2;
+          const bool had_ref = m_ref != -INFINITY;
+          const bool grow = tmax > m_ref + kRestartThreshold;
+          if (grow) m_ref = tmax;
+          redo |= __builtin_amdgcn_ballot_w64(grow && had_ref) != 0;
+        };
+        // bf16 cache, every pair of the wave with a reference: the weights are
+        // taken against it right away, and the tile max only when a lane's
+        // sum of rounded weights reaches 2^16 (a weight above 2^16 rounds to at
+        // least 2^16, so no jump goes unseen); the rule applied is the same
+        const bool fast = !kFp8 && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) == 0;
+        if (!fast) ref_update();
         // exp2 of masked scores is 0; an unset reference (no visible key yet) is taken as 0
         const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
         float psum = 0.f;
@@ -429,6 +435,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
             pk[i / 2] = *(const uint32_t*)&pb2;
           }
         }
+        if (fast && __builtin_amdgcn_ballot_w64(psum >= 65536.f) != 0) ref_update();
         l_part += psum;
         const uint32_t pw = p_wr + (uint32_t)(T & 1) * kPBufBytes;
 #pragma unroll
