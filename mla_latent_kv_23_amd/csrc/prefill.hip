@@ -36,10 +36,14 @@
 //     over the codes are multiplied by the token's scale before the rounding
 //     (W (code * scale) = scale * (W code)).
 //  3. prefill_attn_kernel: causal flash attention per (sequence, head, block of
-//     128 queries), one wave per 32 queries:
+//     128 queries), one wave per 32 queries; a work-group takes two query
+//     blocks of its sequence, j and nq - 1 - j, so that every work-group has
+//     the same causal work:
 //     * key blocks of 64 rows [k_C | k_R | v] (640 B) are staged in LDS with
 //       direct-to-LDS loads, two stages, in 1 KB blocks of 8 rows x 8 chunks
 //       with the chunk XOR-swizzled by the row (the decode kernel's layout);
+//       the next block's ten loads per wave go out one by one between the QK
+//       MFMAs of the current one;
 //     * S^T = K Q^T on MFMA 32x32x16 (queries in registers as the B operand);
 //       the A operand reads key rows in the order that makes S^T come out in
 //       the B-operand layout of PV (row R holds key R with bits 2 and 3
@@ -199,7 +203,24 @@ __device__ __forceinline__ void dma16(const void* src, uint32_t voff, uint32_t m
                : [v] "v"(voff), [s] "s"(sv), [m] "s"(m)
                : "memory", "m0");
 }
+// the same load with no memory clobber, so that it can sit between the LDS reads
+// and MFMAs of a block: the stage it writes is read by no one before the next
+// barrier, which is itself ordered after it (both are volatile asm)
+__device__ __forceinline__ void dma16_free(uint64_t sv, uint32_t voff, uint32_t m) {
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[v], %[s]"
+               :
+               : [v] "v"(voff), [s] "s"(sv), [m] "s"(m)
+               : "m0");
+}
 #pragma clang diagnostic pop
+
+// a wave-uniform address in scalar registers
+__device__ __forceinline__ uint64_t sgpr_addr(const void* p) {
+  const uint64_t a = (uint64_t)(uintptr_t)p;
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+  return ((uint64_t)hi << 32) | (uint64_t)lo;
+}
 
 // ---------------------------------------------------------------- 2. decompression
 
@@ -369,249 +390,278 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int H = a.H;
 
-  // work order: all query blocks of one (sequence, head) on one XCD, the
-  // heaviest (last) block first, so that the head's keys stay in its L2
-  const int total = a.n_seq * H * a.n_qblk;
-  const int k = xcd_unit(blockIdx.x, total);
-  const int pair = k / a.n_qblk, qb = a.n_qblk - 1 - k % a.n_qblk;
+  // work order: work-group j of a (sequence, head) takes its query blocks
+  // nq - 1 - j and then j (nq = the sequence's own block count), so that under
+  // the causal mask every work-group of a sequence has the same number of key
+  // blocks and no long block is left alone at the end of the launch; all the
+  // work-groups of one (sequence, head) run on one XCD, so the head's keys stay
+  // in its L2
+  const int n_slot = (a.n_qblk + 1) / 2;
+  const int k = xcd_unit(blockIdx.x, a.n_seq * H * n_slot);
+  const int pair = k / n_slot, j = k % n_slot;
   const int b = pair / H, s = pair % H;
   const int cu0 = a.cu_q[b], Lq = a.cu_q[b + 1] - cu0;
-  const int ck0 = a.cu_k[b], L = a.cu_k[b + 1] - ck0;  // L keys; query j sits at position off + j
+  const int ck0 = a.cu_k[b], L = a.cu_k[b + 1] - ck0;  // L keys; query i sits at position off + i
   const int off = L - Lq;
-  const int q0 = qb * kQBlk;
-  if (q0 >= Lq) return;
-  const int qw = q0 + 32 * wave;                       // this wave's first query
-  const int q = min(qw + lr, Lq - 1);                  // this lane's query (past the end: a copy of the last)
-
-  // queries: B operand, query q, dims 16k + 8 half .. +7 (k < 8: q_nope, else the rotated part)
-  f16x8 qf[kQk];
-  {
-    const bf16x8* qn = (const bf16x8*)(a.q_nope + ((int64_t)(cu0 + q) * H + s) * kPfDn) + half;
-    // the RoPE part, rotated here: k-step kk holds pairs 8 (kk - 8) + 4 half .. +3
-    const bf16x8* qr = (const bf16x8*)(a.q_rope + ((int64_t)(cu0 + q) * H + s) * kPfDr) + half;
-    const f32x4* csq = (const f32x4*)(a.cs + (int64_t)(cu0 + q) * kPfDr) + 2 * half;   // 2 pairs per f32x4
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const bf16x8 raw = qn[2 * kk];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) qf[kk][e] = (_Float16)(float)raw[e];   // exact
+  const int nq = (Lq + kQBlk - 1) / kQBlk;
+  if (j >= (nq + 1) / 2) return;
+#pragma unroll 1
+  for (int pass = 0; pass < 2; ++pass) {
+    const int qb = pass == 0 ? nq - 1 - j : j;
+    if (pass == 1) {
+      if (qb == nq - 1 - j) break;             // the middle block of an odd count: taken once
+      lds_barrier();                           // every wave is done with the stages of the first block
     }
+    const int q0 = qb * kQBlk;
+    const int qw = q0 + 32 * wave;                       // this wave's first query
+    const int q = min(qw + lr, Lq - 1);                  // this lane's query (past the end: a copy of the last)
+
+    // queries: B operand, query q, dims 16k + 8 half .. +7 (k < 8: q_nope, else the rotated part)
+    f16x8 qf[kQk];
+    {
+      const bf16x8* qn = (const bf16x8*)(a.q_nope + ((int64_t)(cu0 + q) * H + s) * kPfDn) + half;
+      // the RoPE part, rotated here: k-step kk holds pairs 8 (kk - 8) + 4 half .. +3
+      const bf16x8* qr = (const bf16x8*)(a.q_rope + ((int64_t)(cu0 + q) * H + s) * kPfDr) + half;
+      const f32x4* csq = (const f32x4*)(a.cs + (int64_t)(cu0 + q) * kPfDr) + 2 * half;   // 2 pairs per f32x4
 #pragma unroll
-    for (int kk = 8; kk < kQk; ++kk) {
-      const bf16x8 raw = qr[2 * (kk - 8)];
-      const f32x4 c01 = csq[4 * (kk - 8)], c23 = csq[4 * (kk - 8) + 1];
-      const float cv[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
-      f16x8 rot;
+      for (int kk = 0; kk < 8; ++kk) {
+        const bf16x8 raw = qn[2 * kk];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        // the RoPE rule of the absorb: the pair formed in fp64, rounded to fp32, then to the fp16 operand
-        float ox, oy;
-        rope_pair((float)raw[2 * e], (float)raw[2 * e + 1], cv[2 * e], cv[2 * e + 1], &ox, &oy);
-        rot[2 * e] = (_Float16)ox;
-        rot[2 * e + 1] = (_Float16)oy;
+        for (int e = 0; e < 8; ++e) qf[kk][e] = (_Float16)(float)raw[e];   // exact
       }
-      qf[kk] = rot;
-    }
-  }
-  __builtin_amdgcn_s_waitcnt(0);             // queries resident before any stage load is queued
-
-  // per-lane LDS offsets.  K (A operand of QK): row R = lr of a 32-key half reads
-  // key R with bits 2 and 3 swapped; k-step kk reads chunk 2 kk + half.
-  const int kr_row = (lr & ~12) | ((lr & 4) << 1) | ((lr & 8) >> 1);
-  uint32_t kb[4];
 #pragma unroll
-  for (int m = 0; m < 4; ++m) kb[m] = stage_off(kr_row, 2 * m + half);
-  // V^T (A operand of PV), dims 32 db + lane % 32, keys 16 ks + 8 half .. +7, as
-  // two transpose reads (4 keys each); base by (db & 1, hh), + (db >> 1) KB, + 10 KB ks
-  uint32_t vb[4];
-  {
-    const int gi = lane >> 4, sp = lane & 15;
-    const int rr0 = 8 * (gi >> 1) + (sp >> 2);
+      for (int kk = 8; kk < kQk; ++kk) {
+        const bf16x8 raw = qr[2 * (kk - 8)];
+        const f32x4 c01 = csq[4 * (kk - 8)], c23 = csq[4 * (kk - 8) + 1];
+        const float cv[8] = {c01[0], c01[1], c01[2], c01[3], c23[0], c23[1], c23[2], c23[3]};
+        f16x8 rot;
 #pragma unroll
-    for (int x = 0; x < 2; ++x)
-#pragma unroll
-      for (int hh = 0; hh < 2; ++hh) {
-        const int vdim = 32 * x + 16 * (gi & 1) + 4 * (sp & 3);
-        vb[x * 2 + hh] = stage_off(rr0 + 4 * hh, 24 + (vdim >> 3)) + ((vdim & 7) << 1);
+        for (int e = 0; e < 4; ++e) {
+          // the RoPE rule of the absorb: the pair formed in fp64, rounded to fp32, then to the fp16 operand
+          float ox, oy;
+          rope_pair((float)raw[2 * e], (float)raw[2 * e + 1], cv[2 * e], cv[2 * e + 1], &ox, &oy);
+          rot[2 * e] = (_Float16)ox;
+          rot[2 * e + 1] = (_Float16)oy;
+        }
+        qf[kk] = rot;
       }
-  }
-
-  // stage loads: wave w brings rows 16w .. 16w+15 of the block, five 1 KB
-  // blocks per 8 rows; lane l (row position l/8): row 16w + 8g + ((l/8) ^ g),
-  // logical chunk 8cb + ((l % 8) ^ swz(row % 8))
-  const int last_key = min(L, off + q0 + kQBlk) - 1;
-  const int n_kblk = last_key / kKBlk + 1;
-  auto load_stage = [&](int kbk, int par) {   // par = kbk % 2 (a constant where the caller knows it)
-    const uint32_t dst = (uint32_t)(uintptr_t)(lds + par * kStage);
-    const int key0 = kbk * kKBlk;
-    const int64_t row0 = ck0 + key0;
-#pragma unroll
-    for (int g = 0; g < 2; ++g) {
-      const int rho = (lane >> 3) ^ g;           // the row (of 8) at position lane / 8 (rpos of row 8(2w + g) + rho)
-      const int r = 16 * wave + 8 * g + rho;
-      const int re = key0 + r < L ? r : 0;       // past the end: the block's first key (finite, masked)
-      const int sl = (lane & 7) ^ swz(rho);
-      const uint32_t m0 = dst + (uint32_t)(((2 * wave + g) * kRowBlocks) * 1024);
-      // k_C chunks 0..15 and v chunks 24..39 (per-head rows of 256 B), k_R chunks 16..23 (128 B rows)
-      const uint32_t hoff = (uint32_t)((re * H + s) * (kPfDn * 2)) + 16 * sl;
-      dma16(a.k_c + row0 * H * kPfDn, hoff, m0);
-      dma16(a.k_c + row0 * H * kPfDn, hoff + 128, m0 + 1024);
-      dma16(a.k_rot + row0 * kPfDr, (uint32_t)(re * (kPfDr * 2)) + 16 * sl, m0 + 2048);
-      dma16(a.v + row0 * H * kPfDv, hoff, m0 + 3072);
-      dma16(a.v + row0 * H * kPfDv, hoff + 128, m0 + 4096);
     }
-  };
+    __builtin_amdgcn_s_waitcnt(0);             // queries resident before any stage load is queued
 
-  const float sl2 = a.scale_log2;
-  float m_ref = -INFINITY, l_part = 0.f;
-  f32x16 o[4];
+    // per-lane LDS offsets.  K (A operand of QK): row R = lr of a 32-key half reads
+    // key R with bits 2 and 3 swapped; k-step kk reads chunk 2 kk + half.
+    const int kr_row = (lr & ~12) | ((lr & 4) << 1) | ((lr & 8) >> 1);
+    uint32_t kb[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = f32x16{};
-
-  // one key block; par = kbk % 2 is a constant in each of the two calls below, so the stage
-  // base folds into the LDS instructions' immediate offsets
-  auto block = [&](int kbk, int par) {
-    wait_vmcnt<0>();                         // this wave's share of stage kbk has landed
-    lds_barrier();                           // ... and everyone's; stage kbk-1 is free
-    if (kbk + 1 < n_kblk) load_stage(kbk + 1, par ^ 1);
-    const uint32_t tb = (uint32_t)(uintptr_t)(lds + par * kStage);
-
-    // ---- S^T for the two 32-key halves
-    f32x16 sacc[2] = {f32x16{}, f32x16{}};
+    for (int m = 0; m < 4; ++m) kb[m] = stage_off(kr_row, 2 * m + half);
+    // V^T (A operand of PV), dims 32 db + lane % 32, keys 16 ks + 8 half .. +7, as
+    // two transpose reads (4 keys each); base by (db & 1, hh), + (db >> 1) KB, + 10 KB ks
+    uint32_t vb[4];
+    {
+      const int gi = lane >> 4, sp = lane & 15;
+      const int rr0 = 8 * (gi >> 1) + (sp >> 2);
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
+      for (int x = 0; x < 2; ++x)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int vdim = 32 * x + 16 * (gi & 1) + 4 * (sp & 3);
+          vb[x * 2 + hh] = stage_off(rr0 + 4 * hh, 24 + (vdim >> 3)) + ((vdim & 7) << 1);
+        }
+    }
+
+    // stage loads: wave w brings rows 16w .. 16w+15 of the block, five 1 KB
+    // blocks per 8 rows; lane l (row position l/8): row 16w + 8g + ((l/8) ^ g),
+    // logical chunk 8cb + ((l % 8) ^ swz(row % 8))
+    const int last_key = min(L, off + q0 + kQBlk) - 1;
+    const int n_kblk = last_key / kKBlk + 1;
+    // A block's loads are prepared once (stage_prep: scalar sources, per-lane
+    // offsets) and issued one at a time (stage_issue) between the QK MFMAs of the
+    // block before, so that no wave stalls on ten load issues in a row.
+    struct StageLd {
+      uint64_t kc, kr, vv;          // k_C, k_R and v of the block's first key (wave-uniform)
+      uint32_t off[2], roff[2], m0; // per-lane offsets of the k_C / v rows and the k_R row; LDS base
+    };
+    auto stage_prep = [&](int kbk, int par) -> StageLd {
+      StageLd S;
+      const int key0 = kbk * kKBlk;
+      const int64_t row0 = ck0 + key0;
+      S.kc = sgpr_addr(a.k_c + row0 * H * kPfDn);
+      S.kr = sgpr_addr(a.k_rot + row0 * kPfDr);
+      S.vv = sgpr_addr(a.v + row0 * H * kPfDv);
+      S.m0 = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds + par * kStage) +
+                                                      (uint32_t)(2 * wave * kRowBlocks * 1024));
+#pragma unroll
+      for (int g = 0; g < 2; ++g) {
+        const int rho = (lane >> 3) ^ g;           // the row (of 8) at position lane / 8 (rpos of row 8(2w + g) + rho)
+        const int r = 16 * wave + 8 * g + rho;
+        const int re = key0 + r < L ? r : 0;       // past the end: the block's first key (finite, masked)
+        const int sl = (lane & 7) ^ swz(rho);
+        // k_C chunks 0..15 and v chunks 24..39 (per-head rows of 256 B), k_R chunks 16..23 (128 B rows)
+        S.off[g] = (uint32_t)((re * H + s) * (kPfDn * 2)) + 16 * sl;
+        S.roff[g] = (uint32_t)(re * (kPfDr * 2)) + 16 * sl;
+      }
+      return S;
+    };
+    // load i = 5 g + j (a constant after unrolling): 1 KB block j of row group g
+    auto stage_issue = [&](const StageLd& S, int i) {
+      const int g = i / 5, j = i % 5;
+      const uint32_t m = S.m0 + (uint32_t)((g * kRowBlocks + j) * 1024);
+      if (j == 0) dma16_free(S.kc, S.off[g], m);
+      else if (j == 1) dma16_free(S.kc, S.off[g] + 128, m);
+      else if (j == 2) dma16_free(S.kr, S.roff[g], m);
+      else if (j == 3) dma16_free(S.vv, S.off[g], m);
+      else dma16_free(S.vv, S.off[g] + 128, m);
+    };
+
+    const float sl2 = a.scale_log2;
+    float m_ref = -INFINITY, l_part = 0.f;
+    f32x16 o[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) o[i] = f32x16{};
+
+    // one key block; par = kbk % 2 is a constant in each of the two calls below, so the stage
+    // base folds into the LDS instructions' immediate offsets
+    auto block = [&](int kbk, int par) {
+      wait_vmcnt<0>();                         // this wave's share of stage kbk has landed
+      lds_barrier();                           // ... and everyone's; stage kbk-1 is free
+      // the last block loads itself again into the free stage (never read), so that
+      // the ten loads below need no branch
+      const StageLd ld = stage_prep(min(kbk + 1, n_kblk - 1), par ^ 1);
+      const uint32_t tb = (uint32_t)(uintptr_t)(lds + par * kStage);
+
+      // ---- S^T for the two 32-key halves: one stream of 24 MFMAs with kKf K reads
+      // in flight, the next block's ten loads after every other MFMA
+      f32x16 sacc[2];
+      auto kaddr = [&](int f) {
+        const int t = f / kQk, kk = f % kQk;
+        return tb + kb[kk % 4] + 1024 * (kk / 4) + 20480 * t;
+      };
       f16x8 kf[kKf];
 #pragma unroll
-      for (int kk = 0; kk < kKf; ++kk) kf[kk] = *(const lds_f16x8*)(uintptr_t)(tb + kb[kk % 4] + 1024 * (kk / 4) + 20480 * t);
+      for (int f = 0; f < kKf; ++f) kf[f] = *(const lds_f16x8*)(uintptr_t)kaddr(f);
 #pragma unroll
-      for (int kk = 0; kk < kQk; ++kk) {
-        const f16x8 cur = kf[kk % kKf];
-        if (kk + kKf < kQk)
-          kf[kk % kKf] = *(const lds_f16x8*)(uintptr_t)(tb + kb[kk % 4] + 1024 * ((kk + kKf) / 4) + 20480 * t);
-        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur, qf[kk], sacc[t], 0, 0, 0);
+      for (int f = 0; f < 2 * kQk; ++f) {
+        const f16x8 cur = kf[f % kKf];
+        if (f + kKf < 2 * kQk) kf[f % kKf] = *(const lds_f16x8*)(uintptr_t)kaddr(f + kKf);
+        const int t = f / kQk, kk = f % kQk;
+        sacc[t] = __builtin_amdgcn_mfma_f32_32x32x16_f16(cur, qf[kk], kk == 0 ? f32x16{} : sacc[t], 0, 0, 0);
+        if ((f & 1) && f / 2 < 10) stage_issue(ld, f / 2);
+        __builtin_amdgcn_sched_barrier(0);
       }
-    }
-    // issue order per half: kKf K reads, then (MFMA, read) pairs, then the last kKf MFMAs, so that kKf
-    // reads stay in flight ahead of the MFMA chain (left to itself the compiler sinks each read to its
-    // MFMA and waits on it)
-#pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      __builtin_amdgcn_sched_group_barrier(0x100, kKf, 0);
-#pragma unroll
-      for (int kk = 0; kk < kQk - kKf; ++kk) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
-      }
-      __builtin_amdgcn_sched_group_barrier(0x008, kKf, 0);
-    }
 
-    // ---- softmax: lane holds query q, keys 64 kbk + 32 t + 16 (i / 8) + 8 half + i % 8
-    float sv[2][16];
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int i = 0; i < 16; ++i) sv[t][i] = sacc[t][i];
-    if (kbk * kKBlk + kKBlk - 1 > off + qw) {   // a block reaching this wave's diagonal (wave-uniform)
+      // ---- softmax: lane holds query q, keys 64 kbk + 32 t + 16 (i / 8) + 8 half + i % 8
+      float sv[2][16];
 #pragma unroll
       for (int t = 0; t < 2; ++t)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = kbk * kKBlk + 32 * t + 16 * (i / 8) + 8 * half + (i % 8);
-          sv[t][i] = key <= off + q ? sv[t][i] : -INFINITY;
+        for (int i = 0; i < 16; ++i) sv[t][i] = sacc[t][i];
+      if (kbk * kKBlk + kKBlk - 1 > off + qw) {   // a block reaching this wave's diagonal (wave-uniform)
+#pragma unroll
+        for (int t = 0; t < 2; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = kbk * kKBlk + 32 * t + 16 * (i / 8) + 8 * half + (i % 8);
+            sv[t][i] = key <= off + q ? sv[t][i] : -INFINITY;
+          }
+      }
+      float bmax = sv[0][0];
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, sv[t][i]);
+      {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
+        bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      }
+      const float tmax = bmax * sl2;
+      const bool raise = tmax > m_ref + 8.0f;  // also when nothing is accumulated yet (m_ref = -inf)
+      if (__builtin_amdgcn_ballot_w64(raise) != 0) {
+        const float m_new = raise ? tmax : m_ref;
+        const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] *= alpha;
+        l_part *= alpha;
+        m_ref = m_new;
+      }
+      const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
+      f16x8 pb[4];                             // B operand of PV k-step 2t + j: regs 8j .. 8j+7 of half t
+      const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+      float psum = 0.f;
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          f16x8 v8;
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const f32x2 pv = {__builtin_amdgcn_exp2f(fmaf(sv[t][8 * j + e], sl2, neg_m)),
+                              __builtin_amdgcn_exp2f(fmaf(sv[t][8 * j + e + 1], sl2, neg_m))};
+            const f16x2 p2 = __builtin_convertvector(pv, f16x2);   // round to nearest even; weights <= 2^8
+            psum = __builtin_amdgcn_fdot2(p2, ones, psum, false);   // sum of the rounded weights
+            v8[e] = p2[0];
+            v8[e + 1] = p2[1];
+          }
+          pb[2 * t + j] = v8;
         }
-    }
-    float bmax = sv[0][0];
+      l_part += psum;
+
+      // ---- O^T += V^T P^T: 4 dim blocks x 4 key steps
 #pragma unroll
-    for (int t = 0; t < 2; ++t)
+      for (int ks = 0; ks < 4; ++ks)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) bmax = fmaxf(bmax, sv[t][i]);
+        for (int db = 0; db < 4; ++db) {
+          const uint32_t base = tb + 10240 * ks + 1024 * (db >> 1);
+          const f16x4 lo = __builtin_bit_cast(
+              f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + vb[(db & 1) * 2])));
+          const f16x4 hi = __builtin_bit_cast(
+              f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + vb[(db & 1) * 2 + 1])));
+          const f16x8 vf = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pb[ks], o[db], 0, 0, 0);
+        }
+    };
     {
-      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(bmax), __float_as_uint(bmax), false, false);
-      bmax = fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1]));
+      const StageLd ld0 = stage_prep(0, 0);
+#pragma unroll
+      for (int i = 0; i < 10; ++i) stage_issue(ld0, i);
     }
-    const float tmax = bmax * sl2;
-    const bool raise = tmax > m_ref + 8.0f;  // also when nothing is accumulated yet (m_ref = -inf)
-    if (__builtin_amdgcn_ballot_w64(raise) != 0) {
-      const float m_new = raise ? tmax : m_ref;
-      const float alpha = m_ref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_ref - m_new);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] *= alpha;
-      l_part *= alpha;
-      m_ref = m_new;
+    for (int kbk = 0; kbk < n_kblk; kbk += 2) {
+      block(kbk, 0);
+      if (kbk + 1 < n_kblk) block(kbk + 1, 1);
     }
-    const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
-    f16x8 pb[4];                             // B operand of PV k-step 2t + j: regs 8j .. 8j+7 of half t
-    const f16x2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-    float psum = 0.f;
-#pragma unroll
-    for (int t = 0; t < 2; ++t)
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        f16x8 v8;
-#pragma unroll
-        for (int e = 0; e < 8; e += 2) {
-          const f32x2 pv = {__builtin_amdgcn_exp2f(fmaf(sv[t][8 * j + e], sl2, neg_m)),
-                            __builtin_amdgcn_exp2f(fmaf(sv[t][8 * j + e + 1], sl2, neg_m))};
-          const f16x2 p2 = __builtin_convertvector(pv, f16x2);   // round to nearest even; weights <= 2^8
-          psum = __builtin_amdgcn_fdot2(p2, ones, psum, false);   // sum of the rounded weights
-          v8[e] = p2[0];
-          v8[e + 1] = p2[1];
-        }
-        pb[2 * t + j] = v8;
-      }
-    l_part += psum;
 
-    // ---- O^T += V^T P^T: 4 dim blocks x 4 key steps
+    wait_vmcnt<0>();                           // the last block's extra loads have landed
+    // ---- normalise and store: O^T tile db, lane holds query qw + lr, dims 32 db + 8 (i / 4) + 4 half + i % 4
+    float l_tot;
+    {
+      const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
+      l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+    }
+    if (qw + lr < Lq) {
+      const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
+      const int64_t at = ((int64_t)(cu0 + qw + lr) * H + s) * kPfDv + 4 * half;
+      uint16_t* dst = a.out + at;
+      if (a.gate) {
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+        for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        const uint32_t base = tb + 10240 * ks + 1024 * (db >> 1);
-        const f16x4 lo = __builtin_bit_cast(
-            f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + vb[(db & 1) * 2])));
-        const f16x4 hi = __builtin_bit_cast(
-            f16x4, __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(uintptr_t)(base + vb[(db & 1) * 2 + 1])));
-        const f16x8 vf = f16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pb[ks], o[db], 0, 0, 0);
+          for (int g = 0; g < 4; ++g) {
+            const u32x2 g4 = *(const u32x2*)(a.gate + at + 32 * db + 8 * g);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t w2 = g4[e >> 1];
+              o[db][4 * g + e] *= sigmoid_f32(__uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16)));
+            }
+          }
       }
-  };
-  load_stage(0, 0);
-  for (int kbk = 0; kbk < n_kblk; kbk += 2) {
-    block(kbk, 0);
-    if (kbk + 1 < n_kblk) block(kbk + 1, 1);
-  }
-
-  // ---- normalise and store: O^T tile db, lane holds query qw + lr, dims 32 db + 8 (i / 4) + 4 half + i % 4
-  float l_tot;
-  {
-    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(l_part), __float_as_uint(l_part), false, false);
-    l_tot = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
-  }
-  if (qw + lr < Lq) {
-    const float inv = l_tot > 0.f ? 1.0f / l_tot : 0.f;
-    const int64_t at = ((int64_t)(cu0 + qw + lr) * H + s) * kPfDv + 4 * half;
-    uint16_t* dst = a.out + at;
-    if (a.gate) {
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const u32x2 g4 = *(const u32x2*)(a.gate + at + 32 * db + 8 * g);
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const uint32_t w2 = g4[e >> 1];
-            o[db][4 * g + e] *= sigmoid_f32(__uint_as_float((e & 1) ? (w2 & 0xffff0000u) : (w2 << 16)));
-          }
-        }
+        for (int g = 0; g < 4; ++g)
+          *(u32x2*)(dst + 32 * db + 8 * g) =
+              pf_pack4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
+      if (half == 0)
+        a.lse[(int64_t)(cu0 + qw + lr) * H + s] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
     }
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int g = 0; g < 4; ++g)
-        *(u32x2*)(dst + 32 * db + 8 * g) =
-            pf_pack4(o[db][4 * g] * inv, o[db][4 * g + 1] * inv, o[db][4 * g + 2] * inv, o[db][4 * g + 3] * inv);
-    if (half == 0)
-      a.lse[(int64_t)(cu0 + qw + lr) * H + s] = l_tot > 0.f ? (m_ref + log2f(l_tot)) * 0.69314718055994530942f : -INFINITY;
   }
 }
 
@@ -682,7 +732,7 @@ void launch_attention(const mla_dims& d, int32_t n_seq, const int32_t* cu_q, con
   a.H = d.n_heads;
   a.n_qblk = (max_q + kQBlk - 1) / kQBlk;
   a.scale_log2 = d.softmax_scale * 1.4426950408889634f;
-  const int64_t grid = (int64_t)n_seq * d.n_heads * a.n_qblk;
+  const int64_t grid = (int64_t)n_seq * d.n_heads * ((a.n_qblk + 1) / 2);
   hipLaunchKernelGGL(prefill_attn_kernel, dim3((unsigned)grid), dim3(256), 0, st, a);
 }
 }  // namespace
