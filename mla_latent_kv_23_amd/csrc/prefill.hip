@@ -440,6 +440,9 @@ __global__ void __launch_bounds__(256, 2) prefill_attn_kernel(PrefillArgs a) {
           // the RoPE rule of the absorb: the pair formed in fp64, rounded to fp32, then to the fp16 operand
           float ox, oy;
           rope_pair((float)raw[2 * e], (float)raw[2 * e + 1], cv[2 * e], cv[2 * e + 1], &ox, &oy);
+          // opaque: the compiler would otherwise fuse the two roundings into one float64 -> fp16
+          // conversion, in software
+          asm("" : "+v"(ox), "+v"(oy));
           rot[2 * e] = (_Float16)ox;
           rot[2 * e + 1] = (_Float16)oy;
         }
