@@ -325,6 +325,29 @@ mla_status mla_up_proj_gated(const mla_dims* dims, int32_t n_tok, const void* o_
                              const void* w_uv, const void* gate, void* out, mla_stream_t stream);
 
 /*
+ * mla_combine_up_proj -- mla_combine followed by mla_up_proj (or
+ * mla_up_proj_gated with a gate) on the rows of mla_decode, in one call:
+ * the split partials are merged by log-sum-exp as in mla_combine and the
+ * merged latent rows go through W_UV as in mla_up_proj ("Transformer升级之路：
+ * 21、MLA好在哪里？（下）", 双重投影, decoding column), without the merged rows
+ * making a round trip through memory.  Arguments: those of mla_combine for
+ * the decode that left the workspace, then w_uv [H, d_v, d_c], gate
+ * [n_seq * q_per_seq, H, d_v] or null, out [n_seq * q_per_seq, H, d_v].
+ * o_latent is read for the rows mla_decode finished itself (a sequence that
+ * lies inside one work unit, or has no token); the merged rows are written
+ * back to it only when write_latent != 0 (otherwise those rows of o_latent are
+ * left as mla_decode left them).  lse is written for the merged rows as
+ * mla_combine writes it.  The results are bit-identical to the two calls.
+ * Errors as mla_combine and mla_up_proj, checked before any launch.
+ */
+mla_status mla_combine_up_proj(const mla_dims* dims, int32_t n_seq, int32_t q_per_seq,
+                               const int32_t* cache_seqlens, int32_t max_blocks,
+                               int32_t num_splits, const void* workspace,
+                               size_t workspace_bytes, void* o_latent, int32_t write_latent,
+                               const void* w_uv, const void* gate, void* out, float* lse,
+                               mla_stream_t stream);
+
+/*
  * mla_prefill -- causal attention over whole prompts in the MHA form
  * ("Transformer升级之路：21、MLA好在哪里？（下）", 双重投影, training/prefill
  * column: each head gets its own key k = [c W_k^(s) | k_R] and value

@@ -68,6 +68,7 @@ SIGNATURES = {
     "mla_absorb_append": (ctypes.c_int, [_DP, _I32, _P, _P, _P, _P, _P, _I32, _P, _P, _P, _P, _P, _I32, _I32, _P,
                                          ctypes.c_int64, _P]),
     "mla_prefill_workspace_bytes": (_SZ, [_DP, _I32]),
+    "mla_combine_up_proj": (ctypes.c_int, [_DP, _I32, _I32, _P, _I32, _I32, _P, _SZ, _P, _I32, _P, _P, _P, _P, _P]),
     "mla_prefill": (ctypes.c_int, [_DP, _I32, _P, _I32, _I32, _P, _P, _P, _P, _P, _P, _P, _P, _SZ, _P, _P, _P]),
     "mla_prefill_paged_workspace_bytes": (_SZ, [_DP, _I32, _I32]),
     "mla_project_down_workspace_bytes": (_SZ, [_DP, _I32, _I32, _I32]),
@@ -228,6 +229,24 @@ def combine(d: Dims, seqlens, max_blocks: int, workspace, o_latent, lse, num_spl
         _ptr(workspace, "workspace"), ws_bytes, _ptr(o_latent, "o_latent", at), _ptr(lse, "lse", torch.float32),
         _stream(stream)))
     return o_latent, lse
+
+
+def combine_up_proj(d: Dims, seqlens, max_blocks: int, workspace, o_latent, lse, w_uv, out=None, num_splits: int = 0,
+                    gate=None, write_latent: bool = True, stream=None):
+    """combine followed by up_proj (gated with `gate`) in one call: o_latent [n_seq, q_per_seq, H, d_c] as left by
+    decode (the merged rows written back only with write_latent), lse [n_seq, q_per_seq, H];
+    returns out [n_seq * q_per_seq, H, d_v]."""
+    at = act_torch_dtype(d)
+    n_seq, q_per_seq = o_latent.shape[0], o_latent.shape[1]
+    if out is None:
+        out = torch.empty((n_seq * q_per_seq, d.n_heads, d.d_v), dtype=at, device=o_latent.device)
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("mla_combine_up_proj", load_library().mla_combine_up_proj(
+        ctypes.byref(d), n_seq, q_per_seq, _ptr(seqlens, "seqlens", torch.int32), max_blocks, num_splits,
+        _ptr(workspace, "workspace"), ws_bytes, _ptr(o_latent, "o_latent", at), 1 if write_latent else 0,
+        _ptr(w_uv, "w_uv", at), _ptr(gate, "gate", at), _ptr(out, "out", at), _ptr(lse, "lse", torch.float32),
+        _stream(stream)))
+    return out
 
 
 def absorb_append(d: Dims, q_nope, q_rope, q_pos, w_uk, c_kv, k_rope, seq_id, pos, block_table, pool, q_abs=None,

@@ -356,6 +356,30 @@ mla_status mla_up_proj_gated(const mla_dims* d, int32_t n_tok, const void* o_lat
   return up_proj_common(d, n_tok, o_latent, w_uv, gate, out, stream);
 }
 
+mla_status mla_combine_up_proj(const mla_dims* d, int32_t n_seq, int32_t q_per_seq, const int32_t* cache_seqlens,
+                               int32_t max_blocks, int32_t num_splits, const void* workspace, size_t workspace_bytes,
+                               void* o_latent, int32_t write_latent, const void* w_uv, const void* gate, void* out,
+                               float* lse, mla_stream_t stream) {
+  const mla_status s = check_decode_args(d, n_seq, q_per_seq, max_blocks, num_splits);
+  if (s != MLA_OK) return s;
+  if (!cache_seqlens || !o_latent || !lse || !w_uv || !out) return MLA_ERR_INVALID_ARG;
+  const int32_t n_tok = n_seq * q_per_seq;
+  if (n_tok > 2147483647 / d->n_heads) return MLA_ERR_UNSUPPORTED;
+  const DecodePlan plan = make_plan(*d, n_seq, q_per_seq, max_blocks, num_splits);
+  if (plan.needs_combine && (!workspace || workspace_bytes < plan.ws_bytes)) return MLA_ERR_WORKSPACE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (plan.needs_combine && combine_up_proj_applies(*d, plan) && aligned16(o_latent) && aligned16(w_uv) &&
+      aligned16(out) && aligned16(workspace) && (!gate || aligned16(gate)))
+    return launch_combine_up_proj(*d, plan, n_seq, q_per_seq, cache_seqlens, workspace, o_latent,
+                                  write_latent ? o_latent : nullptr, w_uv, gate, out, lse, st);
+  // otherwise the two calls (their kernels), the merged rows through o_latent
+  if (plan.needs_combine) {
+    const mla_status c = launch_combine(*d, plan, n_seq, q_per_seq, cache_seqlens, workspace, o_latent, lse, st);
+    if (c != MLA_OK) return c;
+  }
+  return up_proj_common(d, n_tok, o_latent, w_uv, gate, out, stream);
+}
+
 size_t mla_prefill_workspace_bytes(const mla_dims* d, int32_t total_tokens) {
   if (dims_supported(d) != MLA_OK || !prefill_supported(*d) || total_tokens < 0) return 0;
   return prefill_workspace_bytes(*d, total_tokens);

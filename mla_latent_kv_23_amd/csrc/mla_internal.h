@@ -73,6 +73,10 @@ mla_status launch_combine(const mla_dims& d, const DecodePlan& plan, int32_t n_s
                           const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st);
 mla_status launch_combine_stream(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
                                  const int32_t* seqlens, const void* ws, void* o_lat, float* lse, hipStream_t st);
+bool combine_up_proj_applies(const mla_dims& d, const DecodePlan& plan);
+mla_status launch_combine_up_proj(const mla_dims& d, const DecodePlan& plan, int32_t n_seq, int32_t q_per_seq,
+                                  const int32_t* seqlens, const void* ws, const void* o_lat, void* o_lat_out,
+                                  const void* w_uv, const void* gate, void* out, float* lse, hipStream_t st);
 bool prefill_supported(const mla_dims& d);
 size_t prefill_workspace_bytes(const mla_dims& d, int64_t total_tokens);
 size_t prefill_paged_workspace_bytes(const mla_dims& d, int64_t total_q, int64_t total_k);

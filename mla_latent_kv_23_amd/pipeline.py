@@ -1,6 +1,8 @@
-"""One MLA decode step for one layer, as the five library calls in order:
-absorb the query, append the new tokens to the paged cache, attend over the
-latent cache, merge the key splits, project back to per-head outputs.
+"""One MLA decode step for one layer, as the library calls in order: absorb
+the query and append the new tokens to the paged cache (one call), attend over
+the latent cache, then merge the key splits and project back to per-head
+outputs (one call, mla_combine_up_proj, when the attention was split; else the
+up-projection alone).
 `run_from_hidden` starts one step earlier, from the hidden states: the
 down-projections with the append, and the query up-projection with the
 absorb, replace the first two calls.
@@ -17,8 +19,11 @@ from . import binding as B
 
 class DecodeStep:
     def __init__(self, dims: B.Dims, n_seq: int, q_per_seq: int, max_blocks: int, num_splits: int = 0,
-                 device="cuda"):
+                 device="cuda", keep_latent: bool = True):
+        """keep_latent: the merged latent rows are written to o_latent (returned by run);
+        without it o_latent holds only the rows decode finished itself."""
         self.d, self.n_seq, self.q_per_seq = dims, n_seq, q_per_seq
+        self.keep_latent = keep_latent
         self.max_blocks, self.num_splits = max_blocks, num_splits
         at = B.act_torch_dtype(dims)
         n_tok = n_seq * q_per_seq
@@ -30,6 +35,21 @@ class DecodeStep:
         ws = B.decode_workspace_bytes(dims, n_seq, q_per_seq, max_blocks, num_splits)
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
         self.needs_combine = B.decode_needs_combine(dims, n_seq, q_per_seq, max_blocks, num_splits)
+
+    def _finish(self, seqlens, w_uv, gate, stream):
+        """The split merge and the up-projection: one launch when decode left partials
+        (mla_combine_up_proj), else the up-projection of the rows decode wrote."""
+        d = self.d
+        n_tok = self.n_seq * self.q_per_seq
+        if self.needs_combine:
+            B.combine_up_proj(d, seqlens, self.max_blocks, self.workspace, self.o_latent, self.lse, w_uv, out=self.out,
+                              num_splits=self.num_splits, gate=gate, write_latent=self.keep_latent, stream=stream)
+        else:
+            B.up_proj(d, self.o_latent.view(n_tok, d.n_heads, d.d_c), w_uv, out=self.out, stream=stream, gate=gate)
+
+    def _latent(self):
+        """o_latent, or None when the merged rows were not written back."""
+        return self.o_latent if self.keep_latent or not self.needs_combine else None
 
     def run(self, *, q_nope, q_rope, q_pos, new_c_kv, new_k_rope, new_seq_id, new_pos, block_table, seqlens,
             pool, w_uk, w_uv, gate=None, stream=None):
@@ -44,11 +64,8 @@ class DecodeStep:
             B.absorb_q(d, q_nope, q_rope, q_pos, w_uk, q_abs=self.q_abs.view(n_tok, d.n_heads, -1), stream=stream)
         B.decode(d, self.q_abs, pool, block_table, seqlens, self.num_splits, self.workspace, self.o_latent,
                  self.lse, stream=stream)
-        if self.needs_combine:
-            B.combine(d, seqlens, self.max_blocks, self.workspace, self.o_latent, self.lse, self.num_splits,
-                      stream=stream)
-        B.up_proj(d, self.o_latent.view(n_tok, d.n_heads, d.d_c), w_uv, out=self.out, stream=stream, gate=gate)
-        return self.out, self.o_latent, self.lse
+        self._finish(seqlens, w_uv, gate, stream)
+        return self.out, self._latent(), self.lse
 
     def run_from_hidden(self, *, h, w_down, d_cq, w_uq, q_pos, new_seq_id, new_pos, block_table, seqlens, pool,
                         w_uk, w_uv, gate=None, stream=None):
@@ -72,8 +89,5 @@ class DecodeStep:
                              workspace=self._ws_q, stream=stream)
         B.decode(d, self.q_abs, pool, block_table, seqlens, self.num_splits, self.workspace, self.o_latent,
                  self.lse, stream=stream)
-        if self.needs_combine:
-            B.combine(d, seqlens, self.max_blocks, self.workspace, self.o_latent, self.lse, self.num_splits,
-                      stream=stream)
-        B.up_proj(d, self.o_latent.view(n_tok, d.n_heads, d.d_c), w_uv, out=self.out, stream=stream, gate=gate)
-        return self.out, self.o_latent, self.lse
+        self._finish(seqlens, w_uv, gate, stream)
+        return self.out, self._latent(), self.lse

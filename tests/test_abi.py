@@ -72,6 +72,14 @@ def test_invalid_arguments_are_rejected(lib):
     assert lib.mla_up_proj_gated(r, 4, FAKE, FAKE, None, FAKE, None) == 1   # the gate is required
     assert lib.mla_up_proj_gated(r, 4, FAKE, None, FAKE, FAKE, None) == 1
     assert lib.mla_combine(r, 1, 1, None, 1, 0, FAKE, 0, FAKE, FAKE, None) == 1
+    # the fused merge + up-projection: seqlens, o_latent, w_uv, out and lse are required
+    cup = lambda *p: lib.mla_combine_up_proj(r, 1, 1, *p)
+    assert cup(None, 1, 0, FAKE, 0, FAKE, 1, FAKE, None, FAKE, FAKE, None) == 1
+    assert cup(FAKE, 1, 0, FAKE, 0, None, 1, FAKE, None, FAKE, FAKE, None) == 1
+    assert cup(FAKE, 1, 0, FAKE, 0, FAKE, 1, None, None, FAKE, FAKE, None) == 1
+    assert cup(FAKE, 1, 0, FAKE, 0, FAKE, 1, FAKE, None, None, FAKE, None) == 1
+    assert cup(FAKE, 1, 0, FAKE, 0, FAKE, 1, FAKE, None, FAKE, None, None) == 1
+    assert lib.mla_combine_up_proj(r, 0, 1, FAKE, 1, 0, FAKE, 0, FAKE, 1, FAKE, None, FAKE, FAKE, None) == 1
     # the pool size bounds every block id the decode reads: an empty pool is rejected
     assert lib.mla_decode(r, 1, 1, FAKE, FAKE, 0, FAKE, 1, FAKE, 0, None, 0, FAKE, FAKE, None) == 1
     assert lib.mla_decode(r, 1, 1, FAKE, FAKE, -3, FAKE, 1, FAKE, 0, None, 0, FAKE, FAKE, None) == 1
@@ -152,6 +160,8 @@ def test_workspace_size_is_checked_before_launch(lib):
     assert lib.mla_decode(r, 1, 1, FAKE, FAKE, 1, FAKE, 64, FAKE, 8, None, 0, FAKE, FAKE, None) == 3
     assert lib.mla_decode(r, 1, 1, FAKE, FAKE, 1, FAKE, 64, FAKE, 8, FAKE, need - 1, FAKE, FAKE, None) == 3
     assert lib.mla_combine(r, 1, 1, FAKE, 64, 8, FAKE, need - 4, FAKE, FAKE, None) == 3
+    assert lib.mla_combine_up_proj(r, 1, 1, FAKE, 64, 8, FAKE, need - 4, FAKE, 0, FAKE, None, FAKE, FAKE, None) == 3
+    assert lib.mla_combine_up_proj(r, 1, 1, FAKE, 64, 8, None, 0, FAKE, 1, FAKE, None, FAKE, FAKE, None) == 3
     assert lib.mla_decode_workspace_bytes(r, 0, 1, 64, 8) == 0
     # one split: no partials, no workspace, nothing for combine to do
     assert lib.mla_decode_workspace_bytes(r, 1, 1, 64, 1) == 0
