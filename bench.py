@@ -90,6 +90,9 @@ def parse():
     ap.add_argument("--upstream", action="store_true",
                     help="start the step from the hidden state: mla_project_down (W_DQ, W_DKV, W_KR and the append) "
                          "and mla_absorb_from_latent (W_UQ and the absorb) replace the append and the absorb")
+    ap.add_argument("--separate-merge", action="store_true",
+                    help="merge the key splits and up-project with two calls (mla_combine, mla_up_proj) instead of "
+                         "the one fused call (mla_combine_up_proj)")
     ap.add_argument("--gated", action="store_true",
                     help="gated MLA: the up-projection applies a sigmoid output gate (mla_up_proj_gated)")
     ap.add_argument("--prefill", action="store_true",
@@ -248,13 +251,20 @@ def main():
                  step.lse, stream=stream)
         if ev:
             ev[1].record(stream)
-        if step.needs_combine:
-            M.combine(dd, seqlens, table.shape[1], step.workspace, step.o_latent, step.lse, args.num_splits,
-                      stream=stream)
-        if ev:
-            ev[2].record(stream)
-        M.up_proj(dd, step.o_latent.view(n_tok, H, -1), step_inputs["w_uv"], out=step.out, stream=stream,
-                  gate=gate)
+        if step.needs_combine and not args.separate_merge:   # the merge and the up-projection in one launch
+            M.combine_up_proj(dd, seqlens, table.shape[1], step.workspace, step.o_latent, step.lse,
+                              step_inputs["w_uv"], out=step.out, num_splits=args.num_splits, gate=gate,
+                              write_latent=False, stream=stream)
+            if ev:
+                ev[2].record(stream)
+        else:
+            if step.needs_combine:
+                M.combine(dd, seqlens, table.shape[1], step.workspace, step.o_latent, step.lse, args.num_splits,
+                          stream=stream)
+            if ev:
+                ev[2].record(stream)
+            M.up_proj(dd, step.o_latent.view(n_tok, H, -1), step_inputs["w_uv"], out=step.out, stream=stream,
+                      gate=gate)
         if ev and len(ev) > 3:
             ev[4].record(stream)
 
@@ -285,6 +295,7 @@ def main():
     else:
         ms_step = ms_total / args.steps
     dec_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
+    fused_merge = step.needs_combine and not args.separate_merge and not args.decode_only
     dec_comb_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
 
     total_tokens = int(inp["seqlens"].to(torch.int64).sum())
@@ -333,6 +344,9 @@ def main():
                    **({"cache_flush_mode": args.flush_mode} if args.flush_mib > 0 else {}),
                    "parallelism": "single GPU"},
         "decode_ms": round(dec_ms, 4),
+        # from the decode's start to the end of the split merge (with the fused call: of the
+        # merge and the up-projection, i.e. the step without the absorb and the append)
+        "merge": ("mla_combine_up_proj" if fused_merge else "mla_combine" if step.needs_combine else "none"),
         "decode_combine_ms": round(dec_comb_ms, 4),
         "decode_combine_tokens_per_s": round(n_tok / (dec_comb_ms * 1e-3), 1),
         "decode_hbm_gbps": round(dec_gbps, 1),

@@ -10,7 +10,7 @@
 // are bit-identical to the two calls.
 //
 // One work-group of 8 waves per (head s, 32 query rows t of that head), one
-// per CU.  Wave w < 4 merges rows 8w .. 8w+7 of the block: it brings the pieces of
+// per CU.  Wave w merges rows 4w .. 4w+3 of the block: it brings the pieces of
 // its rows straight into LDS (one 1 KB direct-to-LDS load per piece; four
 // pieces per row per round, more rounds only for a row split over more than
 // four work units), folds them in order against a running maximum (lane i
@@ -19,8 +19,8 @@
 // inside one work unit, or has no keys) is brought from o_lat instead.  The
 // 1 KB row of block row j is stored with its 16-byte chunk c at position
 // c ^ j, so the MFMA operand reads (16 rows at one chunk) hit 16 different
-// LDS slots.  Waves 4-7 load their W_UV operands meanwhile (the two roles
-// keep their registers apart) and then multiply as the up-projection kernel does: wave 4 + w
+// LDS slots.  Waves 4-7 load their W_UV operands first, while the pieces are
+// in flight, and after the merge multiply as the up-projection kernel does: wave 4 + w
 // contracts latent dims 128w .. 128w+127 for the four output-row blocks, the
 // four fp32 partial tiles are summed through LDS in a fixed order, and wave
 // 4 + w finishes output rows 32w .. 32w+31.
@@ -44,7 +44,7 @@ typedef __attribute__((address_space(3))) float lds_f32;
 
 constexpr int kDc = 512, kDv = 128;
 constexpr int kTok = 32;             // query rows (of one head) per work-group
-constexpr int kRowsPerWave = 8;      // rows merged by each of the 4 merge waves
+constexpr int kRowsPerWave = 4;      // rows merged by each of the 8 waves
 constexpr int kPieces = 4;           // pieces per row staged per round
 constexpr int kSlotB = 1024;         // one latent row of bf16
 
@@ -115,24 +115,39 @@ __global__ void __launch_bounds__(512, 1) combine_up_proj_kernel(CombineUpArgs a
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks) af[vb][ks] = asrc[2 * ks];
     }
-  } else {
-    // ---- the merge of block rows 8w .. 8w+7 (row j: token t0 + j of sequence
+  }
+  {
+    // ---- the merge of block rows 4w .. 4w+3 (row j: token t0 + j of sequence
     // t / q_per_seq).  The per-row and per-piece bookkeeping runs across lanes
-    // (lane k < 8: row k; lane 4k + p < 32: piece p of row k in a round) and is
+    // (lane k < 4: row k; lane 4k + p < 16: piece p of row k in a round) and is
     // broadcast with readlane, so each lane does a few 64-bit divisions, not
     // one per piece.
     const int kl = lane & (kRowsPerWave - 1);
     const int jl = kRowsPerWave * wave + kl;                 // the block row of lane k
     const int tl = t0 + jl;
     const int bl = min(tl, a.n_tok - 1) / a.q_per_seq;
-    // tiles of all sequences and before sequence bl, with the decode kernel's clamped lengths
-    int before = 0, all = 0;
-    for (int i = 0; i < a.n_seq; ++i) {
+    // tiles of all sequences and before each row's sequence, with the decode kernel's
+    // clamped lengths: the lanes take the sequences 64 apart, then sum across the wave
+    int b_of[kRowsPerWave], before_k[kRowsPerWave] = {}, all = 0;
+#pragma unroll
+    for (int k = 0; k < kRowsPerWave; ++k)
+      b_of[k] = min(t0 + kRowsPerWave * wave + k, a.n_tok - 1) / a.q_per_seq;
+    for (int i = lane; i < a.n_seq; i += 64) {
       const int32_t L = min(max(a.seqlens[i], 0), a.lay.max_len);
       const int nt = (L + a.lay.tile - 1) / a.lay.tile;
       all += nt;
-      before += i < bl ? nt : 0;
+#pragma unroll
+      for (int k = 0; k < kRowsPerWave; ++k) before_k[k] += i < b_of[k] ? nt : 0;
     }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      all += __shfl_xor(all, off, 64);
+#pragma unroll
+      for (int k = 0; k < kRowsPerWave; ++k) before_k[k] += __shfl_xor(before_k[k], off, 64);
+    }
+    int before = before_k[0];
+#pragma unroll
+    for (int k = 1; k < kRowsPerWave; ++k) before = kl == k ? before_k[k] : before;
     const int64_t total = all;
     const int64_t G = a.lay.n_splits;
     const int32_t Lb = min(max(a.seqlens[bl], 0), a.lay.max_len);
@@ -223,7 +238,6 @@ __global__ void __launch_bounds__(512, 1) combine_up_proj_kernel(CombineUpArgs a
           }
           m[k] = mn;
         }
-        __builtin_amdgcn_sched_barrier(0);       // one row's pieces in registers at a time
       }
     }
     // the merged rows (bf16) into their first slot, lse to memory
