@@ -91,8 +91,9 @@ def parse():
                     help="start the step from the hidden state: mla_project_down (W_DQ, W_DKV, W_KR and the append) "
                          "and mla_absorb_from_latent (W_UQ and the absorb) replace the append and the absorb")
     ap.add_argument("--separate-merge", action="store_true",
-                    help="merge the key splits and up-project with two calls (mla_combine, mla_up_proj) instead of "
-                         "the one fused call (mla_combine_up_proj)")
+                    help="merge the key splits and up-project with two calls (mla_combine, mla_up_proj) also where "
+                         "the step would use the one fused call (mla_combine_up_proj: when one work-group per head "
+                         "and 32 query rows fills the chip)")
     ap.add_argument("--gated", action="store_true",
                     help="gated MLA: the up-projection applies a sigmoid output gate (mla_up_proj_gated)")
     ap.add_argument("--prefill", action="store_true",
@@ -251,7 +252,7 @@ def main():
                  step.lse, stream=stream)
         if ev:
             ev[1].record(stream)
-        if step.needs_combine and not args.separate_merge:   # the merge and the up-projection in one launch
+        if step.fuse_merge and not args.separate_merge:   # the merge and the up-projection in one launch
             M.combine_up_proj(dd, seqlens, table.shape[1], step.workspace, step.o_latent, step.lse,
                               step_inputs["w_uv"], out=step.out, num_splits=args.num_splits, gate=gate,
                               write_latent=False, stream=stream)
@@ -295,7 +296,7 @@ def main():
     else:
         ms_step = ms_total / args.steps
     dec_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    fused_merge = step.needs_combine and not args.separate_merge and not args.decode_only
+    fused_merge = step.fuse_merge and not args.separate_merge and not args.decode_only
     dec_comb_ms = sum(e[0].elapsed_time(e[2]) for e in evs) / args.steps
 
     total_tokens = int(inp["seqlens"].to(torch.int64).sum())

@@ -21,7 +21,7 @@ class DecodeStep:
     def __init__(self, dims: B.Dims, n_seq: int, q_per_seq: int, max_blocks: int, num_splits: int = 0,
                  device="cuda", keep_latent: bool = True):
         """keep_latent: the merged latent rows are written to o_latent (returned by run);
-        without it o_latent holds only the rows decode finished itself."""
+        without it the fused merge does not write them and run returns None for o_latent."""
         self.d, self.n_seq, self.q_per_seq = dims, n_seq, q_per_seq
         self.keep_latent = keep_latent
         self.max_blocks, self.num_splits = max_blocks, num_splits
@@ -35,21 +35,30 @@ class DecodeStep:
         ws = B.decode_workspace_bytes(dims, n_seq, q_per_seq, max_blocks, num_splits)
         self.workspace = torch.empty(max(ws, 1), dtype=torch.uint8, device=device)
         self.needs_combine = B.decode_needs_combine(dims, n_seq, q_per_seq, max_blocks, num_splits)
+        # the fused merge + up-projection runs one work-group per (head, 32 query rows): it
+        # pays off when that fills the chip, else the two calls (many small work-groups) win
+        cus = torch.cuda.get_device_properties(torch.device(device)).multi_processor_count \
+            if torch.cuda.is_available() else 256
+        self.fuse_merge = self.needs_combine and H * ((n_tok + 31) // 32) >= cus
 
     def _finish(self, seqlens, w_uv, gate, stream):
-        """The split merge and the up-projection: one launch when decode left partials
-        (mla_combine_up_proj), else the up-projection of the rows decode wrote."""
+        """The split merge and the up-projection: one launch (mla_combine_up_proj) when decode
+        left partials and the fused kernel fills the chip, else mla_combine (if needed) and
+        mla_up_proj."""
         d = self.d
         n_tok = self.n_seq * self.q_per_seq
-        if self.needs_combine:
+        if self.fuse_merge:
             B.combine_up_proj(d, seqlens, self.max_blocks, self.workspace, self.o_latent, self.lse, w_uv, out=self.out,
                               num_splits=self.num_splits, gate=gate, write_latent=self.keep_latent, stream=stream)
-        else:
-            B.up_proj(d, self.o_latent.view(n_tok, d.n_heads, d.d_c), w_uv, out=self.out, stream=stream, gate=gate)
+            return
+        if self.needs_combine:
+            B.combine(d, seqlens, self.max_blocks, self.workspace, self.o_latent, self.lse, self.num_splits,
+                      stream=stream)
+        B.up_proj(d, self.o_latent.view(n_tok, d.n_heads, d.d_c), w_uv, out=self.out, stream=stream, gate=gate)
 
     def _latent(self):
         """o_latent, or None when the merged rows were not written back."""
-        return self.o_latent if self.keep_latent or not self.needs_combine else None
+        return None if self.fuse_merge and not self.keep_latent else self.o_latent
 
     def run(self, *, q_nope, q_rope, q_pos, new_c_kv, new_k_rope, new_seq_id, new_pos, block_table, seqlens,
             pool, w_uk, w_uv, gate=None, stream=None):

@@ -92,7 +92,7 @@ def test_decode_step_without_the_latent(cuda_device):
     call and returns the same out and lse as the step that keeps the latent."""
     import mla_latent_kv_23_amd as M
     dev = cuda_device
-    lens = [1200, 90, 2600, 500]
+    lens = [1200, 90, 2600, 500] + [150 + 41 * i for i in range(60)]   # 64 rows: the step fuses the merge
     w = S.WORKLOADS["v3_bs64_ctx8k"].replace(batch=len(lens))
     inp = S.make_inputs(w, 9950, seqlens=torch.tensor(lens, dtype=torch.int32))
     d = U.dims_of(w)
@@ -116,7 +116,8 @@ def test_decode_step_without_the_latent(cuda_device):
             new_seq_id=inp["tok_seq"][rows].to(dev), new_pos=inp["tok_pos"][rows].to(dev), block_table=bt,
             seqlens=inp["seqlens"].to(dev), pool=pool, w_uk=inp["w_uk"].to(dev), w_uv=inp["w_uv"].to(dev))
         torch.cuda.synchronize()
-        assert (o_lat is None) == (not keep) or not step.needs_combine
+        assert step.fuse_merge
+        assert (o_lat is None) == (not keep)
         outs.append((out.clone(), lse.clone()))
     assert torch.equal(outs[0][0].view(torch.int16), outs[1][0].view(torch.int16))
     assert torch.equal(outs[0][1].view(torch.int32), outs[1][1].view(torch.int32))
