@@ -334,9 +334,13 @@ mla_status mla_up_proj_gated(const mla_dims* dims, int32_t n_tok, const void* o_
  * the decode that left the workspace, then w_uv [H, d_v, d_c], gate
  * [n_seq * q_per_seq, H, d_v] or null, out [n_seq * q_per_seq, H, d_v].
  * o_latent is read for the rows mla_decode finished itself (a sequence that
- * lies inside one work unit, or has no token); the merged rows are written
- * back to it only when write_latent != 0 (otherwise those rows of o_latent are
- * left as mla_decode left them).  lse is written for the merged rows as
+ * lies inside one work unit, or has no token); with write_latent != 0 the
+ * merged rows are written back to it as mla_combine writes them.  With
+ * write_latent == 0 the caller gives up those rows: the one-kernel path leaves
+ * them as mla_decode left them, and the two-launch path (taken where the
+ * one-kernel path does not apply: no split, an unaligned buffer, or a shape
+ * it does not support) writes the merged values; either way every other
+ * output is the same.  lse is written for the merged rows as
  * mla_combine writes it.  The results are bit-identical to the two calls.
  * Errors as mla_combine and mla_up_proj, checked before any launch.
  */

@@ -234,8 +234,8 @@ def combine(d: Dims, seqlens, max_blocks: int, workspace, o_latent, lse, num_spl
 def combine_up_proj(d: Dims, seqlens, max_blocks: int, workspace, o_latent, lse, w_uv, out=None, num_splits: int = 0,
                     gate=None, write_latent: bool = True, stream=None):
     """combine followed by up_proj (gated with `gate`) in one call: o_latent [n_seq, q_per_seq, H, d_c] as left by
-    decode (the merged rows written back only with write_latent), lse [n_seq, q_per_seq, H];
-    returns out [n_seq * q_per_seq, H, d_v]."""
+    decode, lse [n_seq, q_per_seq, H]; returns out [n_seq * q_per_seq, H, d_v].  With write_latent the merged rows
+    land in o_latent; without it their contents there are unspecified (as decode left them, or merged)."""
     at = act_torch_dtype(d)
     n_seq, q_per_seq = o_latent.shape[0], o_latent.shape[1]
     if out is None:
