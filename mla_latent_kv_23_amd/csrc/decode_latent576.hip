@@ -35,6 +35,16 @@
 //  * O^T += V^T P^T on bf16 MFMA 32x32x16: wave w owns latent dims
 //    128w..128w+127 for all 128 pairs (fp32 accumulators, 256 per lane); V^T
 //    comes straight from the row-major tile with the LDS transpose read.
+//  * fp8 cache (E4M3FN codes with one fp32 scale per token, bf16 k_R): a
+//    token's score is scale * <q_lat, code> + <q_R, k_R> and its value is
+//    scale * code, so the codes enter both contractions exactly as bf16 and the
+//    scale multiplies the latent part of the score and the PV weight.  With 128
+//    pairs per work-group the staged tile (codes, k_R, scales: 24 KB) is read in
+//    place: one 16-byte code read per lane feeds the A operands of two QK
+//    k-steps (the queries are loaded in the same dim order), converted to bf16
+//    in registers, and each V^T fragment is one 8-bit LDS transpose read,
+//    converted the same way.  With fewer pairs the tile is first expanded to
+//    the bf16 layout in LDS.
 #include <type_traits>
 
 #include "decode_tile.h"
@@ -122,12 +132,24 @@ __device__ __forceinline__ void mfma_qk_first(f32x16& acc, const bf16x8& a, cons
 __device__ __forceinline__ void mfma_qk(f32x16& acc, const bf16x8& a, const bf16x8& b) {
   asm volatile("v_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
 }
+// the same, for an A operand written by vector ALU instructions (two wait states first)
+__device__ __forceinline__ void mfma_qk_first_n(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, 0" : "=&v"(acc) : "v"(a), "v"(b));
+}
+__device__ __forceinline__ void mfma_qk_n(f32x16& acc, const bf16x8& a, const bf16x8& b) {
+  asm volatile("s_nop 1\n\tv_mfma_f32_32x32x16_bf16 %0, %1, %2, %0" : "+v"(acc) : "v"(a), "v"(b));
+}
 __device__ __forceinline__ void mfma_to_valu(f32x16& acc) { asm volatile("s_nop 15\n\ts_nop 7" : "+v"(acc)); }
 
 template <bool kFp8, int kPB>
 __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t* __restrict__ block_table,
                                                           const int32_t* __restrict__ seqlens) {
   __shared__ __attribute__((aligned(1024))) uint8_t lds_raw[kLdsBytes];
+  // fp8 cache, 4 pair blocks: the codes are read in place and converted to
+  // bf16 in registers (kF8D); the other fp8 instantiations expand each tile
+  // to bf16 in LDS first (kF8X)
+  constexpr bool kF8D = kFp8 && kPB == 4;
+  constexpr bool kF8X = kFp8 && !kF8D;
   lds_u8* lds = (lds_u8*)lds_raw;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -224,6 +246,21 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
   const uint32_t p_rd = (uint32_t)(uintptr_t)(lds + kOffP) + (lane & 31) * kPRow + 16 * (half ^ (psw & 1)) +
                         32 * (psw >> 1);
   const int p_ks_sign = (psw >> 1) ? -1 : 1;
+  // fp8 in place: K code reads (row lane % 32, chunk 2m + half; chunk pair j adds 1 KB per 4),
+  // k_R reads (chunk 2m + half), V^T transpose reads (dim block db: 16 lanes bring 8 rows x 16 codes)
+  uint32_t f8_cb[4], f8_rb[4], f8_vb[4];
+  if constexpr (kF8D) {
+    const int r = lane & 31;
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      f8_cb[m] = f8_code_off(r, 2 * m + half);
+      f8_rb[m] = f8_rope_off(r, 2 * m + half);
+    }
+    const int g = lane >> 4, i = lane & 15;
+    const int row = 8 * (g >> 1) + (i >> 1);
+#pragma unroll
+    for (int db = 0; db < 4; ++db) f8_vb[db] = f8_code_off(row, 8 * wave + 2 * db + (g & 1)) + 8 * (i & 1);
+  }
 
   const float sl2 = a.scale_log2;
   lds_f32* s_l = (lds_f32*)(lds + kOffL);
@@ -231,17 +268,13 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
   lds_i32* s_flag = (lds_i32*)(lds + kOffFlag);
 
   // O^T tiles [db][pb] for dims 128*wave + 32*db, pairs 32*pb.  With 16
-  // tiles (kPB = 4) they fill the 256 AGPRs, so the score tile has to live
-  // elsewhere: the bf16 cache keeps it in VGPRs (kAsmQK); the fp8 cache keeps
-  // tiles 0..14 as MFMA accumulators and tile 15 in plain VGPRs (o15), getting
-  // each tile's contribution added with vector ALU ops, so that the MFMA
-  // accumulators (15 O tiles + the S tile) fit the AGPRs.  The accumulators are
-  // only ever MFMA-updated, zeroed, or stored raw.
-  constexpr bool kAsmQK = !kFp8 && kPB == 4;
-  constexpr bool kSplitTile = kPB == 4 && !kAsmQK;
-  constexpr int kOAcc = kSplitTile ? 15 : 4 * kPB;
+  // tiles (kPB = 4) they fill the 256 AGPRs, so the score tile (and, for an
+  // fp8 cache, the RoPE part of the scores) lives in VGPRs: the QK MFMAs are
+  // written as assembly (kAsmQK).  The accumulators are only ever
+  // MFMA-updated, zeroed, or stored raw.
+  constexpr bool kAsmQK = kPB == 4;
+  constexpr int kOAcc = 4 * kPB;
   f32x16 o[kOAcc];
-  float o15[kSplitTile ? 16 : 1];
   bf16x8 q[kQSteps];
 
   // ---- the pieces: one per sequence overlapping [T0, T1)
@@ -266,6 +299,8 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     // bit T % kStages: tile T lies in a padding block (bf16 cache; the fp8
     // cache masks such rows through their scales)
     uint32_t stage_pad = 0;
+    // fp8 in place: byte T % kStages holds tile T's valid row count
+    uint32_t stage_valid = 0;
     // issue this wave's share of the loads of tile T: bf16 straight into ring
     // stage T % kStages; fp8 into staging slot T % 3 (expanded later)
     // Load cursor (bf16 cache): the block-table position of the next tile to
@@ -281,25 +316,38 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       c_blk = bt_row[c_pos];
       c_nxt = c_pos + 1 < a.max_blocks ? bt_row[c_pos + 1] : -1;
     };
-    if constexpr (!kFp8) cursor_at(p0);
-    // bf16: prepare the loads of tile T (the cursor's tile) and advance the cursor
-    auto load_prep = [&](int T) -> TilePart {
+    if constexpr (!kF8X) cursor_at(p0);
+    // bf16 (and fp8 in place): prepare the loads of tile T (the cursor's tile) and advance the cursor
+    auto load_prep = [&](int T) {
       const int tok0 = (int)(T - seq_start) * kTile;
       const bool ok = c_blk >= 0 && c_blk < npool32;
       const int valid = ok ? min(kTile, L - tok0) : 0;
-      const uint8_t* src = ok ? a.pool + (int64_t)c_blk * a.block_bytes + (int64_t)c_sub * (kTile * kRowBytes) : a.pool;
+      const uint8_t* blkp = ok ? a.pool + (int64_t)c_blk * a.block_bytes : a.pool;
+      const int slot = ok ? c_sub * kTile : 0;
       const uint32_t bit = 1u << (T % kStages);
       stage_pad = valid == 0 ? (stage_pad | bit) : (stage_pad & ~bit);
+      const uint32_t sh = 8u * (uint32_t)(T % kStages);
+      stage_valid = (stage_valid & ~(0xffu << sh)) | ((uint32_t)valid << sh);
       if (++c_sub == tpb) {
         c_sub = 0;
         ++c_pos;
         c_blk = c_nxt;
         c_nxt = c_pos + 1 < a.max_blocks ? bt_row[c_pos + 1] : -1;
       }
-      return tile_part_prep(src, valid, lds + (int)(T % kStages) * kTileBytes, wave, lane);
+      if constexpr (kF8D) {
+        return tile_f8_prep(blkp, slot, a.block_size, valid, lds + (int)(T % kStages) * kF8StageBytes, wave, lane);
+      } else {
+        return tile_part_prep(blkp + (int64_t)slot * kRowBytes, valid, lds + (int)(T % kStages) * kTileBytes, wave,
+                              lane);
+      }
     };
+    using LoadT = decltype(load_prep(0));
     auto load_tile = [&](int T) {
-      if constexpr (!kFp8) {
+      if constexpr (kF8D) {
+        const TileF8 p = load_prep(T);
+#pragma unroll
+        for (int i = 0; i < kF8LoadsPerWave; ++i) tile_f8_issue(p, i);
+      } else if constexpr (!kFp8) {
         const TilePart p = load_prep(T);
 #pragma unroll
         for (int i = 0; i < kLoadsPerWave; ++i) tile_part_issue(p, i);
@@ -323,6 +371,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     };
     // LDS address of tile T's bf16 image
     auto tile_base = [&](int T) -> uint32_t {
+      if constexpr (kF8D) return (uint32_t)(uintptr_t)(lds + (int)(T % kStages) * kF8StageBytes);
       const int slot = kFp8 ? (int)(T & 1) : (int)(T % kStages);
       return (uint32_t)(uintptr_t)(lds + slot * kTileBytes);
     };
@@ -335,7 +384,12 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       const int64_t row = ((int64_t)b * a.q_per_seq + my_j) * a.n_heads + my_s;
       const bf16x8* src = (const bf16x8*)(a.q_abs + row * kDk) + half;
 #pragma unroll
-      for (int k = 0; k < kQSteps; ++k) q[k] = src[2 * k];
+      for (int k = 0; k < kQSteps; ++k) {
+        // fp8 in place: latent k-step 2j + e takes dims 32j + 16 half + 8e .. +7 (one 16-byte code read
+        // serves both k-steps of a pair); the query follows the same order
+        if constexpr (kF8D) q[k] = k < 32 ? src[4 * (k >> 1) + half + (k & 1)] : src[2 * k];
+        else q[k] = src[2 * k];
+      }
     }
     int pre = 0;                         // tiles of the first attempt already issued
     for (; pre < kStages - 2 && p0 + pre < p1; ++pre) load_tile(p0 + pre);
@@ -344,10 +398,6 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
     for (;;) {                               // attempts: a second one only after a reference jump
 #pragma unroll
       for (int i = 0; i < kOAcc; ++i) o[i] = f32x16{};
-      if constexpr (kSplitTile) {
-#pragma unroll
-        for (int i = 0; i < 16; ++i) o15[i] = 0.f;
-      }
       l_part = 0.f;
       int T_issue = p0 + pre;            // loads in flight cover [T, T_issue)
       pre = 0;                               // a second attempt loads every tile again
@@ -363,18 +413,25 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         if constexpr (kFp8) {
           // this lane's 16 token scales (rows past the tile's valid ones hold
           // no data: scale 0 and score -inf)
-          const lds_u8* scl = lds + kOffF + (int)(T % kF8Slots) * kF8StageBytes + kF8OffScales + 1024 * wave;
-          const int nv = tile_valid(T);
+          const lds_u8* scl = kF8D ? lds + (int)(T % kStages) * kF8StageBytes + kF8OffScales + 1024 * wave
+                                   : lds + kOffF + (int)(T % kF8Slots) * kF8StageBytes + kF8OffScales + 1024 * wave;
+          const int nv = kF8D ? (int)((stage_valid >> (8 * (T % kStages))) & 0xffu) : tile_valid(T);
+          auto scale_scores = [&](auto full_c) {
+            constexpr bool kFull = decltype(full_c)::value;
 #pragma unroll
-          for (int g = 0; g < 4; ++g) {
-            const f32x4 s4 = *(const lds_f32x4*)(scl + 4 * (8 * g + 4 * half));
+            for (int g = 0; g < 4; ++g) {
+              const f32x4 s4 = *(const lds_f32x4*)(scl + 4 * (8 * g + 4 * half));
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-              const bool in = 8 * g + 4 * half + e < nv;
-              sc[4 * g + e] = in ? s4[e] : 0.f;
-              sv[4 * g + e] = in ? fmaf(sacc[4 * g + e], s4[e], s_rope[4 * g + e]) : -INFINITY;
+              for (int e = 0; e < 4; ++e) {
+                const bool in = kFull || 8 * g + 4 * half + e < nv;
+                sc[4 * g + e] = in ? s4[e] : 0.f;
+                sv[4 * g + e] = in ? fmaf(sacc[4 * g + e], s4[e], s_rope[4 * g + e]) : -INFINITY;
+              }
             }
-          }
+          };
+          // a full tile (wave-uniform test) needs no per-row mask
+          if (nv == kTile) scale_scores(std::true_type{});
+          else scale_scores(std::false_type{});
         } else {
 #pragma unroll
           for (int i = 0; i < 16; ++i) sv[i] = sacc[i];
@@ -413,7 +470,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         // taken against it right away, and the tile max only when a lane's
         // sum of rounded weights reaches 2^16 (a weight above 2^16 rounds to at
         // least 2^16, so no jump goes unseen); the rule applied is the same
-        const bool fast = !kFp8 && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) == 0;
+        const bool fast = (!kFp8 || kF8D) && __builtin_amdgcn_ballot_w64(m_ref == -INFINITY) == 0;
         if (!fast) ref_update();
         // exp2 of masked scores is 0; an unset reference (no visible key yet) is taken as 0
         const float neg_m = m_ref == -INFINITY ? 0.f : -m_ref;
@@ -447,13 +504,25 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
 
       // ---- O^T += V^T P^T for tile T: this wave's 128 dims x all 128 pairs
       auto pv = [&](uint32_t tb, int T) {
-        f32x16 t15 = {};
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bf16x8 pf[kPB];
           const uint32_t pbuf = p_rd + (uint32_t)(T & 1) * kPBufBytes + (uint32_t)(32 * ks * p_ks_sign);
 #pragma unroll
           for (int pb = 0; pb < kPB; ++pb) pf[pb] = *(const lds_bf16x8*)(uintptr_t)(pbuf + 32 * pb * kPRow);
+          if constexpr (kF8D) {
+            // V^T fragment of dim block db: one 8-bit transpose read (lane: dim 32 db + lane % 32 of
+            // this wave's 128, tokens 16 ks + 8 half .. +7), converted to bf16
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+              const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)(tb + f8_vb[db] + 8192 * ks));
+              const bf16x8 vf = f8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1]);
+#pragma unroll
+              for (int pb = 0; pb < kPB; ++pb)
+                o[db * kPB + pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], o[db * kPB + pb], 0, 0, 0);
+            }
+            continue;
+          }
           // V^T fragments for the 4 dim blocks: two transpose reads each (4 tokens apiece)
           bf16x4 h[8];
 #pragma unroll
@@ -468,15 +537,9 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
             const bf16x4 lo = h[(db >> 1) * 4 + (db & 1) * 2], hi = h[(db >> 1) * 4 + (db & 1) * 2 + 1];
             const bf16x8 vf = bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 #pragma unroll
-            for (int pb = 0; pb < kPB; ++pb) {
-              if (kSplitTile && db * kPB + pb == 15) t15 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], t15, 0, 0, 0);
-              else o[db * kPB + pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], o[db * kPB + pb], 0, 0, 0);
-            }
+            for (int pb = 0; pb < kPB; ++pb)
+              o[db * kPB + pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], o[db * kPB + pb], 0, 0, 0);
           }
-        }
-        if constexpr (kSplitTile) {
-#pragma unroll
-          for (int i = 0; i < 16; ++i) o15[i] += t15[i];
         }
       };
 
@@ -484,7 +547,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       while (T_issue - p0 < (kAsmQK ? kStages - 2 : kStages - 1) && T_issue < p1) load_tile(T_issue++);
       wait_tile(T_issue - 1 - p0);           // tile p0 has landed
       lds_barrier();
-      if constexpr (kFp8) {
+      if constexpr (kF8X) {
         expand(p0);
         lds_barrier();
       }
@@ -507,7 +570,46 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
           const uint32_t tb = tile_base(T);
           f32x16 sacc;
           float s_rope[16];
-          auto qk = [&](const TilePart* lp) {
+          auto qk = [&](const LoadT* lp) {
+            if constexpr (kF8D) {
+              // fp8 in place: the 4 RoPE k-steps (bf16 k_R) into their own sum, then the 32 latent
+              // k-steps, each 16-byte code read converted into the A operands of a k-step pair; the
+              // conversion of pair j+1 runs while the MFMAs of pair j do.  The tile's six loads go
+              // out between them.
+              f32x16 srope;
+              bf16x8 kr[4];
+#pragma unroll
+              for (int m = 0; m < 4; ++m) kr[m] = *(const lds_bf16x8*)(uintptr_t)(tb + f8_rb[m]);
+              u32x4 raw[2];
+              raw[0] = *(const lds_u32x4*)(uintptr_t)(tb + f8_cb[0]);
+              raw[1] = *(const lds_u32x4*)(uintptr_t)(tb + f8_cb[1]);
+#pragma unroll
+              for (int m = 0; m < 4; ++m) {
+                if (m == 0) mfma_qk_first(srope, kr[0], q[32]);
+                else mfma_qk(srope, kr[m], q[32 + m]);
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              bf16x8 a0 = f8x8_to_bf16(raw[0][0], raw[0][1]), a1 = f8x8_to_bf16(raw[0][2], raw[0][3]);
+              raw[0] = *(const lds_u32x4*)(uintptr_t)(tb + f8_cb[2]);
+#pragma unroll
+              for (int j = 0; j < 16; ++j) {
+                if (j == 0) mfma_qk_first_n(sacc, a0, q[0]);
+                else mfma_qk_n(sacc, a0, q[2 * j]);
+                mfma_qk_n(sacc, a1, q[2 * j + 1]);
+                if (lp != nullptr && j % 3 == 0) tile_f8_issue(*lp, j / 3);
+                if (j + 1 < 16) {
+                  const u32x4 w = raw[(j + 1) & 1];
+                  if (j + 3 < 16) raw[(j + 1) & 1] = *(const lds_u32x4*)(uintptr_t)(tb + f8_cb[(j + 3) & 3] + 1024 * ((j + 3) >> 2));
+                  a0 = f8x8_to_bf16(w[0], w[1]);
+                  a1 = f8x8_to_bf16(w[2], w[3]);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+              }
+              mfma_to_valu(sacc);
+#pragma unroll
+              for (int i = 0; i < 16; ++i) s_rope[i] = srope[i];
+              return;
+            }
             bf16x8 kf[kKAhead];
 #pragma unroll
             for (int k = 0; k < kKAhead; ++k) kf[k] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * (k / 4));
@@ -518,13 +620,15 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
               else mfma_qk(sacc, cur, q[k]);
               if (k + kKAhead < kQSteps)
                 kf[k % kKAhead] = *(const lds_bf16x8*)(uintptr_t)(tb + kq_base[k % 4] + 1024 * ((k + kKAhead) / 4));
-              if (lp != nullptr && k % 4 == 1) tile_part_issue(*lp, k / 4);
+              if constexpr (!kF8D) {
+                if (lp != nullptr && k % 4 == 1) tile_part_issue(*lp, k / 4);
+              }
               __builtin_amdgcn_sched_barrier(0);
             }
             mfma_to_valu(sacc);
           };
           if (T_issue < p1) {
-            const TilePart lp = load_prep(T_issue++);
+            const LoadT lp = load_prep(T_issue++);
             qk(&lp);
           } else {
             qk(nullptr);
@@ -598,7 +702,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       const bool any_redo = (s_flag[0] | s_flag[1] | s_flag[2] | s_flag[3]) != 0;
       lds_barrier();                         // flags read
       if (!any_redo) break;
-      if constexpr (!kFp8) cursor_at(p0);    // the second attempt loads from the first tile again
+      if constexpr (!kF8X) cursor_at(p0);    // the second attempt loads from the first tile again
       // Some pair's reference rose by more than 2^16 after it had accumulated
       // weights: run the piece again.  Every reference now lies within 2^16 of
       // its pair's maximum over the piece, so the second pass cannot jump.
@@ -639,7 +743,7 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
       s_l[e_pair] = l_tot;
       s_m[e_pair] = m_ref;
     }
-    if constexpr (!kFp8) {
+    if constexpr (!kF8X) {
       lds_barrier();                               // every pair's l is in LDS
       // a partial is stored raw (a factor of 1 is exact), a whole sequence normalised
       const bool norm = whole;
@@ -655,10 +759,8 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         for (int db = 0; db < 4; ++db)
 #pragma unroll
           for (int qq = 0; qq < 4; ++qq) {
-            f32x4 v;
-            if (kSplitTile && db * kPB + pb == 15) v = f32x4{o15[4 * qq], o15[4 * qq + 1], o15[4 * qq + 2], o15[4 * qq + 3]};
-            else v = f32x4{o[db * kPB + pb][4 * qq], o[db * kPB + pb][4 * qq + 1], o[db * kPB + pb][4 * qq + 2],
-                           o[db * kPB + pb][4 * qq + 3]};
+            f32x4 v = f32x4{o[db * kPB + pb][4 * qq], o[db * kPB + pb][4 * qq + 1], o[db * kPB + pb][4 * qq + 2],
+                            o[db * kPB + pb][4 * qq + 3]};
             // hardware pack, round to nearest even
             if constexpr (kNorm) v = v * inv;
             const bf16x2 lo = __builtin_convertvector(f32x2{v[0], v[1]}, bf16x2);
@@ -697,10 +799,8 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
           for (int db = 0; db < 4; ++db)
 #pragma unroll
             for (int qq = 0; qq < 4; ++qq) {
-              f32x4 v;
-              if (kSplitTile && db * kPB + pb == 15) v = f32x4{o15[4 * qq], o15[4 * qq + 1], o15[4 * qq + 2], o15[4 * qq + 3]};
-              else v = f32x4{o[db * kPB + pb][4 * qq], o[db * kPB + pb][4 * qq + 1], o[db * kPB + pb][4 * qq + 2],
-                             o[db * kPB + pb][4 * qq + 3]};
+              f32x4 v = f32x4{o[db * kPB + pb][4 * qq], o[db * kPB + pb][4 * qq + 1], o[db * kPB + pb][4 * qq + 2],
+                              o[db * kPB + pb][4 * qq + 3]};
               *(lds_f32x4*)(xrow + (32 * db + 8 * qq) * 4) = v;
             }
         }

@@ -19,6 +19,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x2_t __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
@@ -27,6 +28,7 @@ typedef __attribute__((address_space(3))) float lds_f32;
 typedef __attribute__((address_space(3))) f32x4 lds_f32x4;
 typedef __attribute__((address_space(3))) int32_t lds_i32;
 typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) i32x2_t lds_i32x2;
 
 constexpr int kDc = 512, kDk = 576, kRowBytes = kDk * 2;   // bf16 cache row
 constexpr int kTile = kDecodeTile;                          // 32 tokens
@@ -169,6 +171,72 @@ __device__ __forceinline__ void issue_tile_fp8(const uint8_t* blk, int slot, int
       : [vc] "v"(off_c), [vr] "v"(off_r), [vs] "v"(off_s), [sc] "s"(s_c), [sr] "s"(s_r), [ss] "s"(s_s),
         [mc] "s"(m_c), [mr] "s"(m_r), [ms] "s"(m_s)
       : "memory", "m0", "scc");
+}
+
+// fp8 tile read in place (four pair blocks): the staged tile keeps the codes
+// in fp8 and the MFMA operands are converted to bf16 in registers.  The stage
+// (24 KB) uses the swizzle of the bf16 tile so that both the 16-byte K reads
+// (16 rows at one chunk) and the 8-bit transpose reads (8 rows x 16 bytes)
+// are free of bank conflicts:
+//   codes  [0, 16384):     row r, 16-byte chunk c (c < 32) at
+//                          ((r / 8) * 4 + c / 8) * 1024 + rpos(r) * 128 + 16 ((c % 8) ^ swz(r % 8));
+//   k_R    [16384, 20480): row r, chunk c (c < 8) at 16384 + (r / 8) * 1024 + rpos(r) * 128 + 16 (c ^ swz(r % 8));
+//   scales [20480, 24576): wave w's own copy of the 32 scales at 20480 + 1024 w.
+__device__ __forceinline__ uint32_t f8_code_off(int r, int c) {
+  return ((r >> 3) * 4 + (c >> 3)) * 1024 + rpos(r) * 128 + 16 * ((c & 7) ^ swz(r & 7));
+}
+__device__ __forceinline__ uint32_t f8_rope_off(int r, int c) {
+  return kF8OffRope + (r >> 3) * 1024 + rpos(r) * 128 + 16 * ((c & 7) ^ swz(r & 7));
+}
+// A wave's six loads of one tile: wave w brings rows 8w .. 8w+7 (lane l: row
+// position l / 8, slot l % 8 of each 1 KB block): four code blocks, one k_R
+// block, its copy of the scales.  Rows at or beyond `valid` re-read row 0.
+struct TileF8 {
+  uint64_t sc, sr, ss;     // sources (wave-uniform): codes, k_R, scales of the tile's first row
+  uint32_t mc, mr, ms;     // LDS bases (wave-uniform)
+  uint32_t oc, orr, os;    // per-lane source offsets
+};
+__device__ __forceinline__ TileF8 tile_f8_prep(const uint8_t* blk, int slot, int block_size, int valid, lds_u8* dst,
+                                               int wave, int lane) {
+  const int r = 8 * wave + ((lane >> 3) ^ (wave & 1));
+  const bool in = r < valid;
+  const int x = (lane & 7) ^ swz(r & 7);
+  TileF8 p;
+  p.oc = (in ? r * kDc : 0) + 16 * x;
+  p.orr = (in ? r * 128 : 0) + 16 * x;
+  p.os = 16 * (lane & 7);
+  const uint32_t base = (uint32_t)(uintptr_t)dst;
+  p.mc = (uint32_t)__builtin_amdgcn_readfirstlane(base + (uint32_t)(wave * 4096));
+  p.mr = (uint32_t)__builtin_amdgcn_readfirstlane(base + (uint32_t)(kF8OffRope + wave * 1024));
+  p.ms = (uint32_t)__builtin_amdgcn_readfirstlane(base + (uint32_t)(kF8OffScales + wave * 1024));
+  auto sreg = [](const uint8_t* q) -> uint64_t {
+    const uint64_t a = (uint64_t)(uintptr_t)q;
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(a >> 32));
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)a);
+    return ((uint64_t)hi << 32) | (uint64_t)lo;
+  };
+  p.sc = sreg(blk + (int64_t)slot * kDc);
+  p.sr = sreg(blk + (int64_t)block_size * (kDc + 4) + (int64_t)slot * 128);
+  p.ss = sreg(blk + (int64_t)block_size * kDc + (int64_t)slot * 4);
+  return p;
+}
+// load i (0..5) of a wave's share: code blocks 0..3, k_R, scales
+__device__ __forceinline__ void tile_f8_issue(const TileF8& p, int i) {
+  const uint32_t off = i < 4 ? p.oc + 0x80u * (uint32_t)i : i == 4 ? p.orr : p.os;
+  const uint64_t src = i < 4 ? p.sc : i == 4 ? p.sr : p.ss;
+  const uint32_t m = i < 4 ? p.mc + 0x400u * (uint32_t)i : i == 4 ? p.mr : p.ms;
+  asm volatile("s_mov_b32 m0, %[m]\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %[t], %[s]"
+               :
+               : [t] "v"(off), [s] "s"(src), [m] "s"(m)
+               : "m0");
+}
+// eight fp8 codes (two dwords, byte b = element b) -> bf16x8, exactly
+__device__ __forceinline__ bf16x8 f8x8_to_bf16(uint32_t w0, uint32_t w1) {
+  const bf16x2 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, false);
+  const bf16x2 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w0, 1.0f, true);
+  const bf16x2 c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, false);
+  const bf16x2 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w1, 1.0f, true);
+  return bf16x8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
 #pragma clang diagnostic pop
