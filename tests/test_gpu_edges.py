@@ -26,11 +26,15 @@ from tests import _util as U
 pytestmark = pytest.mark.gpu
 
 V3 = S.WORKLOADS["v3_bs64_ctx8k"]
-# (workload, cache) cases: the tuned decode with a bf16 and an fp8 cache, and
+# (workload, cache) cases: the tuned decode with a bf16 and an fp8 cache (32 and 128 heads), and
 # the generic decode (fp32, the tiny workload's dims; bf16 with 16-token blocks)
 CASES = {
     "bf16": V3.replace(batch=3, n_heads=32),
     "fp8": V3.replace(batch=3, n_heads=32, cache_dtype="fp8"),
+    # 128 heads: one 128-pair work-group per query row (with an fp8 cache, the kernel that
+    # reads the staged codes in place instead of expanding each tile)
+    "bf16_128": V3.replace(batch=3),
+    "fp8_128": V3.replace(batch=3, cache_dtype="fp8"),
     "f32_generic": S.WORKLOADS["tiny_fp32"].replace(batch=3, n_heads=4),
     "bf16_generic": V3.replace(batch=3, n_heads=16, block_size=16),
 }
@@ -108,7 +112,7 @@ def test_identical_latents_give_that_latent(case, num_splits, cuda_device):
         assert np.all(ratio <= 1.5), f"seq {b}: worst {float(ratio.max()):.2f} ulp"
 
 
-@pytest.mark.parametrize("case", ["bf16", "fp8", "bf16_generic"])
+@pytest.mark.parametrize("case", ["bf16", "fp8", "fp8_128", "bf16_generic"])
 @pytest.mark.parametrize("num_splits", [0, 7])
 def test_decode_and_combine_are_deterministic(case, num_splits, cuda_device):
     w = CASES[case]
