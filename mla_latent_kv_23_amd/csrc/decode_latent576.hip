@@ -443,10 +443,17 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
         // causal / length mask: only a tile reaching past the first query row's
         // last visible token needs it (wave-uniform test)
         if (tok0 + kTile > L - a.q_per_seq + 1) {
-          const int vis = L - a.q_per_seq + my_j - tok0 + 1;  // tokens [0, vis) of this tile are visible
+          // the lane's row and token offsets are derived here from an opaque copy of the
+          // lane id: kept across the tile loop (the compiler would carry the visible count
+          // as a per-lane induction variable) they can be spilled, and the reload's
+          // memory-count wait, placed inside the loop, waits for every tile load in flight
+          int lx = lane;
+          asm volatile("" : "+v"(lx));
+          const int mj = kPB == 4 ? (32 * wave + (lx & 31)) / hpw : min((32 * wave + (lx & 31)) / hpw, a.q_per_seq - 1);
+          const int vis = L - a.q_per_seq + mj - tok0 + 1;  // tokens [0, vis) of this tile are visible
 #pragma unroll
           for (int i = 0; i < 16; ++i) {
-            const int t = 8 * (i / 4) + 4 * half + (i % 4);
+            const int t = 8 * (i / 4) + 4 * (lx >> 5) + (i % 4);
             sv[i] = t < vis ? sv[i] : -INFINITY;
           }
         }
@@ -504,25 +511,45 @@ __global__ void __launch_bounds__(256, 1) decode576_kernel(Args a, const int32_t
 
       // ---- O^T += V^T P^T for tile T: this wave's 128 dims x all 128 pairs
       auto pv = [&](uint32_t tb, int T) {
+        if constexpr (kF8D) {
+          // fp8 in place.  V^T fragment (k-step ks, dim block db): one 8-bit transpose read
+          // (lane: dim 32 db + lane % 32 of this wave's 128, tokens 16 ks + 8 half .. +7),
+          // converted to bf16.  The first k-step's P fragments and all eight transpose reads go
+          // out first, the second k-step's P fragments once its MFMAs have started.
+          const uint32_t pbuf = p_rd + (uint32_t)(T & 1) * kPBufBytes;
+          bf16x8 pf0[kPB], pf1[kPB];
+#pragma unroll
+          for (int pb = 0; pb < kPB; ++pb) pf0[pb] = *(const lds_bf16x8*)(uintptr_t)(pbuf + 32 * pb * kPRow);
+          i32x2_t v[2][4];
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+              v[ks][db] = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)(tb + f8_vb[db] + 8192 * ks));
+#pragma unroll
+          for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+            for (int db = 0; db < 4; ++db) {
+              const bf16x8 vf = f8x8_to_bf16((uint32_t)v[ks][db][0], (uint32_t)v[ks][db][1]);
+#pragma unroll
+              for (int pb = 0; pb < kPB; ++pb)
+                o[db * kPB + pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, ks ? pf1[pb] : pf0[pb], o[db * kPB + pb],
+                                                                           0, 0, 0);
+              if (ks == 0 && db == 0) {
+#pragma unroll
+                for (int pb = 0; pb < kPB; ++pb)
+                  pf1[pb] = *(const lds_bf16x8*)(uintptr_t)(pbuf + (uint32_t)(32 * p_ks_sign) + 32 * pb * kPRow);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          return;
+        }
 #pragma unroll
         for (int ks = 0; ks < 2; ++ks) {
           bf16x8 pf[kPB];
           const uint32_t pbuf = p_rd + (uint32_t)(T & 1) * kPBufBytes + (uint32_t)(32 * ks * p_ks_sign);
 #pragma unroll
           for (int pb = 0; pb < kPB; ++pb) pf[pb] = *(const lds_bf16x8*)(uintptr_t)(pbuf + 32 * pb * kPRow);
-          if constexpr (kF8D) {
-            // V^T fragment of dim block db: one 8-bit transpose read (lane: dim 32 db + lane % 32 of
-            // this wave's 128, tokens 16 ks + 8 half .. +7), converted to bf16
-#pragma unroll
-            for (int db = 0; db < 4; ++db) {
-              const i32x2_t v = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_i32x2*)(uintptr_t)(tb + f8_vb[db] + 8192 * ks));
-              const bf16x8 vf = f8x8_to_bf16((uint32_t)v[0], (uint32_t)v[1]);
-#pragma unroll
-              for (int pb = 0; pb < kPB; ++pb)
-                o[db * kPB + pb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[pb], o[db * kPB + pb], 0, 0, 0);
-            }
-            continue;
-          }
           // V^T fragments for the 4 dim blocks: two transpose reads each (4 tokens apiece)
           bf16x4 h[8];
 #pragma unroll
