@@ -62,11 +62,14 @@ static_assert(kKAhead % 4 == 0, "K prefetch depth is a multiple of the 4 per-lan
 
 constexpr int kOffP = kStages * kTileBytes;                 // 147456: two P buffers (tile T in buffer T % 2)
 constexpr int kLdsBytes = kOffP + 2 * kPBufBytes;           // 163840
-// fp8 cache: two bf16 tile buffers (tile T in buffer T % 2), then a 3-slot
-// staging ring for the raw tiles, ending where the P buffers start
+// fp8 cache, tiles expanded in LDS (fewer than 4 pair blocks): two bf16 tile
+// buffers (tile T in buffer T % 2), then a 3-slot staging ring for the raw
+// tiles, ending where the P buffers start
 constexpr int kF8Slots = 3;
 constexpr int kOffF = 2 * kTileBytes;
 static_assert(kOffF + kF8Slots * kF8StageBytes == kOffP, "fp8 buffers use the bf16 ring's space");
+// fp8 cache read in place (4 pair blocks): a ring of kStages raw stages
+static_assert(kStages * kF8StageBytes <= kOffP, "fp8 stages fit below the P buffers");
 // Small scratch shares P buffer 0; it is used only while no weights are live
 // there: the sequence scan before the first tile, the redo flags after the
 // last PV of an attempt, the (l, m) rows in the piece epilogue.
